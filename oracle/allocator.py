@@ -1,0 +1,245 @@
+"""Block manager model: the reference semantics of the host allocator. TEST INFRASTRUCTURE.
+
+Sources
+  * "From OOM to Smooth Inference (RAG memory management)", §2.3: the Python
+    KV cache manager. Free pool is a list popped from the front and extended
+    at the back; a pool that is too small raises before anything is popped;
+    block count is ceil(tokens / block_size); per-request token count.
+  * "Inference Engine Memory Optimisation (KV Cache to Continuous Batching)",
+    §3: the block manager with a FIFO queue of free blocks, block tables,
+    per-block reference counts, allocate / append-token / free / share-prefix,
+    available blocks and utilisation (used / total).
+  * "vLLM Architecture and Memory Use, ch. 3", §3.2: sequences forked from one
+    parent (beams, parallel samples) share blocks through reference counts; a
+    block returns to the pool when its count reaches zero. §3.3: copy-on-write
+    allocates a new block, copies the shared block into it, writes the new one
+    and decrements the original's count.
+  * "From OOM to Smooth Inference", §6.1: forked beams copy only the last block.
+
+Readings taken where the pages are silent or garbled (each is tested):
+  R1  Block ids are 0-based; the initial free order is caller-supplied
+      (default ascending).
+  R2  allocate() on an existing id is an error (EXISTS); growth goes through
+      append(). A 0-token allocate is allowed and holds no block.
+  R3  append(n) allocates ceil(count/bs) - len(table) new blocks at once, so
+      n > block_size is handled (the Python sample pops only one block).
+  R4  The fill of the last block is derived from a per-sequence token count,
+      not from a per-block count, so that two sharers of a block never bump
+      the same counter.
+  R5  Copy-on-write: when an append's first new position lands inside the
+      existing last block and that block's refcount is > 1, a fresh block is
+      popped first, the old block's refcount drops by one, the table entry is
+      replaced and the pair (old, new) is reported for a whole-block copy. A
+      full last block is never copied: the next token goes to a new block.
+  R6  share_prefix(src, n, dst) fails if n exceeds src's table length (the
+      comparison sign was lost in the page's extraction) or dst exists. dst's
+      token count is min(n * bs, src's count).
+  R7  fork(parent, child) copies the whole table and the token count and adds
+      one reference to every block.
+  R8  free() walks the table in order; every block whose count reaches zero is
+      appended to the back of the free queue.
+  R9  A failing call changes no state: every check runs before any mutation.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass
+
+OK = 0
+ERR_INVALID = -1
+ERR_OOM = -2
+ERR_NO_SEQ = -3
+ERR_EXISTS = -4
+
+
+class AllocError(Exception):
+    """Raised for a rejected call; ``code`` is one of the ERR_* values."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+@dataclass
+class AppendResult:
+    slots: list  # flat slot (block * bs + offset) of each appended token
+    cow_src: int  # -1 when no copy-on-write happened
+    cow_dst: int
+
+
+class BlockAllocatorModel:
+    """Pure-Python model of the paged KV block manager."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        # "From OOM to Smooth Inference", §2.3: sizes must be positive.
+        if num_blocks <= 0 or block_size <= 0:
+            raise AllocError(ERR_INVALID, "num_blocks and block_size must be positive")
+        if free_order is None:
+            order = list(range(num_blocks))
+        else:
+            order = [int(b) for b in free_order]
+            if sorted(order) != list(range(num_blocks)):
+                raise AllocError(ERR_INVALID, "free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.bs = block_size
+        self.free = deque(order)
+        self.tables: dict[int, list[int]] = {}
+        self.counts: dict[int, int] = {}
+        self.ref = [0] * num_blocks
+
+    # ----------------------------------------------------------- helpers
+    def _needed(self, tokens: int) -> int:
+        # ceil(tokens / block_size), "From OOM to Smooth Inference", §2.3
+        return (tokens + self.bs - 1) // self.bs
+
+    def _pop(self, count: int) -> list[int]:
+        if len(self.free) < count:
+            raise AllocError(ERR_OOM, f"need {count} blocks, {len(self.free)} free")
+        return [self.free.popleft() for _ in range(count)]
+
+    def _require(self, seq: int):
+        if seq not in self.tables:
+            raise AllocError(ERR_NO_SEQ, f"sequence {seq} does not exist")
+
+    def _slot(self, table: list[int], pos: int) -> int:
+        return table[pos // self.bs] * self.bs + pos % self.bs
+
+    # ----------------------------------------------------------- operations
+    def allocate(self, seq: int, num_tokens: int) -> list[int]:
+        """New sequence holding num_tokens tokens; returns their slots."""
+        if num_tokens < 0:
+            raise AllocError(ERR_INVALID, "negative token count")
+        if seq in self.tables:
+            raise AllocError(ERR_EXISTS, f"sequence {seq} exists")
+        blocks = self._pop(self._needed(num_tokens))
+        for b in blocks:
+            self.ref[b] += 1
+        self.tables[seq] = blocks
+        self.counts[seq] = num_tokens
+        return [self._slot(blocks, p) for p in range(num_tokens)]
+
+    def append(self, seq: int, n: int = 1) -> AppendResult:
+        """Add n tokens to seq (R3, R5); returns their slots and any CoW pair."""
+        self._require(seq)
+        if n < 0:
+            raise AllocError(ERR_INVALID, "negative token count")
+        table = self.tables[seq]
+        count = self.counts[seq]
+        if n == 0:
+            return AppendResult([], -1, -1)
+        cow = bool(table) and count % self.bs != 0 and self.ref[table[-1]] > 1
+        grow = self._needed(count + n) - len(table)
+        need = grow + (1 if cow else 0)
+        if len(self.free) < need:
+            raise AllocError(ERR_OOM, f"need {need} blocks, {len(self.free)} free")
+        cow_src = cow_dst = -1
+        if cow:
+            cow_src = table[-1]
+            cow_dst = self._pop(1)[0]
+            self.ref[cow_src] -= 1
+            self.ref[cow_dst] += 1
+            table[-1] = cow_dst
+        for b in self._pop(grow):
+            self.ref[b] += 1
+            table.append(b)
+        self.counts[seq] = count + n
+        return AppendResult([self._slot(table, p) for p in range(count, count + n)], cow_src, cow_dst)
+
+    def fork(self, parent: int, child: int) -> None:
+        """child shares every block of parent (R7)."""
+        self._require(parent)
+        if child in self.tables:
+            raise AllocError(ERR_EXISTS, f"sequence {child} exists")
+        table = list(self.tables[parent])
+        for b in table:
+            self.ref[b] += 1
+        self.tables[child] = table
+        self.counts[child] = self.counts[parent]
+
+    def share_prefix(self, src: int, num_blocks: int, dst: int) -> None:
+        """dst's table is src's first num_blocks blocks (R6)."""
+        self._require(src)
+        if dst in self.tables:
+            raise AllocError(ERR_EXISTS, f"sequence {dst} exists")
+        table = self.tables[src]
+        if num_blocks < 0 or num_blocks > len(table):
+            raise AllocError(ERR_INVALID, "more shared blocks than the source holds")
+        shared = list(table[:num_blocks])
+        for b in shared:
+            self.ref[b] += 1
+        self.tables[dst] = shared
+        self.counts[dst] = min(num_blocks * self.bs, self.counts[src])
+
+    def free_seq(self, seq: int) -> None:
+        """Release seq's blocks in table order (R8)."""
+        self._require(seq)
+        table = self.tables.pop(seq)
+        del self.counts[seq]
+        for b in table:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    # ----------------------------------------------------------- queries
+    def slots(self, seq: int, start: int, n: int) -> list[int]:
+        self._require(seq)
+        if start < 0 or n < 0 or start + n > self.counts[seq]:
+            raise AllocError(ERR_INVALID, "positions out of range")
+        t = self.tables[seq]
+        return [self._slot(t, p) for p in range(start, start + n)]
+
+    def block_table(self, seq: int) -> list[int]:
+        self._require(seq)
+        return list(self.tables[seq])
+
+    def num_tokens(self, seq: int) -> int:
+        self._require(seq)
+        return self.counts[seq]
+
+    def refcount(self, block: int) -> int:
+        if block < 0 or block >= self.num_blocks:
+            raise AllocError(ERR_INVALID, "block id out of range")
+        return self.ref[block]
+
+    def free_list(self) -> list[int]:
+        return list(self.free)
+
+    def available_blocks(self) -> int:
+        return len(self.free)
+
+    def utilization(self) -> float:
+        """(total - free) / total: the second page's definition."""
+        return (self.num_blocks - len(self.free)) / self.num_blocks
+
+    def stats(self) -> dict:
+        """Free blocks, live sequences, used blocks, physical utilisation,
+        filled slots and slot utilisation.
+
+        A used block's filled slots are the largest fill any sequence that
+        references it sees in it, so a shared block counts its tokens once.
+        """
+        filled: dict[int, int] = {}
+        for seq, table in self.tables.items():
+            c = self.counts[seq]
+            for i, b in enumerate(table):
+                f = max(0, min(self.bs, c - i * self.bs))
+                filled[b] = max(filled.get(b, 0), f)
+        used = self.num_blocks - len(self.free)
+        total_filled = sum(filled.values())
+        return {
+            "free_blocks": len(self.free),
+            "live_seqs": len(self.tables),
+            "used_blocks": used,
+            "utilization": used / self.num_blocks,
+            "filled_slots": total_filled,
+            "slot_utilization": (total_filled / (used * self.bs)) if used else 0.0,
+        }
+
+    def state(self) -> dict:
+        """Full state snapshot for bit-exact comparison."""
+        return {
+            "free": list(self.free),
+            "tables": {s: list(t) for s, t in sorted(self.tables.items())},
+            "counts": dict(sorted(self.counts.items())),
+            "ref": list(self.ref),
+        }

@@ -1,0 +1,73 @@
+"""Decode attention over a paged KV cache, in float64. TEST INFRASTRUCTURE.
+
+What is computed (one new query token per sequence):
+  1. Gather: walk the sequence's block table, logical block i -> physical
+     block table[i], and copy tokens 0..L-1 into a contiguous buffer
+     ("From OOM to Smooth Inference (RAG memory management)", §2.1;
+     "Inference Engine Memory Optimisation", §2.2). fp16 values convert to
+     float64 exactly; fp8 bytes become decode(byte) * scale
+     ("Where Did the VRAM Go (KV cache tutorial)", §6.1).
+  2. For query head h, the KV head is h // (Hq / Hkv) (contiguous groups; the
+     pages do not say, this is the reading taken).
+  3. z_t = sm_scale * <q_h, K_t>;  p_t = exp(z_t - max z);  out = sum p_t V_t / sum p_t.
+     This is plain softmax attention, which the pages take as given.
+  4. A sequence of length 0 has output 0 (0/0 read as 0).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fp8
+
+
+def gather_sequence(cache, table, length, block_size, kv_dtype="f16", scale=1.0):
+    """Contiguous [length, Hkv, D] float64 copy of one sequence's K or V."""
+    cache = np.asarray(cache)
+    hkv, d = cache.shape[1], cache.shape[3]
+    out = np.empty((length, hkv, d), dtype=np.float64)
+    for t in range(0, length, block_size):
+        phys = int(table[t // block_size])
+        n = min(block_size, length - t)
+        rows = cache[phys, :, :n, :]  # [Hkv, n, D]
+        if kv_dtype == "fp8":
+            vals = fp8.dequantize(rows, scale)
+        else:
+            vals = rows.astype(np.float64)
+        out[t:t + n] = np.transpose(vals, (1, 0, 2))
+    return out
+
+
+def attend_one(q_h, K, V, sm_scale):
+    """softmax(sm_scale * K q) weighted sum of V rows, float64. K, V: [L, D]."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    z = sm_scale * (K @ np.asarray(q_h, dtype=np.float64))
+    p = np.exp(z - z.max())
+    return (p @ V) / p.sum()
+
+
+def decode_attention(q, k_cache, v_cache, block_tables, ctx_lens, block_size,
+                     sm_scale, kv_dtype="f16", k_scale=1.0, v_scale=1.0,
+                     seqs=None, heads=None):
+    """Reference output [B, Hq, D] float64 for one decode token per sequence.
+
+    q: [B, Hq, D] float16. block_tables: per-sequence lists (or rows of an
+    array) of physical block ids. seqs / heads restrict the computation to
+    a sample (other entries are left NaN).
+    """
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    hkv = np.asarray(k_cache).shape[1]
+    if Hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // hkv
+    out = np.full((B, Hq, D), np.nan, dtype=np.float64)
+    seq_ids = range(B) if seqs is None else seqs
+    for s in seq_ids:
+        L = int(ctx_lens[s])
+        K = gather_sequence(k_cache, block_tables[s], L, block_size, kv_dtype, k_scale)
+        V = gather_sequence(v_cache, block_tables[s], L, block_size, kv_dtype, v_scale)
+        for h in (range(Hq) if heads is None else heads):
+            kv = h // group
+            out[s, h] = attend_one(q[s, h], K[:, kv, :], V[:, kv, :], sm_scale)
+    return out

@@ -1,0 +1,108 @@
+"""Drive a workload script through the oracle. TEST INFRASTRUCTURE.
+
+One round = apply its block-manager operations in order, copy every
+copy-on-write pair the round produced, then write the round's new tokens at
+their slots. This is the lifecycle of "From OOM to Smooth Inference (RAG
+memory management)", §2.3 (allocate, append, release) with the sharing and
+copy-on-write of "vLLM Architecture and Memory Use, ch. 3", §3.2-3.3.
+A decode step is one such round (one appended token per sequence) followed by
+decode attention over the batch.
+
+Unused cache slots start as a NaN bit pattern (0x7E00 for float16, 0x7F for
+e4m3fn) so that a kernel reading past a sequence's tokens shows up.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .allocator import BlockAllocatorModel
+from .attention import decode_attention
+from .cache_ops import block_copy, scatter
+
+F16_NAN_BITS = 0x7E00
+FP8_NAN_BITS = 0x7F
+
+
+def empty_cache(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype):
+    shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    if kv_dtype == "fp8":
+        return np.full(shape, FP8_NAN_BITS, dtype=np.uint8)
+    return np.full(shape, F16_NAN_BITS, dtype=np.uint16).view(np.float16)
+
+
+@dataclass
+class RoundResult:
+    slots: list
+    cow_pairs: list
+
+
+@dataclass
+class OracleRun:
+    alloc: BlockAllocatorModel
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    outputs: list = field(default_factory=list)  # per decode step, [B, Hq, D] float64
+    tables: list = field(default_factory=list)  # per decode step, list of tables
+    ctx_lens: list = field(default_factory=list)  # per decode step
+    rounds: list = field(default_factory=list)  # RoundResult per applied round
+
+
+def apply_ops(alloc: BlockAllocatorModel, ops) -> RoundResult:
+    slots, pairs = [], []
+    for op in ops:
+        if op.kind == "allocate":
+            slots += alloc.allocate(op.seq, op.n)
+        elif op.kind == "append":
+            r = alloc.append(op.seq, op.n)
+            slots += r.slots
+            if r.cow_src >= 0:
+                pairs.append((r.cow_src, r.cow_dst))
+        elif op.kind == "share_prefix":
+            alloc.share_prefix(op.src, op.n, op.seq)
+        elif op.kind == "fork":
+            alloc.fork(op.src, op.seq)
+        elif op.kind == "free":
+            alloc.free_seq(op.seq)
+        else:
+            raise ValueError(op.kind)
+    return RoundResult(slots, pairs)
+
+
+def run_round(wl, alloc, k_cache, v_cache, ops) -> RoundResult:
+    res = apply_ops(alloc, ops)
+    block_copy(k_cache, v_cache, res.cow_pairs)
+    K, V = wl.round_kv(ops)
+    scatter(k_cache, v_cache, K, V, res.slots, wl.block_size, wl.kv_dtype,
+            wl.k_inv_scale, wl.v_inv_scale)
+    return res
+
+
+def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) -> OracleRun:
+    """Apply the setup rounds and `steps` decode steps; attention after each step.
+
+    seqs / heads restrict attention to a sample of batch positions / query heads.
+    """
+    alloc = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
+    kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    run_ = OracleRun(alloc, kc, vc)
+    for ops in wl.setup_rounds:
+        r = run_round(wl, alloc, kc, vc, ops)
+        if keep_rounds:
+            run_.rounds.append(r)
+    for step in range(steps):
+        ops = wl.step_ops(step)
+        r = run_round(wl, alloc, kc, vc, ops)
+        if keep_rounds:
+            run_.rounds.append(r)
+        tables = [alloc.block_table(s) for s in wl.batch]
+        lens = [alloc.num_tokens(s) for s in wl.batch]
+        out = decode_attention(wl.queries(step), kc, vc, tables, lens, wl.block_size,
+                               wl.sm_scale, wl.kv_dtype, wl.k_scale, wl.v_scale,
+                               seqs=seqs, heads=heads)
+        run_.outputs.append(out)
+        run_.tables.append(tables)
+        run_.ctx_lens.append(lens)
+    return run_

@@ -1,0 +1,359 @@
+"""Seeded synthetic workloads for the paged-KV decode path.
+
+This module is the only code that both the CPU oracle (``oracle/``) and the
+HIP library's tests and benchmark use. It holds shapes, random draws and the
+scripts of block-manager operations, and nothing of the method's arithmetic:
+no slot computation, no cache writes, no fp8 encoding, no attention.
+
+Each workload is shaped like a model that the pages on paged KV caches use as
+an example. Random draws come from NumPy's PCG64, one independent stream per
+purpose, keyed by ``SeedSequence([seed, stream, index...])``, so any piece
+(one operation's K/V rows, one step's queries) can be regenerated alone:
+
+    stream 0  sequence lengths
+    stream 1  initial free-block order (a permutation of the pool)
+    stream 2  queries, one draw per decode step
+    stream 3  K then V rows of one token-creating operation
+
+K/V/Q values are float32 N(0, 1) draws rounded to float16.
+
+A workload is a script: setup rounds, then decode steps. A round is a list of
+operations applied to the block manager in order; the tokens that the round
+creates are then written (after any copy-on-write block copies the round
+produced). Each decode step appends one token to every sequence of the batch
+and then runs attention for the batch.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+STREAM_LENGTHS = 0
+STREAM_PERM = 1
+STREAM_Q = 2
+STREAM_KV = 3
+
+
+def rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key])))
+
+
+@dataclass(frozen=True)
+class Op:
+    """One block-manager call.
+
+    kind: "allocate" (seq, n tokens), "append" (seq, n tokens),
+          "share_prefix" (src -> seq, n blocks), "fork" (src -> seq).
+    key:  index of the op's K/V draw in stream 3 (token-creating ops only).
+    """
+    kind: str
+    seq: int
+    n: int = 0
+    src: int = -1
+    key: int = -1
+
+    @property
+    def creates_tokens(self) -> bool:
+        return self.kind in ("allocate", "append") and self.n > 0
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    description: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    kv_dtype: str  # "f16" or "fp8"
+    num_blocks: int
+    free_order: np.ndarray  # int32 permutation of the pool
+    batch: list  # sequence ids, in batch order
+    setup_rounds: list  # list[list[Op]]
+    max_steps: int  # decode steps the pool is sized for
+    max_blocks_per_seq: int  # block-table width that fits max_steps steps
+    k_scale: float = 1.0  # fp8 dequantisation scales (float32 values)
+    v_scale: float = 1.0
+    k_inv_scale: float = 1.0  # fp8 quantisation multipliers (float32 values)
+    v_inv_scale: float = 1.0
+    meta: dict = field(default_factory=dict)
+
+    # ------------------------------------------------------------ derived
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def step_ops(self, step: int) -> list:
+        """Decode step `step` (0-based): append one token to every batch sequence."""
+        if step >= self.max_steps:
+            raise ValueError(f"workload sized for {self.max_steps} decode steps")
+        base = 1_000_000 + step * len(self.batch)
+        return [Op("append", s, 1, key=base + i) for i, s in enumerate(self.batch)]
+
+    def queries(self, step: int) -> np.ndarray:
+        g = rng(self.seed, STREAM_Q, step)
+        B = len(self.batch)
+        return g.standard_normal((B, self.num_q_heads, self.head_dim), dtype=np.float32).astype(np.float16)
+
+    def op_kv(self, op: Op):
+        """(K, V) float16 [n, Hkv, D] for a token-creating op."""
+        g = rng(self.seed, STREAM_KV, op.key)
+        shape = (op.n, self.num_kv_heads, self.head_dim)
+        k = g.standard_normal(shape, dtype=np.float32).astype(np.float16)
+        v = g.standard_normal(shape, dtype=np.float32).astype(np.float16)
+        return k, v
+
+    def round_kv(self, ops, threads: int = 8):
+        """Concatenated (K, V) of a round's token-creating ops, in op order."""
+        ops = [o for o in ops if o.creates_tokens]
+        hkv, d = self.num_kv_heads, self.head_dim
+        if not ops:
+            z = np.zeros((0, hkv, d), dtype=np.float16)
+            return z, z.copy()
+        total = sum(o.n for o in ops)
+        K = np.empty((total, hkv, d), dtype=np.float16)
+        V = np.empty((total, hkv, d), dtype=np.float16)
+        offs = np.cumsum([0] + [o.n for o in ops])
+
+        def fill(i):
+            k, v = self.op_kv(ops[i])
+            K[offs[i]:offs[i + 1]] = k
+            V[offs[i]:offs[i + 1]] = v
+
+        if threads > 1 and len(ops) > 1:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(fill, range(len(ops))))
+        else:
+            for i in range(len(ops)):
+                fill(i)
+        return K, V
+
+    def summary(self) -> dict:
+        return {
+            "workload": self.name,
+            "batch": len(self.batch),
+            "q_heads": self.num_q_heads,
+            "kv_heads": self.num_kv_heads,
+            "head_dim": self.head_dim,
+            "block_size": self.block_size,
+            "kv_dtype": self.kv_dtype,
+            "num_blocks": self.num_blocks,
+            **self.meta,
+        }
+
+
+# ---------------------------------------------------------------- builders
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def _perm(seed, n):
+    return rng(seed, STREAM_PERM).permutation(n).astype(np.int32)
+
+
+def _fp8_scales(wl: Workload, steps: int):
+    """Per-tensor scale max|x| / 448 over every K (resp. V) value the
+    workload generates for its setup and first `steps` decode steps, in
+    float32; the multiplier is float32(1) / scale."""
+    kmax = np.float32(0)
+    vmax = np.float32(0)
+    ops = [o for r in wl.setup_rounds for o in r]
+    for s in range(steps):
+        ops += wl.step_ops(s)
+    for o in ops:
+        if o.creates_tokens:
+            k, v = wl.op_kv(o)
+            kmax = max(kmax, np.abs(k.astype(np.float32)).max())
+            vmax = max(vmax, np.abs(v.astype(np.float32)).max())
+    ks = np.float32(kmax) / np.float32(448.0)
+    vs = np.float32(vmax) / np.float32(448.0)
+    wl.k_scale, wl.v_scale = float(ks), float(vs)
+    wl.k_inv_scale = float(np.float32(1.0) / ks)
+    wl.v_inv_scale = float(np.float32(1.0) / vs)
+
+
+def tiny(max_steps: int = 2) -> Workload:
+    """4 sequences of lengths 37, 100, 16, 250 (attended at the first step);
+    8 query heads = 8 KV heads, head_dim 64, block size 16, a 64-block pool in a
+    seeded random order. Each sequence holds L-1 tokens before the first
+    decode step, so step 0 writes position L-1 and attends L tokens, and step 1
+    writes position L (the length-16 sequence crosses into a second block)."""
+    seed = 1
+    lengths = [37, 100, 16, 250]
+    nb = 64
+    setup = [[Op("allocate", s, L - 1, key=s) for s, L in enumerate(lengths)]]
+    return Workload(
+        name="tiny_paged_decode", seed=seed,
+        description="4 seqs L={37,100,16,250}, 8/8 heads, D=64, bs=16, 64-block pool",
+        num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=16, kv_dtype="f16",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(4)),
+        setup_rounds=setup, max_steps=max_steps,
+        max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, 16),
+        meta={"lengths": lengths},
+    )
+
+
+def llama2_7b(max_steps: int = 128, batch: int = 64) -> Workload:
+    """Llama-2-7B-shaped single layer: 32 query heads = 32 KV heads, head_dim
+    128, block size 16, batch 64, attended lengths uniform on [128, 2048];
+    pool = 1.1 x the blocks the batch needs through max_steps decode steps,
+    in a seeded random order."""
+    seed = 2
+    bs = 16
+    L = rng(seed, STREAM_LENGTHS).integers(128, 2048, size=batch, endpoint=True).tolist()
+    need = sum(_ceil_div(l + max_steps, bs) for l in L)
+    nb = math.ceil(1.1 * need)
+    setup = [[Op("allocate", s, l - 1, key=s) for s, l in enumerate(L)]]
+    return Workload(
+        name="llama2_7b_decode_b64", seed=seed,
+        description="Llama-2-7B-shaped layer: 32/32 heads, D=128, bs=16, batch 64, L~U[128,2048]",
+        num_q_heads=32, num_kv_heads=32, head_dim=128, block_size=bs, kv_dtype="f16",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(batch)),
+        setup_rounds=setup, max_steps=max_steps,
+        max_blocks_per_seq=_ceil_div(max(L) - 1 + max_steps, bs),
+        meta={"lengths": L},
+    )
+
+
+def qwen3_prefix(max_steps: int = 32, batch: int = 256) -> Workload:
+    """Qwen3-0.6B-shaped grouped-query layer: 16 query heads over 8 KV heads,
+    head_dim 128, block size 16, batch 256. Sequence 0 holds a 1024-token
+    system-prompt prefix (64 blocks); sequences 1..255 share it through
+    share_prefix (refcount 256); every sequence then appends a suffix of
+    uniform length in [16, 3072] tokens (the last suffix token is written by
+    the first decode step)."""
+    seed = 3
+    bs = 16
+    prefix = 1024
+    pblocks = prefix // bs
+    suffix = rng(seed, STREAM_LENGTHS).integers(16, 3072, size=batch, endpoint=True).tolist()
+    need = pblocks + sum(_ceil_div(s + max_steps, bs) for s in suffix)
+    nb = math.ceil(1.1 * need)
+    r0 = [Op("allocate", 0, prefix, key=0)]
+    r1 = [Op("share_prefix", s, pblocks, src=0) for s in range(1, batch)]
+    r2 = [Op("append", s, suffix[s] - 1, key=1 + s) for s in range(batch) if suffix[s] > 1]
+    lengths = [prefix + s for s in suffix]
+    return Workload(
+        name="qwen3_0p6b_gqa_prefix_b256", seed=seed,
+        description="Qwen3-0.6B-shaped GQA 16/8 heads, D=128, bs=16, batch 256, "
+                    "shared 1024-token prefix + suffix~U[16,3072]",
+        num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=bs, kv_dtype="f16",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(batch)),
+        setup_rounds=[r0, r1, r2], max_steps=max_steps,
+        max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, bs),
+        meta={"lengths": lengths, "prefix_tokens": prefix},
+    )
+
+
+def opt13b_rag(max_steps: int = 32, batch: int = 128) -> Workload:
+    """OPT-13B-shaped RAG decode: 40 query heads = 40 KV heads, head_dim 128,
+    block size 32, batch 128, attended lengths round(N(3000, 400)) clipped to
+    [1024, 4096]; each decode step writes one token per sequence through its
+    slot and appends a block when the last one is full."""
+    seed = 4
+    bs = 32
+    g = rng(seed, STREAM_LENGTHS)
+    L = np.clip(np.rint(g.normal(3000.0, 400.0, size=batch)), 1024, 4096).astype(int).tolist()
+    need = sum(_ceil_div(l + max_steps, bs) for l in L)
+    nb = math.ceil(1.1 * need)
+    setup = [[Op("allocate", s, l - 1, key=s) for s, l in enumerate(L)]]
+    return Workload(
+        name="opt13b_rag_decode_b128", seed=seed,
+        description="OPT-13B-shaped layer: 40/40 heads, D=128, bs=32, batch 128, L~N(3000,400) in [1024,4096]",
+        num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=bs, kv_dtype="f16",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(batch)),
+        setup_rounds=setup, max_steps=max_steps,
+        max_blocks_per_seq=_ceil_div(max(L) - 1 + max_steps, bs),
+        meta={"lengths": L},
+    )
+
+
+def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4) -> Workload:
+    """Beam / parallel-sampling decode with an fp8 e4m3 KV cache: 64 query
+    heads over 8 KV heads, head_dim 128, block size 64. 32 prompts of uniform
+    length in [512, 2048] are allocated (beam 0 of each prompt holds it) and
+    written in one call; each is forked to 3 more beams (refcount 4). Every beam
+    then grows a private tail of uniform length in [1, 128] tokens, one token
+    per beam per round in sequence order, so the first three beams to write
+    into a partially filled shared prompt block copy it and the last one
+    writes in place; the last tail token is written by the first decode step.
+    K and V each use one float32 scale max|x|/448 over the data generated."""
+    seed = 5
+    bs = 64
+    g = rng(seed, STREAM_LENGTHS)
+    P = g.integers(512, 2048, size=prompts, endpoint=True).tolist()
+    T = g.integers(1, 128, size=(prompts, beams), endpoint=True).tolist()
+    seq = lambda i, b: i * beams + b  # noqa: E731
+    r0 = [Op("allocate", seq(i, 0), P[i], key=i) for i in range(prompts)]
+    r1 = [Op("fork", seq(i, b), src=seq(i, 0)) for i in range(prompts) for b in range(1, beams)]
+    rounds = [r0, r1]
+    key = prompts
+    max_tail = max(max(t) for t in T)
+    for r in range(max_tail - 1):
+        ops = []
+        for i in range(prompts):
+            for b in range(beams):
+                if T[i][b] - 1 > r:
+                    ops.append(Op("append", seq(i, b), 1, key=key))
+                    key += 1
+        if ops:
+            rounds.append(ops)
+    need = 0
+    for i in range(prompts):
+        full = P[i] // bs
+        need += full + sum(_ceil_div(P[i] + T[i][b] + max_steps, bs) - full for b in range(beams))
+    nb = math.ceil(1.1 * need)
+    lengths = [P[i] + T[i][b] for i in range(prompts) for b in range(beams)]
+    wl = Workload(
+        name="beam4_fp8_gqa64x8", seed=seed,
+        description="32 prompts x beam 4, fp8 e4m3 KV (per-tensor scale), 64/8 heads, D=128, bs=64, "
+                    "prompt~U[512,2048], tails~U[1,128] with copy-on-write",
+        num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=bs, kv_dtype="fp8",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(prompts * beams)),
+        setup_rounds=rounds, max_steps=max_steps,
+        max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, bs),
+        meta={"lengths": lengths, "prompts": P, "tails": T},
+    )
+    _fp8_scales(wl, max_steps)
+    return wl
+
+
+CONFIGS = {
+    1: tiny,
+    2: llama2_7b,
+    3: qwen3_prefix,
+    4: opt13b_rag,
+    5: beam_fp8,
+}
+
+
+def make(config: int, **kw) -> Workload:
+    return CONFIGS[config](**kw)
+
+
+def small_custom(seed: int, lengths, num_q_heads, num_kv_heads, head_dim, block_size,
+                 kv_dtype="f16", num_blocks=None, max_steps=1, slack=1.25) -> Workload:
+    """A plain workload of independent sequences for edge-case tests."""
+    L = list(lengths)
+    need = sum(_ceil_div(max(l, 0) + max_steps, block_size) for l in L)
+    nb = num_blocks if num_blocks is not None else max(1, math.ceil(slack * need))
+    setup = [[Op("allocate", s, max(l - 1, 0), key=s) for s, l in enumerate(L)]]
+    wl = Workload(
+        name=f"custom_{seed}", seed=seed, description="edge-case workload",
+        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        block_size=block_size, kv_dtype=kv_dtype, num_blocks=nb, free_order=_perm(seed, nb),
+        batch=list(range(len(L))), setup_rounds=setup, max_steps=max_steps,
+        max_blocks_per_seq=max(1, _ceil_div(max(L + [1]) - 1 + max_steps, block_size)),
+        meta={"lengths": L},
+    )
+    if kv_dtype == "fp8":
+        _fp8_scales(wl, max_steps)
+    return wl
