@@ -1,0 +1,290 @@
+"""Benchmark of the paged KV decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 2] [--flush]
+
+One step = the whole hot path for one batch: host block-manager bookkeeping
+(append one token per sequence), one host-to-device copy of the step's
+metadata, copy-on-write block copies (if any), paged_kv_write of the new
+tokens, paged_attn_decode (partition pass + reduce pass). Inputs are resident
+in HBM before the timed region; the setup (prompt writes) is untimed.
+
+Default workload: Llama-2-7B-shaped single layer, batch 64, 32/32 heads,
+head_dim 128, block size 16, fp16 KV, context lengths uniform in [128, 2048].
+
+Printed: one JSON line. `value` is the whole-step throughput in GB/s of
+algorithmic bytes (K/V read by attention, queries, block tables, context
+lengths, output, plus the bytes paged_kv_write and paged_block_copy move) over
+the wall time of the timed steps. `roofline` is for the dominant kernel, the
+attention partition pass: its algorithmic bytes per launch over its average
+launch duration measured with HIP events on the stream it runs on.
+`cpu_baseline` is the CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + KV tokens read/sec"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "paged_kv_cache_60_amd", "csrc", "attn_decode.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def attention_bytes(ctx, hq, hkv, d, bs, elem):
+    """Algorithmic bytes of one decode-attention call: (partition pass, total)."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    B = len(ctx)
+    kv = int((ctx * hkv * d * 2 * elem).sum())
+    tables = int(((ctx + bs - 1) // bs).sum()) * 4
+    q_in = B * hq * d * 2
+    out = B * hq * d * 2
+    p1 = kv + q_in + tables + 4 * B
+    return p1, p1 + out
+
+
+def write_bytes(T, hkv, d, elem):
+    return T * hkv * d * (2 + elem) * 2 + 8 * T
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """Oracle timing on the host: gather + fp64 attention for whole sequences of
+    the workload, sequence by sequence until ~target_s of work is done."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oattn
+    from oracle import cache_ops
+    from oracle.allocator import BlockAllocatorModel
+    from oracle.runner import empty_cache
+
+    alloc = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
+    kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    order = list(wl.batch)
+    # setup + one decode step, on the host model, writing every sequence's tokens
+    for ops in wl.setup_rounds + [wl.step_ops(0)]:
+        for op in ops:
+            if op.kind == "allocate":
+                slots = alloc.allocate(op.seq, op.n)
+            elif op.kind == "append":
+                r = alloc.append(op.seq, op.n)
+                slots = r.slots
+                if r.cow_src >= 0:
+                    cache_ops.block_copy(kc, vc, [(r.cow_src, r.cow_dst)])
+            elif op.kind == "share_prefix":
+                alloc.share_prefix(op.src, op.n, op.seq)
+                continue
+            elif op.kind == "fork":
+                alloc.fork(op.src, op.seq)
+                continue
+            if op.n:
+                K, V = wl.op_kv(op)
+                cache_ops.scatter(kc, vc, K, V, slots, wl.block_size, wl.kv_dtype,
+                                  wl.k_inv_scale, wl.v_inv_scale)
+    q = wl.queries(0)
+    tables = [alloc.block_table(s) for s in order]
+    lens = [alloc.num_tokens(s) for s in order]
+    done, tokens, elapsed = [], 0, 0.0
+    with threadpool_limits(limits=1):
+        for i in range(len(order)):
+            t0 = time.perf_counter()
+            oattn.decode_attention(q, kc, vc, tables, lens, wl.block_size, wl.sm_scale, wl.kv_dtype,
+                                   wl.k_scale, wl.v_scale, seqs=[i])
+            elapsed += time.perf_counter() - t0
+            done.append(i)
+            tokens += lens[i]
+            if elapsed >= target_s:
+                break
+    elem = 1 if wl.kv_dtype == "fp8" else 2
+    _, nbytes = attention_bytes([lens[i] for i in done], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, elem)
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"gather + fp64 attention of {len(done)} of {len(order)} sequences "
+                  f"({tokens} KV tokens, all {wl.num_q_heads} query heads) of one decode step, "
+                  f"{elapsed:.1f} s on one host core",
+        "kv_tokens_per_s": round(tokens / elapsed, 1),
+    }
+
+
+def load_counters(config_name):
+    """HBM bytes per pass-1 launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(config_name)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (2 = Llama-2-7B batch 64)")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--flush", action="store_true", help="evict L2/MALL between steps (time by events)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path does not "
+              f"shard across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from paged_kv_cache_60_amd import _lib, harness
+    from paged_kv_cache_60_amd import ops as kops
+    _lib.load()  # fail loudly if the HIP library is missing
+
+    total_steps = args.warmup + args.steps
+    wl = workloads.make(args.config, max_steps=total_steps + 1)
+    log(f"bench: {wl.name}: setup")
+    dev = torch.device("cuda")
+    eng = harness.make_engine(wl, poison=False)
+    harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
+    eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, args.partition)
+    part = args.partition or int(_lib.load().paged_attn_default_partition(
+        wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, 1 if wl.kv_dtype == "fp8" else 0))
+
+    # stage every step's inputs in HBM before timing
+    B = len(wl.batch)
+    inputs = [harness.step_inputs(wl, s) for s in range(total_steps)]
+    out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float16, device=dev)
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev) if args.flush else None
+    elem = 1 if wl.kv_dtype == "fp8" else 2
+    torch.cuda.synchronize()
+
+    def one_step(s, ev=None):
+        half, n_cow = eng.host_step()
+        eng.upload(half)
+        k, v, q = inputs[s]
+        if n_cow:
+            kops.paged_block_copy(eng.k_cache, eng.v_cache, eng.cow_dev[:n_cow])
+        kops.paged_kv_write(k, v, eng.k_cache, eng.v_cache, eng.slots_dev, eng.kv_dtype,
+                            eng.k_inv_scale, eng.v_inv_scale)
+        if ev is not None:
+            ev[0].record()
+        eng.attend(q, out, passes=1)
+        if ev is not None:
+            ev[1].record()
+        eng.attend(q, out, passes=2)
+        return n_cow
+
+    log(f"bench: warmup {args.warmup}")
+    for s in range(args.warmup):
+        one_step(s)
+        if flush_buf is not None:
+            flush_buf.zero_()
+    torch.cuda.synchronize()
+
+    cow_total = 0
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = args.warmup + i
+        step_ev[i][0].record()
+        cow_total += one_step(s, ev_pairs[i])
+        step_ev[i][1].record()
+        if flush_buf is not None:
+            flush_buf.zero_()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # context lengths of the timed steps: the final lengths minus the steps after each
+    _, ctx_final = eng.host_tables()
+    ctx_steps = [ctx_final - (args.steps - 1 - i) for i in range(args.steps)]
+    p1_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    p1_bytes = [attention_bytes(c, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, elem)[0]
+                for c in ctx_steps]
+    tot_bytes = [attention_bytes(c, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, elem)[1]
+                 + write_bytes(B, wl.num_kv_heads, wl.head_dim, elem) for c in ctx_steps]
+    tot_bytes[-1] += cow_total * eng.block_bytes * 4  # read + write, K and V
+    kv_tokens = sum(int(c.sum()) for c in ctx_steps)
+
+    if args.flush:
+        elapsed = sum(step_ms) / 1e3  # GPU time of the steps, flushes excluded
+    else:
+        elapsed = wall
+    ms_per_step = elapsed / args.steps * 1e3
+    value = sum(tot_bytes) / elapsed / 1e9
+    p1_avg_s = sum(p1_ms) / len(p1_ms) / 1e3
+    achieved = (sum(p1_bytes) / len(p1_bytes)) / p1_avg_s / 1e9
+    traffic = load_counters(wl.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.kv_dtype == "f16" else "fp8e4m3-kv/f16",
+        "data": "synthetic",
+        "config": {
+            **wl.summary(),
+            "mean_ctx_len": round(float(np.mean([c.mean() for c in ctx_steps])), 1),
+            "partition_tokens": part,
+            "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "kv_tokens_per_s": round(kv_tokens / elapsed, 1),
+        "attention_pass1_us": round(p1_avg_s * 1e6, 2),
+        "step_gpu_us": round(float(np.mean(step_ms)) * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "attn_partition_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(workloads.make(args.config, max_steps=1), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

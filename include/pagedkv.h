@@ -1,0 +1,223 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged KV cache decode path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on paged KV caches / PagedAttention):
+ *   [OOM]    "From OOM to Smooth Inference (RAG memory management)"
+ *   [ENGINE] "Inference Engine Memory Optimisation (KV Cache to Continuous Batching)"
+ *   [VRAM]   "Where Did the VRAM Go (KV cache tutorial)"
+ *   [VLLM]   "vLLM Architecture and Memory Use, ch. 3"
+ *
+ * Conventions shared by every call
+ *   - KV cache layout, for K and for V alike: [num_blocks][num_kv_heads]
+ *     [block_size][head_dim], contiguous, element type fp16 or OCP fp8 e4m3fn
+ *     (one byte). Physical block b, KV head h, offset o starts at element
+ *     ((b * num_kv_heads + h) * block_size + o) * head_dim.
+ *   - A slot is block * block_size + offset ([OOM] §2.1: logical block i of
+ *     a sequence lives in physical block table[i]).
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - Device pointers are owned by the caller and must stay valid until the
+ *     work queued on `stream` has finished. `stream` is a hipStream_t passed
+ *     as void* (NULL = the null stream). Kernels allocate nothing and return
+ *     as soon as the work is queued.
+ *   - Every call returns a pkv_status. Argument errors are detected on the
+ *     host before anything is queued and leave all state unchanged.
+ *   - Out-of-range indices that only the device can see (a slot, a block
+ *     id in a table or a copy pair) are skipped rather than followed, so a
+ *     bad index never reads or writes outside the buffers given.
+ *   - head_dim is 64 or 128; block_size is 16, 32 or 64 (bs is a multiple of
+ *     16); num_q_heads is num_kv_heads times 1, 2, 4 or 8.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1, /* bad argument or shape; nothing done            */
+  PKV_ERR_OOM = -2,     /* block pool exhausted; nothing done            */
+  PKV_ERR_NO_SEQ = -3,  /* unknown sequence id; nothing done             */
+  PKV_ERR_EXISTS = -4,  /* sequence id already live; nothing done        */
+  PKV_ERR_HIP = -5      /* the HIP runtime refused a launch              */
+} pkv_status;
+
+typedef enum { PKV_KV_F16 = 0, PKV_KV_FP8_E4M3 = 1 } pkv_kv_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_str(int status);
+
+/* ======================================================================
+ * Device kernels
+ * ==================================================================== */
+
+/*
+ * paged_kv_write -- scatter new K/V rows into their paged slots.
+ * [OOM] §2.3 (allocation and append map each new token to a slot of a
+ * physical block); [VRAM] §6.1-6.2 (fp8 storage with a scale).
+ *
+ *   k_new, v_new   device, fp16 [num_tokens][num_kv_heads][head_dim]
+ *   k_cache/v_cache device, cache layout above, dtype kv_dtype
+ *   slot_mapping   device, int64 [num_tokens]; -1 = skip this token.
+ *                  Slots outside [0, num_blocks*block_size) are skipped.
+ *   kv_dtype       PKV_KV_F16: the fp16 bits are copied unchanged.
+ *                  PKV_KV_FP8_E4M3: byte = e4m3(float32(x) * inv_scale),
+ *                  rounded to nearest even, saturated to +-448.
+ *   k/v_inv_scale  fp8 only: multiplier applied before encoding (1/scale).
+ * Two valid tokens must not share a slot (the later write would race).
+ */
+int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                   int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                   float k_inv_scale, float v_inv_scale, void* stream);
+
+/*
+ * paged_block_copy -- whole-block copy for copy-on-write.
+ * [VLLM] §3.3 (a write into a shared block first copies it to a new block);
+ * [OOM] §6.1 (forked beams copy only their last block).
+ *
+ *   pairs        device, int32 [num_pairs][2] = (src block, dst block);
+ *                pairs with an id outside [0, num_blocks) are skipped.
+ *   block_bytes  bytes of one block of one cache
+ *                (= num_kv_heads * block_size * head_dim * element size);
+ *                must be a multiple of 16. K and V are both copied.
+ * No dst may equal another pair's src or dst (copy-on-write destinations
+ * are fresh blocks, so this always holds for the block manager's pairs).
+ */
+int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                     int num_blocks, size_t block_bytes, void* stream);
+
+/*
+ * paged_attn_decode -- one query token per sequence attends over its paged
+ * K/V: out[s][h] = sum_t softmax_t(sm_scale * q[s][h].K_t) V_t over the
+ * ctx_lens[s] tokens reached through block_tables[s] ([OOM] §2.1-2.3,
+ * [ENGINE] §2.2). Split-sequence: pass 1 handles partitions of
+ * `partition_tokens` tokens per (sequence, KV head) with an online softmax and
+ * writes (max, sum, unnormalised output) partials; pass 2 combines them.
+ * A sequence that fits in one partition is finished by pass 1.
+ *
+ *   out            device, fp16 [num_seqs][num_q_heads][head_dim]
+ *   q              device, fp16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables   device, int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(ctx_len/block_size) are never read.
+ *   ctx_lens       device, int32 [num_seqs], tokens to attend (includes the
+ *                  token written this step). Clamped to
+ *                  max_blocks_per_seq*block_size; 0 gives a zero output.
+ *   sm_scale       softmax scale (1/sqrt(head_dim) usually).
+ *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale).
+ *   partition_tokens 0 = library default; else a multiple of 64, >= 64.
+ *   workspace      device, >= paged_attn_decode_workspace_bytes(...) bytes
+ *                  (fp32 partials; contents on entry are ignored).
+ * Results are deterministic: they do not depend on block placement.
+ */
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                         int max_blocks_per_seq, int block_size,
+                                         int partition_tokens);
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                      int partition_tokens, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Same as paged_attn_decode, restricted to pass 1 (passes = 1), pass 2
+ * (passes = 2) or both (passes = 3). Queuing pass 1 then pass 2 with the
+ * same arguments is identical to paged_attn_decode; it exists so that each
+ * pass can be timed on its own. */
+int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                             int partition_tokens, void* workspace, size_t workspace_bytes,
+                             int passes, void* stream);
+
+/* The partition size the library uses when partition_tokens is 0. */
+int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int kv_dtype);
+
+/* ======================================================================
+ * Host block manager
+ * A FIFO pool of physical blocks, per-sequence block tables and token
+ * counts, per-block reference counts ([OOM] §2.3; [ENGINE] §3;
+ * [VLLM] §3.2-3.3). Host memory only; not thread-safe per handle. Output
+ * arrays are copies into caller buffers. A failing call changes no state.
+ * ==================================================================== */
+
+typedef struct pkv_bm pkv_bm;
+
+typedef struct {
+  int32_t total_blocks;
+  int32_t free_blocks;
+  int32_t used_blocks;    /* total - free                                    */
+  int32_t live_seqs;
+  int64_t filled_slots;   /* token slots holding data, shared blocks once    */
+  double utilization;     /* used / total ([ENGINE] §3 utilisation)          */
+  double slot_utilization;/* filled_slots / (used * block_size), 0 if unused */
+} pkv_bm_stats_t;
+
+/* New manager over blocks 0..num_blocks-1. free_order (host, may be NULL =
+ * ascending) is the initial FIFO order and must be a permutation. */
+int pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order, pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* New sequence holding num_tokens (>= 0) tokens: pops ceil(n/bs) blocks from
+ * the front of the pool. slots_out (host, may be NULL) receives the n slots.
+ * EXISTS if seq is live, OOM if the pool is short. [ENGINE] §3, [OOM] §2.3. */
+int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out);
+
+/* Append n_tokens (>= 0) to seq. If the first new position falls inside the
+ * current last block and that block is shared (refcount > 1), a fresh block
+ * replaces it in the table (copy-on-write, [VLLM] §3.3) and cow_src / cow_dst
+ * receive the pair to copy (else -1/-1). New blocks are popped for the rest.
+ * slots_out (may be NULL) receives the n slots. */
+int pkv_bm_append(pkv_bm* bm, int64_t seq, int n_tokens, int64_t* slots_out,
+                  int32_t* cow_src, int32_t* cow_dst);
+
+/* Append one token to each of n_seqs sequences, in order (a decode step).
+ * slot_mapping_out[n_seqs] gets each token's slot; cow_pairs_out[2*n_seqs]
+ * gets the copy-on-write pairs in order, *n_cow their count. All or nothing:
+ * on OOM/NO_SEQ no sequence is changed. Duplicate ids are INVALID. */
+int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int* n_cow);
+
+/* child shares every block of parent (refcount +1 each) and its token
+ * count: beams / parallel samples ([VLLM] §3.2). */
+int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
+
+/* dst's table is src's first n_blocks blocks (refcount +1 each); dst's token
+ * count is min(n_blocks*bs, src's count). INVALID if n_blocks exceeds src's
+ * table. [ENGINE] §3 share_prefix. */
+int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst);
+
+/* Release seq: refcount -1 on each block in table order; blocks reaching 0
+ * go to the back of the pool. [OOM] §2.3, [ENGINE] §3, [VLLM] §3.2. */
+int pkv_bm_free(pkv_bm* bm, int64_t seq);
+
+/* Queries. Arrays are host buffers of `cap` entries; *n gets the count. */
+int pkv_bm_slots(const pkv_bm* bm, int64_t seq, int start, int n, int64_t* out);
+int pkv_bm_block_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* n);
+int pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq, int* n);
+int pkv_bm_refcount(const pkv_bm* bm, int32_t block, int* rc);
+int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n); /* FIFO order */
+int pkv_bm_num_free(const pkv_bm* bm);
+int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out);
+
+/* Decode-batch export: tables_out[n_seqs][max_blocks] (-1 padded) and
+ * ctx_lens_out[n_seqs] for the listed sequences. INVALID if a table is
+ * wider than max_blocks. */
+int pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* tables_out,
+                  int max_blocks, int32_t* ctx_lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,108 @@
+"""ctypes loader for libpagedkv.so (argument marshalling only).
+
+The library is built in-tree (``python -m paged_kv_cache_60_amd.build``) and
+loaded from this package's directory. There is no fallback: if the library is
+missing the import of the GPU entry points fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID = -1
+PKV_ERR_OOM = -2
+PKV_ERR_NO_SEQ = -3
+PKV_ERR_EXISTS = -4
+PKV_ERR_HIP = -5
+
+KV_F16 = 0
+KV_FP8_E4M3 = 1
+
+_c_int = ctypes.c_int
+_c_i64 = ctypes.c_int64
+_c_f = ctypes.c_float
+_c_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_p_i32 = ctypes.POINTER(ctypes.c_int32)
+_p_i64 = ctypes.POINTER(ctypes.c_int64)
+_p_int = ctypes.POINTER(ctypes.c_int)
+
+
+class PkvStats(ctypes.Structure):
+    _fields_ = [
+        ("total_blocks", ctypes.c_int32),
+        ("free_blocks", ctypes.c_int32),
+        ("used_blocks", ctypes.c_int32),
+        ("live_seqs", ctypes.c_int32),
+        ("filled_slots", ctypes.c_int64),
+        ("utilization", ctypes.c_double),
+        ("slot_utilization", ctypes.c_double),
+    ]
+
+
+# name -> (restype, argtypes); every symbol include/pagedkv.h declares.
+SIGNATURES = {
+    "pkv_status_str": (ctypes.c_char_p, [_c_int]),
+    "paged_kv_write": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _c_f, _c_f, _vp]),
+    "paged_block_copy": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_sz, _vp]),
+    "paged_attn_decode_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "paged_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _c_int, _vp,
+                                   _c_sz, _vp]),
+    "paged_attn_decode_passes": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f,
+                                          _c_int, _vp, _c_sz, _c_int, _vp]),
+    "paged_attn_default_partition": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_bm_create": (_c_int, [_c_int, _c_int, _p_i32, ctypes.POINTER(_vp)]),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_allocate": (_c_int, [_vp, _c_i64, _c_int, _p_i64]),
+    "pkv_bm_append": (_c_int, [_vp, _c_i64, _c_int, _p_i64, _p_i32, _p_i32]),
+    "pkv_bm_append_batch": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int]),
+    "pkv_bm_fork": (_c_int, [_vp, _c_i64, _c_i64]),
+    "pkv_bm_share_prefix": (_c_int, [_vp, _c_i64, _c_int, _c_i64]),
+    "pkv_bm_free": (_c_int, [_vp, _c_i64]),
+    "pkv_bm_slots": (_c_int, [_vp, _c_i64, _c_int, _c_int, _p_i64]),
+    "pkv_bm_block_table": (_c_int, [_vp, _c_i64, _p_i32, _c_int, _p_int]),
+    "pkv_bm_num_tokens": (_c_int, [_vp, _c_i64, _p_int]),
+    "pkv_bm_refcount": (_c_int, [_vp, ctypes.c_int32, _p_int]),
+    "pkv_bm_free_list": (_c_int, [_vp, _p_i32, _c_int, _p_int]),
+    "pkv_bm_num_free": (_c_int, [_vp]),
+    "pkv_bm_stats": (_c_int, [_vp, ctypes.POINTER(PkvStats)]),
+    "pkv_bm_export": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_i32]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpagedkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_60_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = load().pkv_status_str(code).decode()
+        super().__init__(f"{where}: {msg} ({code})")
+        self.code = code
+
+
+def check(code: int, where: str) -> None:
+    if code != PKV_OK:
+        raise PkvError(code, where)

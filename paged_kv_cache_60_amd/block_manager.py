@@ -1,0 +1,158 @@
+"""Python handle over the C++ block manager (pkv_bm_* in include/pagedkv.h)."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _lib
+from ._lib import PkvError, check
+
+
+@dataclass
+class AppendResult:
+    slots: list
+    cow_src: int
+    cow_dst: int
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _i64p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+class BlockManager:
+    """FIFO pool of physical blocks, block tables, refcounts (host, C++)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        lib = _lib.load()
+        self._lib = lib
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = ctypes.c_void_p()
+        if free_order is None:
+            st = lib.pkv_bm_create(self.num_blocks, self.block_size, None, ctypes.byref(h))
+        else:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.shape != (self.num_blocks,):
+                raise PkvError(_lib.PKV_ERR_INVALID, "pkv_bm_create")
+            st = lib.pkv_bm_create(self.num_blocks, self.block_size, _i32p(order), ctypes.byref(h))
+        check(st, "pkv_bm_create")
+        self._h = h
+        # scratch for decode steps
+        self._cow_buf = np.empty(0, dtype=np.int32)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass
+
+    # ------------------------------------------------------------ operations
+    def allocate(self, seq: int, num_tokens: int) -> list:
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        check(self._lib.pkv_bm_allocate(self._h, seq, num_tokens, _i64p(slots) if num_tokens > 0 else None),
+              "pkv_bm_allocate")
+        return slots.tolist()
+
+    def allocate_np(self, seq: int, num_tokens: int) -> np.ndarray:
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        check(self._lib.pkv_bm_allocate(self._h, seq, num_tokens, _i64p(slots) if num_tokens > 0 else None),
+              "pkv_bm_allocate")
+        return slots
+
+    def append(self, seq: int, n: int = 1) -> AppendResult:
+        slots = np.empty(max(n, 0), dtype=np.int64)
+        cs = ctypes.c_int32(-1)
+        cd = ctypes.c_int32(-1)
+        check(self._lib.pkv_bm_append(self._h, seq, n, _i64p(slots) if n > 0 else None,
+                                      ctypes.byref(cs), ctypes.byref(cd)), "pkv_bm_append")
+        return AppendResult(slots.tolist(), cs.value, cd.value)
+
+    def append_batch(self, seqs: np.ndarray, slot_out: np.ndarray, cow_out: np.ndarray) -> int:
+        """One token for each sequence; fills slot_out[n] and cow_out[2n]; returns #pairs."""
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_append_batch(self._h, _i64p(seqs), len(seqs), _i64p(slot_out),
+                                            _i32p(cow_out), ctypes.byref(n)), "pkv_bm_append_batch")
+        return n.value
+
+    def fork(self, parent: int, child: int) -> None:
+        check(self._lib.pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")
+
+    def share_prefix(self, src: int, num_blocks: int, dst: int) -> None:
+        check(self._lib.pkv_bm_share_prefix(self._h, src, num_blocks, dst), "pkv_bm_share_prefix")
+
+    def free_seq(self, seq: int) -> None:
+        check(self._lib.pkv_bm_free(self._h, seq), "pkv_bm_free")
+
+    # ------------------------------------------------------------ queries
+    def slots(self, seq: int, start: int, n: int) -> list:
+        out = np.empty(max(n, 0), dtype=np.int64)
+        check(self._lib.pkv_bm_slots(self._h, seq, start, n, _i64p(out) if n > 0 else None), "pkv_bm_slots")
+        return out.tolist()
+
+    def block_table(self, seq: int) -> list:
+        n = ctypes.c_int(0)
+        ntok = self.num_tokens(seq)
+        cap = max(1, -(-ntok // self.block_size))
+        out = np.empty(cap, dtype=np.int32)
+        check(self._lib.pkv_bm_block_table(self._h, seq, _i32p(out), cap, ctypes.byref(n)),
+              "pkv_bm_block_table")
+        return out[:n.value].tolist()
+
+    def num_tokens(self, seq: int) -> int:
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_num_tokens(self._h, seq, ctypes.byref(n)), "pkv_bm_num_tokens")
+        return n.value
+
+    def refcount(self, block: int) -> int:
+        rc = ctypes.c_int(0)
+        check(self._lib.pkv_bm_refcount(self._h, block, ctypes.byref(rc)), "pkv_bm_refcount")
+        return rc.value
+
+    def free_list(self) -> list:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_free_list(self._h, _i32p(out), self.num_blocks, ctypes.byref(n)),
+              "pkv_bm_free_list")
+        return out[:n.value].tolist()
+
+    def available_blocks(self) -> int:
+        return self._lib.pkv_bm_num_free(self._h)
+
+    def stats(self) -> dict:
+        s = _lib.PkvStats()
+        check(self._lib.pkv_bm_stats(self._h, ctypes.byref(s)), "pkv_bm_stats")
+        return {
+            "free_blocks": s.free_blocks,
+            "live_seqs": s.live_seqs,
+            "used_blocks": s.used_blocks,
+            "utilization": s.utilization,
+            "filled_slots": s.filled_slots,
+            "slot_utilization": s.slot_utilization,
+        }
+
+    def export(self, seqs: np.ndarray, tables_out: np.ndarray, ctx_out: np.ndarray) -> None:
+        """Fill tables_out [n, max_blocks] (-1 padded) and ctx_out [n] (int32)."""
+        check(self._lib.pkv_bm_export(self._h, _i64p(seqs), len(seqs), _i32p(tables_out),
+                                      tables_out.shape[1], _i32p(ctx_out)), "pkv_bm_export")
+
+    def state(self, seqs) -> dict:
+        """Snapshot comparable with the oracle model's state() for the given live ids."""
+        tables = {int(s): self.block_table(int(s)) for s in sorted(seqs)}
+        counts = {int(s): self.num_tokens(int(s)) for s in sorted(seqs)}
+        return {
+            "free": self.free_list(),
+            "tables": tables,
+            "counts": counts,
+            "ref": [self.refcount(b) for b in range(self.num_blocks)],
+        }

@@ -1,0 +1,353 @@
+// Host block manager of the paged KV cache.
+//
+// A FIFO pool of physical block ids, per-sequence block tables and token
+// counts, and per-block reference counts.
+//   - Pool popped at the front, released to the back, ceil(tokens/bs) blocks
+//     per sequence, check-before-pop on exhaustion:
+//     "From OOM to Smooth Inference (RAG memory management)", §2.3.
+//   - Reference counts, allocate / append / free / share-prefix, utilisation:
+//     "Inference Engine Memory Optimisation (KV Cache to Continuous Batching)", §3.
+//   - Forked sequences share blocks; copy-on-write of a shared block:
+//     "vLLM Architecture and Memory Use, ch. 3", §3.2-3.3.
+// The last block's fill is derived from the sequence's own token count, so two
+// sequences sharing a block never update a common counter. Every call checks
+// before it mutates: a failing call leaves the state as it was.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> table;
+  int64_t count = 0;
+};
+
+// What one append changed, so that a failed batch can be rolled back exactly.
+struct AppendUndo {
+  int64_t seq;
+  int64_t prev_count;
+  int grown;        // blocks pushed at the end of the table
+  int32_t cow_src;  // -1: no copy-on-write
+  int32_t cow_dst;
+};
+
+}  // namespace
+
+struct pkv_bm {
+  int32_t num_blocks;
+  int32_t bs;
+  std::deque<int32_t> free_q;
+  std::unordered_map<int64_t, Seq> seqs;
+  std::vector<int32_t> ref;
+
+  int64_t needed(int64_t tokens) const { return (tokens + bs - 1) / bs; }
+
+  int64_t slot(const std::vector<int32_t>& t, int64_t pos) const {
+    return static_cast<int64_t>(t[pos / bs]) * bs + pos % bs;
+  }
+
+  int32_t pop() {
+    int32_t b = free_q.front();
+    free_q.pop_front();
+    return b;
+  }
+
+  // Append n tokens to s; the caller has checked that s exists.
+  int append_one(int64_t id, Seq& s, int n, int64_t* slots, int32_t* cow_src,
+                 int32_t* cow_dst, AppendUndo* undo) {
+    if (n < 0) return PKV_ERR_INVALID;
+    int32_t csrc = -1, cdst = -1;
+    if (n == 0) {
+      if (cow_src) *cow_src = -1;
+      if (cow_dst) *cow_dst = -1;
+      if (undo) *undo = AppendUndo{id, s.count, 0, -1, -1};
+      return PKV_OK;
+    }
+    const bool cow = !s.table.empty() && (s.count % bs) != 0 && ref[s.table.back()] > 1;
+    const int64_t grow = needed(s.count + n) - static_cast<int64_t>(s.table.size());
+    const int64_t need = grow + (cow ? 1 : 0);
+    if (static_cast<int64_t>(free_q.size()) < need) return PKV_ERR_OOM;
+    if (cow) {
+      csrc = s.table.back();
+      cdst = pop();
+      ref[csrc] -= 1;
+      ref[cdst] += 1;
+      s.table.back() = cdst;
+    }
+    for (int64_t i = 0; i < grow; ++i) {
+      int32_t b = pop();
+      ref[b] += 1;
+      s.table.push_back(b);
+    }
+    const int64_t prev = s.count;
+    s.count += n;
+    if (slots)
+      for (int64_t p = prev; p < s.count; ++p) slots[p - prev] = slot(s.table, p);
+    if (cow_src) *cow_src = csrc;
+    if (cow_dst) *cow_dst = cdst;
+    if (undo) *undo = AppendUndo{id, prev, static_cast<int>(grow), csrc, cdst};
+    return PKV_OK;
+  }
+
+  void undo_append(const AppendUndo& u) {
+    Seq& s = seqs.at(u.seq);
+    // Blocks were popped in the order: cow dst, then grown blocks. Put them
+    // back at the front in reverse order so the pool is exactly as before.
+    for (int i = 0; i < u.grown; ++i) {
+      int32_t b = s.table.back();
+      s.table.pop_back();
+      ref[b] -= 1;
+      free_q.push_front(b);
+    }
+    if (u.cow_src >= 0) {
+      s.table.back() = u.cow_src;
+      ref[u.cow_src] += 1;
+      ref[u.cow_dst] -= 1;
+      free_q.push_front(u.cow_dst);
+    }
+    s.count = u.prev_count;
+  }
+};
+
+extern "C" {
+
+const char* pkv_status_str(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_OOM: return "block pool exhausted";
+    case PKV_ERR_NO_SEQ: return "unknown sequence";
+    case PKV_ERR_EXISTS: return "sequence already exists";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order, pkv_bm** out) {
+  if (!out) return PKV_ERR_INVALID;
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0) return PKV_ERR_INVALID;
+  std::vector<int32_t> order(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) return PKV_ERR_INVALID;
+      seen[b] = 1;
+      order[i] = b;
+    }
+  } else {
+    for (int i = 0; i < num_blocks; ++i) order[i] = i;
+  }
+  pkv_bm* bm = new (std::nothrow) pkv_bm;
+  if (!bm) return PKV_ERR_OOM;
+  bm->num_blocks = num_blocks;
+  bm->bs = block_size;
+  bm->free_q.assign(order.begin(), order.end());
+  bm->ref.assign(num_blocks, 0);
+  *out = bm;
+  return PKV_OK;
+}
+
+void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out) {
+  if (!bm || num_tokens < 0) return PKV_ERR_INVALID;
+  if (bm->seqs.count(seq)) return PKV_ERR_EXISTS;
+  const int64_t nb = bm->needed(num_tokens);
+  if (static_cast<int64_t>(bm->free_q.size()) < nb) return PKV_ERR_OOM;
+  Seq s;
+  s.table.reserve(nb);
+  for (int64_t i = 0; i < nb; ++i) {
+    int32_t b = bm->pop();
+    bm->ref[b] += 1;
+    s.table.push_back(b);
+  }
+  s.count = num_tokens;
+  if (slots_out)
+    for (int64_t p = 0; p < num_tokens; ++p) slots_out[p] = bm->slot(s.table, p);
+  bm->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_bm_append(pkv_bm* bm, int64_t seq, int n_tokens, int64_t* slots_out, int32_t* cow_src,
+                  int32_t* cow_dst) {
+  if (!bm) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  return bm->append_one(seq, it->second, n_tokens, slots_out, cow_src, cow_dst, nullptr);
+}
+
+int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int* n_cow) {
+  if (!bm || n_seqs < 0 || (n_seqs > 0 && (!seqs || !slot_mapping_out || !cow_pairs_out)) || !n_cow)
+    return PKV_ERR_INVALID;
+  std::unordered_set<int64_t> uniq;
+  uniq.reserve(n_seqs * 2 + 1);
+  for (int i = 0; i < n_seqs; ++i) {
+    if (!uniq.insert(seqs[i]).second) return PKV_ERR_INVALID;
+    if (!bm->seqs.count(seqs[i])) return PKV_ERR_NO_SEQ;
+  }
+  std::vector<AppendUndo> log;
+  log.reserve(n_seqs);
+  int ncow = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    Seq& s = bm->seqs.at(seqs[i]);
+    int32_t cs, cd;
+    AppendUndo u;
+    int st = bm->append_one(seqs[i], s, 1, &slot_mapping_out[i], &cs, &cd, &u);
+    if (st != PKV_OK) {
+      for (auto r = log.rbegin(); r != log.rend(); ++r) bm->undo_append(*r);
+      return st;
+    }
+    log.push_back(u);
+    if (cs >= 0) {
+      cow_pairs_out[2 * ncow] = cs;
+      cow_pairs_out[2 * ncow + 1] = cd;
+      ++ncow;
+    }
+  }
+  *n_cow = ncow;
+  return PKV_OK;
+}
+
+int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  if (bm->seqs.count(child)) return PKV_ERR_EXISTS;
+  Seq c = it->second;
+  for (int32_t b : c.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child, std::move(c));
+  return PKV_OK;
+}
+
+int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst) {
+  if (!bm) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(src);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  if (bm->seqs.count(dst)) return PKV_ERR_EXISTS;
+  const Seq& s = it->second;
+  if (n_blocks < 0 || n_blocks > static_cast<int>(s.table.size())) return PKV_ERR_INVALID;
+  Seq d;
+  d.table.assign(s.table.begin(), s.table.begin() + n_blocks);
+  for (int32_t b : d.table) bm->ref[b] += 1;
+  d.count = std::min<int64_t>(static_cast<int64_t>(n_blocks) * bm->bs, s.count);
+  bm->seqs.emplace(dst, std::move(d));
+  return PKV_OK;
+}
+
+int pkv_bm_free(pkv_bm* bm, int64_t seq) {
+  if (!bm) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  for (int32_t b : it->second.table) {
+    bm->ref[b] -= 1;
+    if (bm->ref[b] == 0) bm->free_q.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_bm_slots(const pkv_bm* bm, int64_t seq, int start, int n, int64_t* out) {
+  if (!bm || start < 0 || n < 0 || (n > 0 && !out)) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  const Seq& s = it->second;
+  if (static_cast<int64_t>(start) + n > s.count) return PKV_ERR_INVALID;
+  for (int i = 0; i < n; ++i) out[i] = bm->slot(s.table, static_cast<int64_t>(start) + i);
+  return PKV_OK;
+}
+
+int pkv_bm_block_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* n) {
+  if (!bm || !n || cap < 0) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  const auto& t = it->second.table;
+  if (static_cast<int>(t.size()) > cap || (!t.empty() && !out)) return PKV_ERR_INVALID;
+  std::copy(t.begin(), t.end(), out);
+  *n = static_cast<int>(t.size());
+  return PKV_OK;
+}
+
+int pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq, int* n) {
+  if (!bm || !n) return PKV_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  *n = static_cast<int>(it->second.count);
+  return PKV_OK;
+}
+
+int pkv_bm_refcount(const pkv_bm* bm, int32_t block, int* rc) {
+  if (!bm || !rc || block < 0 || block >= bm->num_blocks) return PKV_ERR_INVALID;
+  *rc = bm->ref[block];
+  return PKV_OK;
+}
+
+int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n) {
+  if (!bm || !n || cap < 0) return PKV_ERR_INVALID;
+  if (static_cast<int>(bm->free_q.size()) > cap || (!bm->free_q.empty() && !out))
+    return PKV_ERR_INVALID;
+  std::copy(bm->free_q.begin(), bm->free_q.end(), out);
+  *n = static_cast<int>(bm->free_q.size());
+  return PKV_OK;
+}
+
+int pkv_bm_num_free(const pkv_bm* bm) {
+  return bm ? static_cast<int>(bm->free_q.size()) : PKV_ERR_INVALID;
+}
+
+int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out) {
+  if (!bm || !out) return PKV_ERR_INVALID;
+  std::vector<int32_t> filled(bm->num_blocks, 0);
+  for (const auto& kv : bm->seqs) {
+    const Seq& s = kv.second;
+    for (size_t i = 0; i < s.table.size(); ++i) {
+      int64_t f = s.count - static_cast<int64_t>(i) * bm->bs;
+      f = std::max<int64_t>(0, std::min<int64_t>(bm->bs, f));
+      filled[s.table[i]] = std::max<int32_t>(filled[s.table[i]], static_cast<int32_t>(f));
+    }
+  }
+  int64_t total_filled = 0;
+  for (int32_t f : filled) total_filled += f;
+  out->total_blocks = bm->num_blocks;
+  out->free_blocks = static_cast<int32_t>(bm->free_q.size());
+  out->used_blocks = bm->num_blocks - out->free_blocks;
+  out->live_seqs = static_cast<int32_t>(bm->seqs.size());
+  out->filled_slots = total_filled;
+  out->utilization = static_cast<double>(out->used_blocks) / bm->num_blocks;
+  out->slot_utilization =
+      out->used_blocks ? static_cast<double>(total_filled) / (static_cast<double>(out->used_blocks) * bm->bs)
+                       : 0.0;
+  return PKV_OK;
+}
+
+int pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* tables_out,
+                  int max_blocks, int32_t* ctx_lens_out) {
+  if (!bm || n_seqs < 0 || max_blocks < 0) return PKV_ERR_INVALID;
+  if (n_seqs > 0 && (!seqs || !tables_out || !ctx_lens_out)) return PKV_ERR_INVALID;
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+    if (static_cast<int>(it->second.table.size()) > max_blocks) return PKV_ERR_INVALID;
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    const Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks;
+    std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + s.table.size(), row + max_blocks, -1);
+    ctx_lens_out[i] = static_cast<int32_t>(s.count);
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

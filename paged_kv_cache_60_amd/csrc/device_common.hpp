@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16); every lane of the
+// group receives the group's total. Uses DPP butterflies: xor 1, xor 2, then
+// the half-row and row mirrors, which pair each quad (half row) with the other.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) v += dpp_f32<kDppQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp_f32<kDppQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// dot of two packed fp16 pairs, accumulated in fp32
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+__device__ __forceinline__ float h_lo(uint32_t a) { return (float)__builtin_bit_cast(f16x2, a).x; }
+__device__ __forceinline__ float h_hi(uint32_t a) { return (float)__builtin_bit_cast(f16x2, a).y; }
+
+// Two e4m3fn bytes (in the low 16 bits of `pair` as byte0, byte1) as two fp16
+// values scaled by 2^-8, exactly: the 7 magnitude bits of each byte become
+// bits 7..13 of an fp16 (exponent field low 4 bits + top 3 mantissa bits), so
+// e4m3 exponent e (bias 7) lands on fp16 exponent e (bias 15), i.e. the value
+// times 2^-8; subnormals map onto fp16 subnormals the same way. The sign moves
+// to bit 15. Caller multiplies by 256 (folded into the scales).
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2_scaled(uint32_t pair) {
+  // put byte0 in bits 8..15 and byte1 in bits 24..31
+  uint32_t t = ((pair & 0xFFu) << 8) | ((pair & 0xFF00u) << 16);
+  uint32_t sign = t & 0x80008000u;
+  uint32_t mag = (t >> 1) & 0x3F803F80u;
+  return sign | mag;
+}
+
+}  // namespace pkv

@@ -1,0 +1,125 @@
+// paged_kv_write: scatter each new token's K and V rows into its paged slot.
+//
+// The slot of a token comes from the host block manager; slot = block *
+// block_size + offset ("From OOM to Smooth Inference (RAG memory
+// management)", §2.1 and §2.3). With an fp8 cache each value is stored as
+// e4m3(float32(x) * inv_scale) ("Where Did the VRAM Go (KV cache tutorial)",
+// §6.1-6.2), rounded to nearest even and saturated to +-448.
+//
+// One thread moves 8 consecutive elements of one (token, head) row: a 16-byte
+// load of fp16 and a 16-byte (fp16) or 8-byte (fp8) store, so a wave covers
+// whole rows with coalesced accesses on both sides.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "device_common.hpp"
+
+namespace pkv {
+namespace {
+
+// e4m3fn byte for a float: round to nearest even, saturate to +-448, keep the
+// sign of zero, NaN -> 0x7F. All steps are exact except the final rint, which
+// is the rounding itself.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(f);
+  if (!(a == a)) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
+    const float q = __builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal, code 0x08
+    return sign | (uint32_t)q;
+  }
+  int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;  // -6..8
+  float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));                 // 8..16
+  if (q == 16.0f) {
+    q = 8.0f;
+    e += 1;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)q - 8u);
+}
+
+template <bool FP8>
+__global__ void __launch_bounds__(256)
+kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+                uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                const int64_t* __restrict__ slots, int64_t total_chunks, int chunks_per_token,
+                int chunks_per_row, int64_t num_slots, int bs, int64_t row_stride_blk,
+                int head_dim, float k_inv, float v_inv) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
+    const int64_t t = i / chunks_per_token;
+    const int within = (int)(i - t * chunks_per_token);
+    const int h = within / chunks_per_row;
+    const int ch = within - h * chunks_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / bs;
+    const int off = (int)(slot - blk * bs);
+    // element index of the destination chunk
+    const int64_t dst = (blk * row_stride_blk + (int64_t)h * bs + off) * head_dim + (int64_t)ch * 8;
+    const u32x4 kv = k_new[i];
+    const u32x4 vv = v_new[i];
+    if constexpr (!FP8) {
+      *reinterpret_cast<u32x4*>(k_cache + dst * 2) = kv;
+      *reinterpret_cast<u32x4*>(v_cache + dst * 2) = vv;
+    } else {
+      u32x2 ko, vo;
+      for (int w = 0; w < 2; ++w) {
+        uint32_t kb = 0, vb = 0;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t kw = kv[w * 2 + j / 2];
+          const uint32_t vw = vv[w * 2 + j / 2];
+          const float kf = (j & 1) ? h_hi(kw) : h_lo(kw);
+          const float vf = (j & 1) ? h_hi(vw) : h_lo(vw);
+          kb |= e4m3_rne_sat(__fmul_rn(kf, k_inv)) << (8 * j);
+          vb |= e4m3_rne_sat(__fmul_rn(vf, v_inv)) << (8 * j);
+        }
+        ko[w] = kb;
+        vo[w] = vb;
+      }
+      *reinterpret_cast<u32x2*>(k_cache + dst) = ko;
+      *reinterpret_cast<u32x2*>(v_cache + dst) = vo;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                              int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                              float k_inv_scale, float v_inv_scale, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID;
+  const int chunks_per_row = head_dim / 8;
+  const int chunks_per_token = chunks_per_row * num_kv_heads;
+  const int64_t total = (int64_t)num_tokens * chunks_per_token;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const int64_t row_stride_blk = (int64_t)num_kv_heads * block_size;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* kn = static_cast<const pkv::u32x4*>(k_new);
+  const auto* vn = static_cast<const pkv::u32x4*>(v_new);
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+  if (kv_dtype == PKV_KV_F16) {
+    hipLaunchKernelGGL(pkv::kv_write_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn,
+                       kc, vc, slot_mapping, total, chunks_per_token, chunks_per_row, num_slots,
+                       block_size, row_stride_blk, head_dim, 1.0f, 1.0f);
+  } else {
+    hipLaunchKernelGGL(pkv::kv_write_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn,
+                       kc, vc, slot_mapping, total, chunks_per_token, chunks_per_row, num_slots,
+                       block_size, row_stride_blk, head_dim, k_inv_scale, v_inv_scale);
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

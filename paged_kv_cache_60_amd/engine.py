@@ -1,0 +1,182 @@
+"""Paged KV cache on one GPU: device caches plus the host block manager.
+
+One decode step, as the pages run it ("From OOM to Smooth Inference (RAG
+memory management)", §2.3: allocate, append per generated token, release;
+"vLLM Architecture and Memory Use, ch. 3", §3.2-3.3: sharing and
+copy-on-write):
+
+  1. host bookkeeping: append one token to every sequence of the batch
+     (one C call); new blocks come from the FIFO pool; a write into a shared,
+     partially filled last block triggers copy-on-write;
+  2. one host-to-device copy of the step's metadata (slot mapping, copy
+     pairs, block tables, context lengths) from a pinned buffer;
+  3. paged_block_copy for the copy-on-write pairs, if any;
+  4. paged_kv_write of the new tokens' K/V;
+  5. paged_attn_decode (partition pass and reduce pass).
+
+Pinned metadata buffers alternate between two halves so the host can prepare
+step k+1 while step k's copy may still be queued; an event per half keeps the
+host from overwriting a half before its copy has run.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ops
+from .block_manager import BlockManager
+
+F16_NAN_BITS = 0x7E00
+FP8_NAN_BITS = 0x7F
+
+
+class PagedKVEngine:
+    def __init__(self, num_blocks, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype="f16",
+                 free_order=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0,
+                 device="cuda", poison=True):
+        self.num_blocks = int(num_blocks)
+        self.hq, self.hkv, self.d, self.bs = int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size)
+        self.kv_dtype = kv_dtype
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.k_inv_scale, self.v_inv_scale = float(k_inv_scale), float(v_inv_scale)
+        self.device = torch.device(device)
+        self.bm = BlockManager(self.num_blocks, self.bs, free_order)
+        shape = (self.num_blocks, self.hkv, self.bs, self.d)
+        dt = ops.cache_torch_dtype(kv_dtype)
+        self.k_cache = torch.empty(shape, dtype=dt, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=dt, device=self.device)
+        if poison:
+            self.poison()
+        self._step_bufs = None
+
+    @property
+    def block_bytes(self) -> int:
+        return self.k_cache[0].numel() * self.k_cache.element_size()
+
+    def poison(self):
+        """Fill every slot with a NaN bit pattern (unused slots must never be read)."""
+        if self.kv_dtype == "f16":
+            for c in (self.k_cache, self.v_cache):
+                c.view(torch.int16).fill_(F16_NAN_BITS)
+        else:
+            for c in (self.k_cache, self.v_cache):
+                c.fill_(FP8_NAN_BITS)
+
+    # ------------------------------------------------------ scripted rounds
+    def apply_ops(self, ops_list):
+        """Run block-manager ops in order; returns (slots int64 array, cow pairs list)."""
+        slots, pairs = [], []
+        bm = self.bm
+        for op in ops_list:
+            if op.kind == "allocate":
+                slots.append(bm.allocate_np(op.seq, op.n))
+            elif op.kind == "append":
+                r = bm.append(op.seq, op.n)
+                slots.append(np.asarray(r.slots, dtype=np.int64))
+                if r.cow_src >= 0:
+                    pairs.append((r.cow_src, r.cow_dst))
+            elif op.kind == "share_prefix":
+                bm.share_prefix(op.src, op.n, op.seq)
+            elif op.kind == "fork":
+                bm.fork(op.src, op.seq)
+            elif op.kind == "free":
+                bm.free_seq(op.seq)
+            else:
+                raise ValueError(op.kind)
+        s = np.concatenate(slots) if slots else np.zeros(0, dtype=np.int64)
+        return s, pairs
+
+    def copy_blocks(self, pairs):
+        if pairs:
+            p = torch.tensor(pairs, dtype=torch.int32).to(self.device, non_blocking=False)
+            ops.paged_block_copy(self.k_cache, self.v_cache, p)
+
+    def write(self, slots, K, V):
+        """Write host K/V [T, Hkv, D] fp16 (numpy or torch) at host slots [T]."""
+        if len(slots) == 0:
+            return
+        kt = torch.as_tensor(K).to(self.device, non_blocking=False)
+        vt = torch.as_tensor(V).to(self.device, non_blocking=False)
+        st = torch.as_tensor(np.ascontiguousarray(slots, dtype=np.int64)).to(self.device)
+        ops.paged_kv_write(kt, vt, self.k_cache, self.v_cache, st, self.kv_dtype,
+                           self.k_inv_scale, self.v_inv_scale)
+
+    # ------------------------------------------------------ decode steps
+    def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0):
+        """Allocate the pinned/device metadata buffers and attention workspace for a batch."""
+        B = len(batch_seqs)
+        self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
+        self.max_blocks = int(max_blocks)
+        self.partition_tokens = int(partition_tokens)
+        # layout (bytes): slots int64[B] | cow int32[2B] | ctx int32[B] | tables int32[B*maxb]
+        o_slots = 0
+        o_cow = o_slots + 8 * B
+        o_ctx = o_cow + 8 * B
+        o_tab = o_ctx + 4 * B
+        total = o_tab + 4 * B * self.max_blocks
+        total = (total + 255) // 256 * 256
+        self._layout = (o_slots, o_cow, o_ctx, o_tab, total)
+        self._pinned = [torch.empty(total, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self._events = [None, None]
+        self._meta_dev = torch.empty(total, dtype=torch.uint8, device=self.device)
+        d = self._meta_dev
+        self.slots_dev = d[o_slots:o_cow].view(torch.int64)
+        self.cow_dev = d[o_cow:o_ctx].view(torch.int32).view(B, 2)
+        self.ctx_dev = d[o_ctx:o_tab].view(torch.int32)
+        self.tables_dev = d[o_tab:o_tab + 4 * B * self.max_blocks].view(torch.int32).view(B, self.max_blocks)
+        wsb = ops.workspace_bytes(B, self.hq, self.d, self.max_blocks, self.bs, self.partition_tokens)
+        self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
+        self._parity = 0
+
+    def host_step(self):
+        """Step part 1: host bookkeeping into the next pinned half; returns (half, n_cow)."""
+        half = self._parity
+        self._parity ^= 1
+        ev = self._events[half]
+        if ev is not None:
+            ev.synchronize()
+        buf = self._pinned[half].numpy()
+        o_slots, o_cow, o_ctx, o_tab, _ = self._layout
+        B = len(self.batch)
+        slots = buf[o_slots:o_cow].view(np.int64)
+        cow = buf[o_cow:o_ctx].view(np.int32)
+        ctx = buf[o_ctx:o_tab].view(np.int32)
+        tab = buf[o_tab:o_tab + 4 * B * self.max_blocks].view(np.int32).reshape(B, self.max_blocks)
+        n_cow = self.bm.append_batch(self.batch, slots, cow)
+        self.bm.export(self.batch, tab, ctx)
+        return half, n_cow
+
+    def upload(self, half):
+        """Step part 2: one async host-to-device copy of the step's metadata."""
+        self._meta_dev.copy_(self._pinned[half], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._events[half] = ev
+
+    def device_step(self, n_cow, k_new, v_new, q, out, passes=3):
+        """Step parts 3-5 on the current stream."""
+        if n_cow:
+            ops.paged_block_copy(self.k_cache, self.v_cache, self.cow_dev[:n_cow])
+        ops.paged_kv_write(k_new, v_new, self.k_cache, self.v_cache, self.slots_dev, self.kv_dtype,
+                           self.k_inv_scale, self.v_inv_scale)
+        self.attend(q, out, passes)
+
+    def attend(self, q, out, passes=3):
+        ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
+                              1.0 / float(self.d) ** 0.5, self.kv_dtype, self.k_scale, self.v_scale,
+                              self.partition_tokens, self.workspace, passes)
+
+    def decode_step(self, k_new, v_new, q, out):
+        """Full decode step: append one token per batch sequence, write it, attend."""
+        half, n_cow = self.host_step()
+        self.upload(half)
+        self.device_step(n_cow, k_new, v_new, q, out)
+        return n_cow
+
+    def host_tables(self):
+        """(tables [B, maxb], ctx [B]) of the current batch, read back from the manager."""
+        B = len(self.batch)
+        tab = np.empty((B, self.max_blocks), dtype=np.int32)
+        ctx = np.empty(B, dtype=np.int32)
+        self.bm.export(self.batch, tab, ctx)
+        return tab, ctx

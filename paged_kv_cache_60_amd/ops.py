@@ -1,0 +1,124 @@
+"""Torch-facing wrappers of the kernel entry points (argument marshalling only).
+
+Every function checks shapes, dtypes and devices, then passes raw device
+pointers and the current HIP stream to libpagedkv.so. All computation happens
+in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PkvError, check
+
+F16 = "f16"
+FP8 = "fp8"
+
+
+def kv_dtype_code(kv_dtype: str) -> int:
+    if kv_dtype == F16:
+        return _lib.KV_F16
+    if kv_dtype == FP8:
+        return _lib.KV_FP8_E4M3
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def cache_torch_dtype(kv_dtype: str) -> torch.dtype:
+    return torch.float16 if kv_dtype == F16 else torch.uint8
+
+
+def _stream_ptr(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(cond: bool, where: str, what: str):
+    if not cond:
+        raise PkvError(_lib.PKV_ERR_INVALID, f"{where}: {what}")
+
+
+def _cache_ok(c: torch.Tensor, kv_dtype: str) -> bool:
+    if not (c.is_cuda and c.is_contiguous() and c.dim() == 4):
+        return False
+    return c.dtype == torch.float16 if kv_dtype == F16 else c.element_size() == 1
+
+
+def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, kv_dtype=F16,
+                   k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
+    """Scatter k_new/v_new [T, Hkv, D] (fp16) into the caches at slot_mapping [T] (int64)."""
+    w = "paged_kv_write"
+    _require(k_new.is_cuda and k_new.dtype == torch.float16 and k_new.is_contiguous(), w, "k_new")
+    _require(v_new.shape == k_new.shape and v_new.dtype == torch.float16 and v_new.is_contiguous(), w, "v_new")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype), w, "caches")
+    _require(k_cache.shape == v_cache.shape, w, "cache shapes")
+    nb, hkv, bs, d = k_cache.shape
+    T = k_new.shape[0]
+    _require(k_new.dim() == 3 and k_new.shape[1] == hkv and k_new.shape[2] == d, w, "k_new shape")
+    _require(slot_mapping.is_cuda and slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
+             and slot_mapping.is_contiguous(), w, "slot_mapping")
+    lib = _lib.load()
+    check(lib.paged_kv_write(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T, nb,
+                             hkv, d, bs, kv_dtype_code(kv_dtype), float(k_inv_scale), float(v_inv_scale),
+                             _stream_ptr(stream)), w)
+
+
+def paged_block_copy(k_cache, v_cache, pairs, stream=None):
+    """Copy whole blocks pairs[i] = (src, dst) (int32 [n, 2] on device) in both caches."""
+    w = "paged_block_copy"
+    _require(k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
+             and k_cache.shape == v_cache.shape and k_cache.dim() == 4, w, "caches")
+    _require(pairs.is_cuda and pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
+             and pairs.is_contiguous(), w, "pairs")
+    nb = k_cache.shape[0]
+    block_bytes = k_cache[0].numel() * k_cache.element_size()
+    lib = _lib.load()
+    check(lib.paged_block_copy(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], nb, block_bytes,
+                               _stream_ptr(stream)), w)
+
+
+def workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens=0) -> int:
+    return int(_lib.load().paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                             max_blocks_per_seq, block_size,
+                                                             partition_tokens))
+
+
+def default_partition(num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype=F16) -> int:
+    return int(_lib.load().paged_attn_default_partition(num_q_heads, num_kv_heads, head_dim, block_size,
+                                                        kv_dtype_code(kv_dtype)))
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale, kv_dtype=F16,
+                      k_scale=1.0, v_scale=1.0, partition_tokens=0, workspace=None, passes=3,
+                      stream=None):
+    """out/q [B, Hq, D] fp16; block_tables [B, max_blocks] int32; ctx_lens [B] int32."""
+    w = "paged_attn_decode"
+    _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
+    _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype) and k_cache.shape == v_cache.shape,
+             w, "caches")
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _require(d == d2, w, "head_dim")
+    _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(), w, "block_tables")
+    _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
+             and ctx_lens.is_contiguous(), w, "ctx_lens")
+    maxb = block_tables.shape[1]
+    need = workspace_bytes(B, hq, d, maxb, bs, partition_tokens) if B > 0 and maxb > 0 else 0
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if need:
+        _require(workspace is not None and workspace.is_cuda
+                 and workspace.numel() * workspace.element_size() >= need, w, "workspace too small")
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check(lib.paged_attn_decode_passes(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), maxb,
+                                       _p(ctx_lens), B, hq, hkv, d, bs, nb, float(sm_scale),
+                                       kv_dtype_code(kv_dtype), float(k_scale), float(v_scale),
+                                       int(partition_tokens), ws_ptr, ws_bytes, int(passes),
+                                       _stream_ptr(stream)), w)

@@ -37,14 +37,14 @@ def run_unit_case(make, case, block_size):
         elif kind == "share_prefix":
             m.share_prefix(op[1], op[2], op[3])
         elif kind == "allocate_fails":
-            before = m.state()
+            before = (m.free_list(), [m.refcount(b) for b in range(case["num_blocks"])])
             try:
                 m.allocate(op[1], op[2])
             except Exception as e:  # noqa: BLE001
                 assert e.code == ERR_CODES[op[3]]
             else:
                 raise AssertionError("allocation should have failed")
-            assert m.state() == before
+            assert (m.free_list(), [m.refcount(b) for b in range(case["num_blocks"])]) == before
         else:
             raise ValueError(kind)
     return m
