@@ -143,6 +143,21 @@ int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, cons
 int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
                                  int block_size, int kv_dtype);
 
+/*
+ * paged_step_metadata -- bring a decode step's metadata to the device.
+ * Copies slot_mapping (int64, n_seqs), ctx_lens (int32, n_seqs) and the
+ * copy-on-write pairs (int32, 2*n_cow) from src buffers into dst buffers and
+ * writes each block-table update (row, logical index, block) -- as produced by
+ * pkv_bm_decode_step -- into block_tables[row * max_blocks + index]
+ * (updates outside [0, num_rows) x [0, max_blocks) are skipped). One small
+ * kernel: the src pointers may be pinned host memory (hipHostMalloc), read
+ * directly by the kernel, so no separate DMA copy is queued.
+ */
+int paged_step_metadata(const int64_t* slots_src, int64_t* slots_dst, const int32_t* ctx_src,
+                        int32_t* ctx_dst, int n_seqs, const int32_t* cow_src, int32_t* cow_dst,
+                        int n_cow, const int32_t* updates, int n_updates, int32_t* block_tables,
+                        int num_rows, int max_blocks, void* stream);
+
 /* ======================================================================
  * Host block manager
  * A FIFO pool of physical blocks, per-sequence block tables and token
@@ -187,6 +202,16 @@ int pkv_bm_append(pkv_bm* bm, int64_t seq, int n_tokens, int64_t* slots_out,
  * on OOM/NO_SEQ no sequence is changed. Duplicate ids are INVALID. */
 int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
                         int32_t* cow_pairs_out, int* n_cow);
+
+/* A decode step's bookkeeping in one call: pkv_bm_append_batch, plus what a
+ * device-resident copy of the batch's block tables needs to stay current.
+ * updates_out[3*k .. 3*k+2] = (batch row, logical block index, physical
+ * block) for every table entry the step added or replaced by copy-on-write
+ * (at most one per sequence), *n_updates their count; ctx_lens_out[n_seqs]
+ * gets the new token counts. Capacity of updates_out: 3*n_seqs. */
+int pkv_bm_decode_step(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                       int32_t* cow_pairs_out, int* n_cow, int32_t* updates_out, int* n_updates,
+                       int32_t* ctx_lens_out);
 
 /* child shares every block of parent (refcount +1 each) and its token
  * count: beams / parallel samples ([VLLM] §3.2). */

@@ -58,11 +58,14 @@ SIGNATURES = {
                                           _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f,
                                           _c_int, _vp, _c_sz, _c_int, _vp]),
     "paged_attn_default_partition": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "paged_step_metadata": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp,
+                                     _c_int, _c_int, _vp]),
     "pkv_bm_create": (_c_int, [_c_int, _c_int, _p_i32, ctypes.POINTER(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_allocate": (_c_int, [_vp, _c_i64, _c_int, _p_i64]),
     "pkv_bm_append": (_c_int, [_vp, _c_i64, _c_int, _p_i64, _p_i32, _p_i32]),
     "pkv_bm_append_batch": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int]),
+    "pkv_bm_decode_step": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int, _p_i32, _p_int, _p_i32]),
     "pkv_bm_fork": (_c_int, [_vp, _c_i64, _c_i64]),
     "pkv_bm_share_prefix": (_c_int, [_vp, _c_i64, _c_int, _c_i64]),
     "pkv_bm_free": (_c_int, [_vp, _c_i64]),

@@ -43,8 +43,6 @@ class BlockManager:
             st = lib.pkv_bm_create(self.num_blocks, self.block_size, _i32p(order), ctypes.byref(h))
         check(st, "pkv_bm_create")
         self._h = h
-        # scratch for decode steps
-        self._cow_buf = np.empty(0, dtype=np.int32)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -84,6 +82,16 @@ class BlockManager:
         check(self._lib.pkv_bm_append_batch(self._h, _i64p(seqs), len(seqs), _i64p(slot_out),
                                             _i32p(cow_out), ctypes.byref(n)), "pkv_bm_append_batch")
         return n.value
+
+    def decode_step(self, seqs: np.ndarray, slot_out: np.ndarray, cow_out: np.ndarray,
+                    upd_out: np.ndarray, ctx_out: np.ndarray):
+        """One token per sequence plus the block-table updates; returns (#pairs, #updates)."""
+        n_cow = ctypes.c_int(0)
+        n_upd = ctypes.c_int(0)
+        check(self._lib.pkv_bm_decode_step(self._h, _i64p(seqs), len(seqs), _i64p(slot_out), _i32p(cow_out),
+                                           ctypes.byref(n_cow), _i32p(upd_out), ctypes.byref(n_upd),
+                                           _i32p(ctx_out)), "pkv_bm_decode_step")
+        return n_cow.value, n_upd.value
 
     def fork(self, parent: int, child: int) -> None:
         check(self._lib.pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")

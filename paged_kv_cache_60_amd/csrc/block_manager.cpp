@@ -187,8 +187,14 @@ int pkv_bm_append(pkv_bm* bm, int64_t seq, int n_tokens, int64_t* slots_out, int
   return bm->append_one(seq, it->second, n_tokens, slots_out, cow_src, cow_dst, nullptr);
 }
 
-int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
-                        int32_t* cow_pairs_out, int* n_cow) {
+}  // extern "C"
+
+namespace {
+
+// One token for each sequence, in order; all or nothing. cow_row (may be
+// null) gets 1 for the rows whose append copied a shared block.
+int append_batch_impl(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                      int32_t* cow_pairs_out, int* n_cow, char* cow_row) {
   if (!bm || n_seqs < 0 || (n_seqs > 0 && (!seqs || !slot_mapping_out || !cow_pairs_out)) || !n_cow)
     return PKV_ERR_INVALID;
   std::unordered_set<int64_t> uniq;
@@ -210,6 +216,7 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* sl
       return st;
     }
     log.push_back(u);
+    if (cow_row) cow_row[i] = cs >= 0;
     if (cs >= 0) {
       cow_pairs_out[2 * ncow] = cs;
       cow_pairs_out[2 * ncow + 1] = cd;
@@ -217,6 +224,47 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* sl
     }
   }
   *n_cow = ncow;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int* n_cow) {
+  return append_batch_impl(bm, seqs, n_seqs, slot_mapping_out, cow_pairs_out, n_cow, nullptr);
+}
+
+int pkv_bm_decode_step(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
+                       int32_t* cow_pairs_out, int* n_cow, int32_t* updates_out, int* n_updates,
+                       int32_t* ctx_lens_out) {
+  if (!bm || !n_updates || n_seqs < 0 || (n_seqs > 0 && (!seqs || !updates_out || !ctx_lens_out)))
+    return PKV_ERR_INVALID;
+  // Table sizes before the step tell which entries the appends replace or add.
+  std::vector<int32_t> before(n_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it != bm->seqs.end()) before[i] = static_cast<int32_t>(it->second.table.size());
+  }
+  std::vector<char> cow_row(n_seqs, 0);
+  const int st = append_batch_impl(bm, seqs, n_seqs, slot_mapping_out, cow_pairs_out, n_cow,
+                                   cow_row.data());
+  if (st != PKV_OK) return st;
+  int nu = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const Seq& s = bm->seqs.at(seqs[i]);
+    const int32_t now = static_cast<int32_t>(s.table.size());
+    const int32_t first = cow_row[i] ? before[i] - 1 : before[i];  // copy-on-write replaced the last entry
+    for (int32_t j = first; j < now; ++j) {
+      updates_out[3 * nu] = i;
+      updates_out[3 * nu + 1] = j;
+      updates_out[3 * nu + 2] = s.table[j];
+      ++nu;
+    }
+    ctx_lens_out[i] = static_cast<int32_t>(s.count);
+  }
+  *n_updates = nu;
   return PKV_OK;
 }
 

@@ -8,15 +8,17 @@ copy-on-write):
   1. host bookkeeping: append one token to every sequence of the batch
      (one C call); new blocks come from the FIFO pool; a write into a shared,
      partially filled last block triggers copy-on-write;
-  2. one host-to-device copy of the step's metadata (slot mapping, copy
-     pairs, block tables, context lengths) from a pinned buffer;
+  2. the step's metadata (slot mapping, context lengths, copy pairs and the
+     block-table entries that changed) goes to the device through one small
+     kernel that reads a pinned host buffer; the block tables themselves stay
+     resident on the device;
   3. paged_block_copy for the copy-on-write pairs, if any;
   4. paged_kv_write of the new tokens' K/V;
   5. paged_attn_decode (partition pass and reduce pass).
 
 Pinned metadata buffers alternate between two halves so the host can prepare
-step k+1 while step k's copy may still be queued; an event per half keeps the
-host from overwriting a half before its copy has run.
+step k+1 while step k's metadata kernel may still be queued; an event per half
+keeps the host from overwriting a half before that kernel has read it.
 """
 from __future__ import annotations
 
@@ -47,7 +49,6 @@ class PagedKVEngine:
         self.v_cache = torch.empty(shape, dtype=dt, device=self.device)
         if poison:
             self.poison()
-        self._step_bufs = None
 
     @property
     def block_bytes(self) -> int:
@@ -103,52 +104,55 @@ class PagedKVEngine:
 
     # ------------------------------------------------------ decode steps
     def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0):
-        """Allocate the pinned/device metadata buffers and attention workspace for a batch."""
+        """Set up a decode batch: device-resident block tables (uploaded once
+        here), the per-step metadata buffers (two pinned halves on the host,
+        one set on the device) and the attention workspace."""
         B = len(batch_seqs)
         self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
         self.max_blocks = int(max_blocks)
         self.partition_tokens = int(partition_tokens)
-        # layout (bytes): slots int64[B] | cow int32[2B] | ctx int32[B] | tables int32[B*maxb]
+        # pinned layout (bytes): slots int64[B] | ctx int32[B] | cow int32[2B] | updates int32[3B]
         o_slots = 0
-        o_cow = o_slots + 8 * B
-        o_ctx = o_cow + 8 * B
-        o_tab = o_ctx + 4 * B
-        total = o_tab + 4 * B * self.max_blocks
-        total = (total + 255) // 256 * 256
-        self._layout = (o_slots, o_cow, o_ctx, o_tab, total)
-        self._pinned = [torch.empty(total, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        o_ctx = o_slots + 8 * B
+        o_cow = o_ctx + 4 * B
+        o_upd = o_cow + 8 * B
+        total = (o_upd + 12 * B + 255) // 256 * 256
+        self._layout = (o_slots, o_ctx, o_cow, o_upd)
+        self._pinned = [torch.empty(max(total, 256), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self._views = []
+        for t in self._pinned:
+            self._views.append((t[o_slots:o_ctx].view(torch.int64), t[o_ctx:o_cow].view(torch.int32),
+                                t[o_cow:o_upd].view(torch.int32), t[o_upd:o_upd + 12 * B].view(torch.int32)))
         self._events = [None, None]
-        self._meta_dev = torch.empty(total, dtype=torch.uint8, device=self.device)
-        d = self._meta_dev
-        self.slots_dev = d[o_slots:o_cow].view(torch.int64)
-        self.cow_dev = d[o_cow:o_ctx].view(torch.int32).view(B, 2)
-        self.ctx_dev = d[o_ctx:o_tab].view(torch.int32)
-        self.tables_dev = d[o_tab:o_tab + 4 * B * self.max_blocks].view(torch.int32).view(B, self.max_blocks)
+        self.slots_dev = torch.empty(B, dtype=torch.int64, device=self.device)
+        self.ctx_dev = torch.empty(B, dtype=torch.int32, device=self.device)
+        self.cow_dev = torch.empty((B, 2), dtype=torch.int32, device=self.device)
+        tab, ctx = self.host_tables()
+        self.tables_dev = torch.from_numpy(tab).to(self.device)
+        self.ctx_dev.copy_(torch.from_numpy(ctx))
         wsb = ops.workspace_bytes(B, self.hq, self.d, self.max_blocks, self.bs, self.partition_tokens)
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
         self._parity = 0
+        torch.cuda.synchronize(self.device)
 
     def host_step(self):
-        """Step part 1: host bookkeeping into the next pinned half; returns (half, n_cow)."""
+        """Step part 1: host bookkeeping into the next pinned half.
+        Returns (half, n_cow, n_updates)."""
         half = self._parity
         self._parity ^= 1
         ev = self._events[half]
         if ev is not None:
             ev.synchronize()
-        buf = self._pinned[half].numpy()
-        o_slots, o_cow, o_ctx, o_tab, _ = self._layout
-        B = len(self.batch)
-        slots = buf[o_slots:o_cow].view(np.int64)
-        cow = buf[o_cow:o_ctx].view(np.int32)
-        ctx = buf[o_ctx:o_tab].view(np.int32)
-        tab = buf[o_tab:o_tab + 4 * B * self.max_blocks].view(np.int32).reshape(B, self.max_blocks)
-        n_cow = self.bm.append_batch(self.batch, slots, cow)
-        self.bm.export(self.batch, tab, ctx)
-        return half, n_cow
+        slots, ctx, cow, upd = (v.numpy() for v in self._views[half])
+        n_cow, n_upd = self.bm.decode_step(self.batch, slots, cow, upd, ctx)
+        return half, n_cow, n_upd
 
-    def upload(self, half):
-        """Step part 2: one async host-to-device copy of the step's metadata."""
-        self._meta_dev.copy_(self._pinned[half], non_blocking=True)
+    def upload(self, half, n_cow, n_upd):
+        """Step part 2: one small kernel reads the pinned half and updates the
+        device slot mapping, context lengths, copy pairs and table entries."""
+        slots, ctx, cow, upd = self._views[half]
+        ops.paged_step_metadata(slots, self.slots_dev, ctx, self.ctx_dev, len(self.batch), cow,
+                                self.cow_dev, n_cow, upd, n_upd, self.tables_dev)
         ev = torch.cuda.Event()
         ev.record()
         self._events[half] = ev
@@ -168,8 +172,8 @@ class PagedKVEngine:
 
     def decode_step(self, k_new, v_new, q, out):
         """Full decode step: append one token per batch sequence, write it, attend."""
-        half, n_cow = self.host_step()
-        self.upload(half)
+        half, n_cow, n_upd = self.host_step()
+        self.upload(half, n_cow, n_upd)
         self.device_step(n_cow, k_new, v_new, q, out)
         return n_cow
 

@@ -122,3 +122,13 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
                                        kv_dtype_code(kv_dtype), float(k_scale), float(v_scale),
                                        int(partition_tokens), ws_ptr, ws_bytes, int(passes),
                                        _stream_ptr(stream)), w)
+
+
+def paged_step_metadata(slots_src, slots_dst, ctx_src, ctx_dst, n_seqs, cow_src, cow_dst, n_cow,
+                        updates_src, n_updates, block_tables, stream=None):
+    """Apply a decode step's metadata (sources: pinned host tensors or device tensors)."""
+    rows, maxb = block_tables.shape
+    lib = _lib.load()
+    check(lib.paged_step_metadata(_p(slots_src), _p(slots_dst), _p(ctx_src), _p(ctx_dst), int(n_seqs),
+                                  _p(cow_src), _p(cow_dst), int(n_cow), _p(updates_src), int(n_updates),
+                                  _p(block_tables), rows, maxb, _stream_ptr(stream)), "paged_step_metadata")

@@ -78,6 +78,13 @@ def test_config5_beam_fp8_full_size():
     _check(wl, steps=2, seqs=sample_seqs(wl.meta["lengths"], 10))
 
 
+def test_copy_on_write_inside_decode_steps():
+    """Every beam's first tail token is written by a decode step: the step's
+    copy-on-write pairs go through paged_step_metadata and paged_block_copy."""
+    wl = workloads.beam_fp8(max_steps=3, prompts=6, tail_max=1)
+    _check(wl, steps=3)
+
+
 @pytest.mark.parametrize("hq,hkv,d,bs,kv", [(8, 8, 64, 16, "f16"), (16, 8, 128, 16, "f16"),
                                            (32, 8, 128, 32, "f16"), (64, 8, 128, 64, "fp8"),
                                            (8, 2, 64, 64, "fp8"), (16, 16, 128, 64, "fp8")])

@@ -137,7 +137,7 @@ class Workload:
         return K, V
 
     def summary(self) -> dict:
-        return {
+        out = {
             "workload": self.name,
             "batch": len(self.batch),
             "q_heads": self.num_q_heads,
@@ -146,8 +146,13 @@ class Workload:
             "block_size": self.block_size,
             "kv_dtype": self.kv_dtype,
             "num_blocks": self.num_blocks,
-            **self.meta,
         }
+        L = self.meta.get("lengths")
+        if L:
+            out.update(ctx_len_min=int(min(L)), ctx_len_max=int(max(L)),
+                       ctx_len_mean=round(float(np.mean(L)), 1))
+        out.update({k: v for k, v in self.meta.items() if not isinstance(v, (list, tuple))})
+        return out
 
 
 # ---------------------------------------------------------------- builders
@@ -276,7 +281,7 @@ def opt13b_rag(max_steps: int = 32, batch: int = 128) -> Workload:
     )
 
 
-def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4) -> Workload:
+def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4, tail_max: int = 128) -> Workload:
     """Beam / parallel-sampling decode with an fp8 e4m3 KV cache: 64 query
     heads over 8 KV heads, head_dim 128, block size 64. 32 prompts of uniform
     length in [512, 2048] are allocated (beam 0 of each prompt holds it) and
@@ -285,12 +290,14 @@ def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4) -> Workload:
     per beam per round in sequence order, so the first three beams to write
     into a partially filled shared prompt block copy it and the last one
     writes in place; the last tail token is written by the first decode step.
-    K and V each use one float32 scale max|x|/448 over the data generated."""
+    K and V each use one float32 scale max|x|/448 over the data generated.
+    tail_max = 1 makes every tail a single token, so all copy-on-write happens
+    inside the first decode step."""
     seed = 5
     bs = 64
     g = rng(seed, STREAM_LENGTHS)
     P = g.integers(512, 2048, size=prompts, endpoint=True).tolist()
-    T = g.integers(1, 128, size=(prompts, beams), endpoint=True).tolist()
+    T = g.integers(1, tail_max, size=(prompts, beams), endpoint=True).tolist()
     seq = lambda i, b: i * beams + b  # noqa: E731
     r0 = [Op("allocate", seq(i, 0), P[i], key=i) for i in range(prompts)]
     r1 = [Op("fork", seq(i, b), src=seq(i, 0)) for i in range(prompts) for b in range(1, beams)]
