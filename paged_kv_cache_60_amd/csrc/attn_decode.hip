@@ -26,7 +26,8 @@
 //     hot loop has no cross-row traffic; rows, then waves (through LDS), are
 //     merged once at the end of the partition.
 //   - All query heads of a GQA group are handled by the workgroup that loads
-//     their KV head, so K/V are read once per group.
+//     their KV head, so K/V are read once per group. Groups of 4 or 8 heads
+//     run on the matrix cores instead (attn_gqa_mfma.hpp).
 //   - A sequence that fits in one partition is normalised and written here.
 // Pass 2 (reduce kernel). One wave per (sequence, query head): combines the
 // partitions' (m, l, o) with weights exp(m_p - max m) and writes fp16.
@@ -377,6 +378,14 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
   for (int e = 0; e < DL; ++e) a.out[(size_t)wid * D + lane * DL + e] = (f16)(acc[e] * inv);
 }
 
+}  // namespace
+}  // namespace pkv
+
+#include "attn_gqa_mfma.hpp"
+
+namespace pkv {
+namespace {
+
 typedef void (*PartFn)(AttnArgs);
 
 template <int D, bool FP8>
@@ -384,8 +393,8 @@ PartFn pick_partition_kernel(int G) {
   switch (G) {
     case 1: return attn_partition_kernel<D, 1, FP8, kWaves>;
     case 2: return attn_partition_kernel<D, 2, FP8, kWaves>;
-    case 4: return attn_partition_kernel<D, 4, FP8, kWaves>;
-    case 8: return attn_partition_kernel<D, 8, FP8, kWaves>;
+    case 4: return attn_partition_mfma_kernel<D, 4, FP8, kWaves>;
+    case 8: return attn_partition_mfma_kernel<D, 8, FP8, kWaves>;
     default: return nullptr;
   }
 }
