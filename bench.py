@@ -39,10 +39,16 @@ PEAK_GBS = 8000.0  # MI355X HBM3E
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
+KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "device_common.hpp")
+
+
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "paged_kv_cache_60_amd", "csrc", "attn_decode.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the sources the attention kernels are built from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_60_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def attention_bytes(ctx, hq, hkv, d, bs, elem):
@@ -165,7 +171,6 @@ def main():
 
     import workloads
     from paged_kv_cache_60_amd import _lib, harness
-    from paged_kv_cache_60_amd import ops as kops
     _lib.load()  # fail loudly if the HIP library is missing
 
     total_steps = args.warmup + args.steps
@@ -188,27 +193,10 @@ def main():
 
     def one_step(s, ev=None):
         half, n_cow, n_upd = eng.host_step()
-        eng.upload(half, n_cow, n_upd)
         k, v, q = inputs[s]
-        if n_cow:
-            kops.paged_block_copy(eng.k_cache, eng.v_cache, eng.cow_dev[:n_cow])
-        kops.paged_kv_write(k, v, eng.k_cache, eng.v_cache, eng.slots_dev, eng.kv_dtype,
-                            eng.k_inv_scale, eng.v_inv_scale)
-        if ev is not None:
-            ev[0].record()
-        eng.attend(q, out, passes=1)
-        if ev is not None:
-            ev[1].record()
-        eng.attend(q, out, passes=2)
+        between = None if ev is None else (lambda i: ev[i].record())
+        eng.device_step(half, n_cow, n_upd, k, v, q, out, between=between)
         return n_cow
-
-    if args.calibrate:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)  # reads 256 MiB, writes 256 MiB
-        torch.cuda.synchronize()
-        del src, dst
 
     log(f"bench: warmup {args.warmup}")
     for s in range(args.warmup):

@@ -77,12 +77,29 @@ int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_
                    float k_inv_scale, float v_inv_scale, void* stream);
 
 /*
+ * paged_kv_write_step -- paged_kv_write and paged_step_metadata in one
+ * launch, for a decode step: writes the new tokens exactly as paged_kv_write
+ * and, in the same kernel, copies ctx_src[n_ctx] -> ctx_dst and writes each
+ * block-table update (row, logical index, block) into
+ * block_tables[row * max_blocks + index] (updates outside [0, num_rows) x
+ * [0, max_blocks) are skipped). slot_mapping, ctx_src and updates may be
+ * pinned host memory read directly by the kernel. Work that reads ctx_dst or
+ * block_tables must be queued after this call.
+ */
+int paged_kv_write_step(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                        int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                        float k_inv_scale, float v_inv_scale, const int32_t* ctx_src,
+                        int32_t* ctx_dst, int n_ctx, const int32_t* updates, int n_updates,
+                        int32_t* block_tables, int num_rows, int max_blocks, void* stream);
+
+/*
  * paged_block_copy -- whole-block copy for copy-on-write.
  * [VLLM] §3.3 (a write into a shared block first copies it to a new block);
  * [OOM] §6.1 (forked beams copy only their last block).
  *
- *   pairs        device, int32 [num_pairs][2] = (src block, dst block);
- *                pairs with an id outside [0, num_blocks) are skipped.
+ *   pairs        int32 [num_pairs][2] = (src block, dst block), device memory
+ *                or pinned host memory; ids outside [0, num_blocks) are skipped.
  *   block_bytes  bytes of one block of one cache
  *                (= num_kv_heads * block_size * head_dim * element size);
  *                must be a multiple of 16. K and V are both copied.

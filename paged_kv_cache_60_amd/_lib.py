@@ -49,6 +49,9 @@ SIGNATURES = {
     "pkv_status_str": (ctypes.c_char_p, [_c_int]),
     "paged_kv_write": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 _c_int, _c_f, _c_f, _vp]),
+    "paged_kv_write_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_f, _c_f, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
+                                     _c_int, _vp]),
     "paged_block_copy": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_sz, _vp]),
     "paged_attn_decode_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,

@@ -59,7 +59,6 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   constexpr int LPR = RB / 16;          // lanes per row in the V load
   constexpr int RPL = 64 / LPR;         // rows per V load
   constexpr int VLD = 32 / RPL;         // V loads per lane per 32-token chunk
-  constexpr int VE = 16 / ELEM;         // V elements per lane per load
   constexpr int VS = D + 16;            // LDS row stride of V, halves (16-byte aligned)
   constexpr int V_LDS = NW * 32 * VS * 2;
   constexpr int M_LDS = NW * G * D * 4 + 2 * NW * 16 * 4;

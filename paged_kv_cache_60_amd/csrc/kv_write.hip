@@ -41,15 +41,38 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
   return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)q - 8u);
 }
 
-template <bool FP8>
+// Step metadata applied by the write kernel of a decode step (see
+// paged_kv_write_step): context lengths and changed block-table entries.
+struct StepMeta {
+  const int32_t* ctx_src;
+  int32_t* ctx_dst;
+  int n_ctx;
+  const int32_t* updates;  // [n_updates][3] = (row, logical index, block)
+  int n_updates;
+  int32_t* tables;
+  int rows;
+  int max_blocks;
+};
+
+template <bool FP8, bool META>
 __global__ void __launch_bounds__(256)
 kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
                 uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                 const int64_t* __restrict__ slots, int64_t total_chunks, int chunks_per_token,
                 int chunks_per_row, int64_t num_slots, int bs, int64_t row_stride_blk,
-                int head_dim, float k_inv, float v_inv) {
+                int head_dim, float k_inv, float v_inv, StepMeta meta) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if constexpr (META) {
+    for (int64_t i = gtid; i < meta.n_ctx; i += stride) meta.ctx_dst[i] = meta.ctx_src[i];
+    for (int64_t k = gtid; k < meta.n_updates; k += stride) {
+      const int row = meta.updates[3 * k];
+      const int idx = meta.updates[3 * k + 1];
+      if (row >= 0 && row < meta.rows && idx >= 0 && idx < meta.max_blocks)
+        meta.tables[(int64_t)row * meta.max_blocks + idx] = meta.updates[3 * k + 2];
+    }
+  }
+  for (int64_t i = gtid; i < total_chunks; i += stride) {
     const int64_t t = i / chunks_per_token;
     const int within = (int)(i - t * chunks_per_token);
     const int h = within / chunks_per_row;
@@ -89,37 +112,69 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
 }  // namespace
 }  // namespace pkv
 
-extern "C" int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                              const int64_t* slot_mapping, int num_tokens, int num_blocks,
-                              int num_kv_heads, int head_dim, int block_size, int kv_dtype,
-                              float k_inv_scale, float v_inv_scale, void* stream) {
+namespace pkv {
+namespace {
+
+int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int64_t* slot_mapping, int num_tokens, int num_blocks, int num_kv_heads,
+                    int head_dim, int block_size, int kv_dtype, float k_inv_scale, float v_inv_scale,
+                    const StepMeta* meta, void* stream) {
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
   if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
   if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
-  if (num_tokens == 0) return PKV_OK;
-  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID;
+  const int64_t meta_work = meta ? (meta->n_ctx > meta->n_updates ? meta->n_ctx : meta->n_updates) : 0;
+  if (num_tokens == 0 && meta_work == 0) return PKV_OK;
+  if (num_tokens > 0 && (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)) return PKV_ERR_INVALID;
   const int chunks_per_row = head_dim / 8;
   const int chunks_per_token = chunks_per_row * num_kv_heads;
   const int64_t total = (int64_t)num_tokens * chunks_per_token;
   const int64_t num_slots = (int64_t)num_blocks * block_size;
   const int64_t row_stride_blk = (int64_t)num_kv_heads * block_size;
   const int threads = 256;
-  int64_t blocks = (total + threads - 1) / threads;
+  const int64_t work = total > meta_work ? total : meta_work;
+  int64_t blocks = (work + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const auto* kn = static_cast<const pkv::u32x4*>(k_new);
-  const auto* vn = static_cast<const pkv::u32x4*>(v_new);
+  const auto* kn = static_cast<const u32x4*>(k_new);
+  const auto* vn = static_cast<const u32x4*>(v_new);
   auto* kc = static_cast<uint8_t*>(k_cache);
   auto* vc = static_cast<uint8_t*>(v_cache);
-  if (kv_dtype == PKV_KV_F16) {
-    hipLaunchKernelGGL(pkv::kv_write_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn,
-                       kc, vc, slot_mapping, total, chunks_per_token, chunks_per_row, num_slots,
-                       block_size, row_stride_blk, head_dim, 1.0f, 1.0f);
-  } else {
-    hipLaunchKernelGGL(pkv::kv_write_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn,
-                       kc, vc, slot_mapping, total, chunks_per_token, chunks_per_row, num_slots,
-                       block_size, row_stride_blk, head_dim, k_inv_scale, v_inv_scale);
-  }
+  const StepMeta m = meta ? *meta : StepMeta{nullptr, nullptr, 0, nullptr, 0, nullptr, 0, 0};
+  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
+  const float ki = fp8 ? k_inv_scale : 1.0f;
+  const float vi = fp8 ? v_inv_scale : 1.0f;
+  auto kern = fp8 ? (meta ? kv_write_kernel<true, true> : kv_write_kernel<true, false>)
+                  : (meta ? kv_write_kernel<false, true> : kv_write_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn, kc, vc, slot_mapping,
+                     total, chunks_per_token, chunks_per_row, num_slots, block_size, row_stride_blk,
+                     head_dim, ki, vi, m);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                              int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                              float k_inv_scale, float v_inv_scale, void* stream) {
+  return pkv::launch_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_blocks,
+                              num_kv_heads, head_dim, block_size, kv_dtype, k_inv_scale, v_inv_scale,
+                              nullptr, stream);
+}
+
+extern "C" int paged_kv_write_step(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                   const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                                   int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                                   float k_inv_scale, float v_inv_scale, const int32_t* ctx_src,
+                                   int32_t* ctx_dst, int n_ctx, const int32_t* updates, int n_updates,
+                                   int32_t* block_tables, int num_rows, int max_blocks, void* stream) {
+  if (n_ctx < 0 || n_updates < 0 || num_rows < 0 || max_blocks < 0) return PKV_ERR_INVALID;
+  if (n_ctx > 0 && (!ctx_src || !ctx_dst)) return PKV_ERR_INVALID;
+  if (n_updates > 0 && (!updates || !block_tables)) return PKV_ERR_INVALID;
+  const pkv::StepMeta m{ctx_src, ctx_dst, n_ctx, updates, n_updates, block_tables, num_rows, max_blocks};
+  return pkv::launch_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_blocks,
+                              num_kv_heads, head_dim, block_size, kv_dtype, k_inv_scale, v_inv_scale,
+                              &m, stream);
 }

@@ -9,16 +9,17 @@ copy-on-write):
      (one C call); new blocks come from the FIFO pool; a write into a shared,
      partially filled last block triggers copy-on-write;
   2. the step's metadata (slot mapping, context lengths, copy pairs and the
-     block-table entries that changed) goes to the device through one small
-     kernel that reads a pinned host buffer; the block tables themselves stay
-     resident on the device;
+     block-table entries that changed) stays in a pinned host buffer that the
+     kernels read directly; the block tables themselves stay resident on the
+     device and only their changed entries are written;
   3. paged_block_copy for the copy-on-write pairs, if any;
-  4. paged_kv_write of the new tokens' K/V;
+  4. paged_kv_write_step: the new tokens' K/V plus the step's context lengths
+     and table entries, in one kernel;
   5. paged_attn_decode (partition pass and reduce pass).
 
 Pinned metadata buffers alternate between two halves so the host can prepare
-step k+1 while step k's metadata kernel may still be queued; an event per half
-keeps the host from overwriting a half before that kernel has read it.
+step k+1 while step k's kernels may still be queued; an event per half keeps
+the host from overwriting a half before the kernels that read it have run.
 """
 from __future__ import annotations
 
@@ -148,22 +149,38 @@ class PagedKVEngine:
         return half, n_cow, n_upd
 
     def upload(self, half, n_cow, n_upd):
-        """Step part 2: one small kernel reads the pinned half and updates the
-        device slot mapping, context lengths, copy pairs and table entries."""
+        """Step part 2 on its own: one small kernel reads the pinned half and
+        updates the device slot mapping, context lengths, copy pairs and table
+        entries (paged_step_metadata). device_step() does this inside the write
+        kernel instead; this form serves callers that write tokens separately."""
         slots, ctx, cow, upd = self._views[half]
         ops.paged_step_metadata(slots, self.slots_dev, ctx, self.ctx_dev, len(self.batch), cow,
                                 self.cow_dev, n_cow, upd, n_upd, self.tables_dev)
+        self._mark_read(half)
+
+    def _mark_read(self, half):
         ev = torch.cuda.Event()
         ev.record()
         self._events[half] = ev
 
-    def device_step(self, n_cow, k_new, v_new, q, out, passes=3):
-        """Step parts 3-5 on the current stream."""
+    def device_step(self, half, n_cow, n_upd, k_new, v_new, q, out, passes=3, between=None):
+        """Step parts 2-5 on the current stream: copy-on-write copies (pairs read
+        from the pinned half), then one kernel that writes the new tokens and
+        applies the step's metadata, then attention. `between` (optional) is
+        called after the write, before attention, and again between the passes."""
+        slots, ctx, cow, upd = self._views[half]
         if n_cow:
-            ops.paged_block_copy(self.k_cache, self.v_cache, self.cow_dev[:n_cow])
-        ops.paged_kv_write(k_new, v_new, self.k_cache, self.v_cache, self.slots_dev, self.kv_dtype,
-                           self.k_inv_scale, self.v_inv_scale)
-        self.attend(q, out, passes)
+            ops.paged_block_copy(self.k_cache, self.v_cache, cow[:2 * n_cow].view(n_cow, 2))
+        ops.paged_kv_write_step(k_new, v_new, self.k_cache, self.v_cache, slots, ctx, self.ctx_dev, upd,
+                                n_upd, self.tables_dev, self.kv_dtype, self.k_inv_scale, self.v_inv_scale)
+        self._mark_read(half)
+        if between is None:
+            self.attend(q, out, passes)
+        else:
+            between(0)
+            self.attend(q, out, 1)
+            between(1)
+            self.attend(q, out, 2)
 
     def attend(self, q, out, passes=3):
         ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
@@ -173,8 +190,7 @@ class PagedKVEngine:
     def decode_step(self, k_new, v_new, q, out):
         """Full decode step: append one token per batch sequence, write it, attend."""
         half, n_cow, n_upd = self.host_step()
-        self.upload(half, n_cow, n_upd)
-        self.device_step(n_cow, k_new, v_new, q, out)
+        self.device_step(half, n_cow, n_upd, k_new, v_new, q, out)
         return n_cow
 
     def host_tables(self):

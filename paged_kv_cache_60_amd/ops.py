@@ -68,18 +68,53 @@ def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, kv_dtype=F16,
                              _stream_ptr(stream)), w)
 
 
+def _device_readable(t) -> bool:
+    """On the GPU, or pinned host memory the kernels can read directly."""
+    return t.is_cuda or t.is_pinned()
+
+
 def paged_block_copy(k_cache, v_cache, pairs, stream=None):
-    """Copy whole blocks pairs[i] = (src, dst) (int32 [n, 2] on device) in both caches."""
+    """Copy whole blocks pairs[i] = (src, dst) (int32 [n, 2], device or pinned) in both caches."""
     w = "paged_block_copy"
     _require(k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
              and k_cache.shape == v_cache.shape and k_cache.dim() == 4, w, "caches")
-    _require(pairs.is_cuda and pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
-             and pairs.is_contiguous(), w, "pairs")
+    _require(_device_readable(pairs) and pairs.dtype == torch.int32 and pairs.dim() == 2
+             and pairs.shape[1] == 2 and pairs.is_contiguous(), w, "pairs")
     nb = k_cache.shape[0]
     block_bytes = k_cache[0].numel() * k_cache.element_size()
     lib = _lib.load()
     check(lib.paged_block_copy(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], nb, block_bytes,
                                _stream_ptr(stream)), w)
+
+
+def paged_kv_write_step(k_new, v_new, k_cache, v_cache, slot_mapping, ctx_src, ctx_dst, updates,
+                        n_updates, block_tables, kv_dtype=F16, k_inv_scale=1.0, v_inv_scale=1.0,
+                        stream=None):
+    """paged_kv_write plus the step metadata (context lengths, table updates) in one launch.
+
+    slot_mapping / ctx_src / updates may be pinned host tensors (read directly by the kernel).
+    """
+    w = "paged_kv_write_step"
+    _require(k_new.is_cuda and k_new.dtype == torch.float16 and k_new.is_contiguous(), w, "k_new")
+    _require(v_new.shape == k_new.shape and v_new.dtype == torch.float16 and v_new.is_contiguous(), w, "v_new")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype) and k_cache.shape == v_cache.shape,
+             w, "caches")
+    nb, hkv, bs, d = k_cache.shape
+    T = k_new.shape[0]
+    _require(k_new.dim() == 3 and k_new.shape[1] == hkv and k_new.shape[2] == d, w, "k_new shape")
+    _require(_device_readable(slot_mapping) and slot_mapping.dtype == torch.int64 and slot_mapping.numel() >= T,
+             w, "slot_mapping")
+    _require(_device_readable(ctx_src) and ctx_src.dtype == torch.int32 and ctx_dst.is_cuda
+             and ctx_dst.dtype == torch.int32 and ctx_src.numel() >= ctx_dst.numel(), w, "ctx")
+    _require(_device_readable(updates) and updates.dtype == torch.int32 and updates.numel() >= 3 * n_updates,
+             w, "updates")
+    _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2, w, "tables")
+    rows, maxb = block_tables.shape
+    lib = _lib.load()
+    check(lib.paged_kv_write_step(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T, nb,
+                                  hkv, d, bs, kv_dtype_code(kv_dtype), float(k_inv_scale), float(v_inv_scale),
+                                  _p(ctx_src), _p(ctx_dst), ctx_dst.numel(), _p(updates), int(n_updates),
+                                  _p(block_tables), rows, maxb, _stream_ptr(stream)), w)
 
 
 def workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens=0) -> int:

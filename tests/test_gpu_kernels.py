@@ -111,3 +111,68 @@ def test_block_copy_config5_scale():
     o = runner.run(wl, steps=0)
     assert np.array_equal(cache_bits(eng.k_cache), oracle_bits(o.k_cache))
     assert np.array_equal(cache_bits(eng.v_cache), oracle_bits(o.v_cache))
+
+
+def _meta_case(seed, B=37, maxb=11, n_upd=20):
+    g = np.random.default_rng(seed)
+    tables = g.integers(-1, 500, size=(B, maxb), dtype=np.int32)
+    upd = np.stack([g.integers(0, B, n_upd), g.integers(0, maxb, n_upd), g.integers(0, 500, n_upd)], 1)
+    upd = upd.astype(np.int32)
+    upd[3] = (B, 0, 7)          # row out of range: skipped
+    upd[4] = (0, maxb, 7)       # index out of range: skipped
+    upd[5] = (-1, 2, 7)
+    # later updates win when two address the same entry; keep entries distinct here
+    _, first = np.unique(upd[:, 0] * 1000 + upd[:, 1], return_index=True)
+    upd = upd[np.sort(first)]
+    expect = tables.copy()
+    for r, i, b in upd.tolist():
+        if 0 <= r < B and 0 <= i < maxb:
+            expect[r, i] = b
+    ctx = g.integers(0, 4000, size=B, dtype=np.int32)
+    return tables, upd, ctx, expect
+
+
+def _pinned(a):
+    t = torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+    return t
+
+
+def test_step_metadata_bit_exact():
+    tables, upd, ctx, expect = _meta_case(1)
+    B = len(ctx)
+    slots = np.random.default_rng(2).integers(-1, 10 ** 6, size=B).astype(np.int64)
+    cow = np.random.default_rng(3).integers(0, 100, size=(5, 2)).astype(np.int32)
+    t_dev = torch.from_numpy(tables).to(DEV)
+    s_dev = torch.empty(B, dtype=torch.int64, device=DEV)
+    c_dev = torch.empty(B, dtype=torch.int32, device=DEV)
+    cw_dev = torch.empty((5, 2), dtype=torch.int32, device=DEV)
+    ops.paged_step_metadata(_pinned(slots), s_dev, _pinned(ctx), c_dev, B, _pinned(cow), cw_dev, 5,
+                            _pinned(upd.reshape(-1)), len(upd), t_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(t_dev.cpu().numpy(), expect)
+    assert np.array_equal(s_dev.cpu().numpy(), slots)
+    assert np.array_equal(c_dev.cpu().numpy(), ctx)
+    assert np.array_equal(cw_dev.cpu().numpy(), cow)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8"])
+def test_kv_write_step_bit_exact(kv_dtype):
+    tables, upd, ctx, expect = _meta_case(4)
+    B = len(ctx)
+    g = np.random.default_rng(5)
+    nb, hkv, bs, d = 40, 8, 16, 128
+    slots = g.permutation(nb * bs)[:B].astype(np.int64)
+    slots[::7] = -1
+    K = g.standard_normal((B, hkv, d), dtype=np.float32).astype(np.float16)
+    V = g.standard_normal((B, hkv, d), dtype=np.float32).astype(np.float16)
+    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, kv_dtype)
+    cache_ops.scatter(o_k, o_v, K, V, slots, bs, kv_dtype, 61.0, 61.0)
+    t_dev = torch.from_numpy(tables).to(DEV)
+    c_dev = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+    ops.paged_kv_write_step(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v, _pinned(slots),
+                            _pinned(ctx), c_dev, _pinned(upd.reshape(-1)), len(upd), t_dev, kv_dtype, 61.0, 61.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
+    assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
+    assert np.array_equal(t_dev.cpu().numpy(), expect)
+    assert np.array_equal(c_dev.cpu().numpy(), ctx)
