@@ -20,7 +20,8 @@
 //     wave load covers 64 x 16 B = 1 KiB of contiguous K (or V) rows of one
 //     block: LPR = row bytes / 16 lanes per token, 64 / LPR tokens per load.
 //   - q.k: per-lane fp16 dot products (fp8 rows are first widened to fp16
-//     exactly) and a DPP butterfly over the LPR lanes of the row.
+//     exactly by the hardware conversion) and a DPP butterfly over the LPR
+//     lanes of the row.
 //   - Each group of LPR lanes keeps its own online softmax state (running
 //     max m, sum l, unnormalised output slice) over the tokens it sees, so the
 //     hot loop has no cross-row traffic; rows, then waves (through LDS), are
@@ -64,8 +65,8 @@ struct AttnArgs {
   int num_blocks;
   int part_tokens;
   int max_parts;
-  float qk_scale;     // sm_scale * k_scale * log2(e), times 256 for fp8
-  float v_out_scale;  // v_scale, times 256 for fp8
+  float qk_scale;     // sm_scale * log2(e), times k_scale for fp8
+  float v_out_scale;  // v_scale for fp8, else 1
 };
 
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
@@ -186,7 +187,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 #pragma unroll
         for (int w = 0; w < W; ++w) {
           if constexpr (FP8)
-            kw[w] = fp8x2_to_f16x2_scaled(kr[i][w / 2] >> (16 * (w & 1)));
+            kw[w] = (w & 1) ? fp8x2_hi_to_f16x2(kr[i][w / 2]) : fp8x2_lo_to_f16x2(kr[i][w / 2]);
           else
             kw[w] = kr[i][w];
         }
@@ -228,7 +229,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
         for (int w = 0; w < W; ++w) {
           uint32_t pw;
           if constexpr (FP8)
-            pw = fp8x2_to_f16x2_scaled(vr[i][w / 2] >> (16 * (w & 1)));
+            pw = (w & 1) ? fp8x2_hi_to_f16x2(vr[i][w / 2]) : fp8x2_lo_to_f16x2(vr[i][w / 2]);
           else
             pw = vr[i][w];
           vf[2 * w] = h_lo(pw);
@@ -499,8 +500,8 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
   a.part_tokens = part;
   a.max_parts = mp;
   const float kLog2e = 1.4426950408889634f;
-  a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale * 256.0f : 1.0f);
-  a.v_out_scale = fp8 ? v_scale * 256.0f : 1.0f;
+  a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
+  a.v_out_scale = fp8 ? v_scale : 1.0f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (passes & 1) {

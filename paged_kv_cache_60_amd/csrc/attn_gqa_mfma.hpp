@@ -36,13 +36,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f16x8 f16x8_from_u32x4(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// 8 fp8 bytes (two dwords) -> 8 fp16 values scaled by 2^-8, exactly
+// 8 fp8 bytes (two dwords) -> 8 fp16 values, exactly
 __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = fp8x2_to_f16x2_scaled(w0);
-  r[1] = fp8x2_to_f16x2_scaled(w0 >> 16);
-  r[2] = fp8x2_to_f16x2_scaled(w1);
-  r[3] = fp8x2_to_f16x2_scaled(w1 >> 16);
+  r[0] = fp8x2_lo_to_f16x2(w0);
+  r[1] = fp8x2_hi_to_f16x2(w0);
+  r[2] = fp8x2_lo_to_f16x2(w1);
+  r[3] = fp8x2_hi_to_f16x2(w1);
   return __builtin_bit_cast(f16x8, r);
 }
 
