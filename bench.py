@@ -181,7 +181,8 @@ def main():
     harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
     eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, args.partition)
     part = args.partition or int(_lib.load().paged_attn_default_partition(
-        wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, 1 if wl.kv_dtype == "fp8" else 0))
+        wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.max_blocks_per_seq,
+        1 if wl.kv_dtype == "fp8" else 0))
 
     # stage every step's inputs in HBM before timing
     B = len(wl.batch)

@@ -132,8 +132,8 @@ int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int num
  *                  (fp32 partials; contents on entry are ignored).
  * Results are deterministic: they do not depend on block placement.
  */
-size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
-                                         int max_blocks_per_seq, int block_size,
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int max_blocks_per_seq, int block_size,
                                          int partition_tokens);
 
 int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -156,9 +156,11 @@ int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, cons
                              int partition_tokens, void* workspace, size_t workspace_bytes,
                              int passes, void* stream);
 
-/* The partition size the library uses when partition_tokens is 0. */
+/* The partition size the library uses when partition_tokens is 0: the largest
+ * power of two in [256, 2048] that is at most max_blocks_per_seq * block_size
+ * divided by 4 (one query head per KV head) or by 2 (grouped heads). */
 int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
-                                 int block_size, int kv_dtype);
+                                 int block_size, int max_blocks_per_seq, int kv_dtype);
 
 /*
  * paged_step_metadata -- bring a decode step's metadata to the device.

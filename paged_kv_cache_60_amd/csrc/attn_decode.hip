@@ -46,7 +46,6 @@ namespace {
 
 constexpr int kTile = 16;
 constexpr int kWaves = 4;
-constexpr int kDefaultPartition = 512;
 
 struct AttnArgs {
   const f16* q;
@@ -412,8 +411,20 @@ int log2_exact(int v) {
   return (1 << k) == v ? k : -1;
 }
 
-int resolve_partition(int partition_tokens) {
-  if (partition_tokens == 0) return kDefaultPartition;
+// Default partition: the largest power of two in [256, 2048] that is at most
+// a quarter (one query head per KV head) or half (grouped heads) of the
+// largest context the block table can hold. Measured on MI355X: 512 for the
+// Llama-2-7B batch-64 workload, 1024-2048 for 4k contexts and for grouped heads.
+int default_partition(int group, int max_blocks, int block_size) {
+  const int64_t max_ctx = (int64_t)max_blocks * block_size;
+  const int64_t target = max_ctx / (group >= 2 ? 2 : 4);
+  int p = 256;
+  while (p < 2048 && 2 * (int64_t)p <= target) p *= 2;
+  return p;
+}
+
+int resolve_partition(int partition_tokens, int group, int max_blocks, int block_size) {
+  if (partition_tokens == 0) return default_partition(group, max_blocks, block_size);
   if (partition_tokens < 64 || partition_tokens % 64 != 0) return -1;
   return partition_tokens;
 }
@@ -427,22 +438,22 @@ int max_partitions(int max_blocks, int block_size, int part) {
 }  // namespace pkv
 
 extern "C" int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
-                                            int block_size, int kv_dtype) {
-  (void)num_q_heads;
-  (void)num_kv_heads;
+                                            int block_size, int max_blocks_per_seq, int kv_dtype) {
   (void)head_dim;
-  (void)block_size;
   (void)kv_dtype;
-  return pkv::kDefaultPartition;
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return -1;
+  return pkv::default_partition(num_q_heads / num_kv_heads, max_blocks_per_seq, block_size);
 }
 
-extern "C" size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
-                                                    int max_blocks_per_seq, int block_size,
-                                                    int partition_tokens) {
-  const int part = pkv::resolve_partition(partition_tokens);
-  if (part < 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0)
+extern "C" size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                                    int head_dim, int max_blocks_per_seq,
+                                                    int block_size, int partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || block_size <= 0)
     return 0;
+  const int part = pkv::resolve_partition(partition_tokens, num_q_heads / num_kv_heads,
+                                          max_blocks_per_seq, block_size);
+  if (part < 0) return 0;
   const int mp = pkv::max_partitions(max_blocks_per_seq, block_size, part);
   if (mp <= 1) return 0;
   return (size_t)num_seqs * num_q_heads * mp * (size_t)(head_dim + 2) * sizeof(float);
@@ -465,16 +476,16 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
   if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
   if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
-  const int part = resolve_partition(partition_tokens);
-  if (part < 0) return PKV_ERR_INVALID;
   const int G = num_q_heads / num_kv_heads;
+  const int part = resolve_partition(partition_tokens, G, max_blocks_per_seq, block_size);
+  if (part < 0) return PKV_ERR_INVALID;
   const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
   PartFn fn = pick(head_dim, G, fp8);
   if (!fn) return PKV_ERR_INVALID;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
   const int mp = max_partitions(max_blocks_per_seq, block_size, part);
-  const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+  const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                         max_blocks_per_seq, block_size, part);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;
   const int64_t grid1 = (int64_t)num_kv_heads * num_seqs * mp;

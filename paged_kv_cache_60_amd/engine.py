@@ -131,7 +131,7 @@ class PagedKVEngine:
         tab, ctx = self.host_tables()
         self.tables_dev = torch.from_numpy(tab).to(self.device)
         self.ctx_dev.copy_(torch.from_numpy(ctx))
-        wsb = ops.workspace_bytes(B, self.hq, self.d, self.max_blocks, self.bs, self.partition_tokens)
+        wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
         self._parity = 0
         torch.cuda.synchronize(self.device)

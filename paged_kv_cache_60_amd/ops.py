@@ -117,15 +117,17 @@ def paged_kv_write_step(k_new, v_new, k_cache, v_cache, slot_mapping, ctx_src, c
                                   _p(block_tables), rows, maxb, _stream_ptr(stream)), w)
 
 
-def workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_tokens=0) -> int:
-    return int(_lib.load().paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                    partition_tokens=0) -> int:
+    return int(_lib.load().paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                              max_blocks_per_seq, block_size,
                                                              partition_tokens))
 
 
-def default_partition(num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype=F16) -> int:
+def default_partition(num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      kv_dtype=F16) -> int:
     return int(_lib.load().paged_attn_default_partition(num_q_heads, num_kv_heads, head_dim, block_size,
-                                                        kv_dtype_code(kv_dtype)))
+                                                        max_blocks_per_seq, kv_dtype_code(kv_dtype)))
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale, kv_dtype=F16,
@@ -145,7 +147,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
     _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
              and ctx_lens.is_contiguous(), w, "ctx_lens")
     maxb = block_tables.shape[1]
-    need = workspace_bytes(B, hq, d, maxb, bs, partition_tokens) if B > 0 and maxb > 0 else 0
+    need = workspace_bytes(B, hq, hkv, d, maxb, bs, partition_tokens) if B > 0 and maxb > 0 else 0
     ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
     if need:
         _require(workspace is not None and workspace.is_cuda

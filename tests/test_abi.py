@@ -70,10 +70,16 @@ def test_attention_empty_batch_is_ok():
 def test_workspace_bytes():
     lib = _lib.load()
     # 128 blocks of 16 = 2048 tokens, 512-token partitions -> 4 partials of (D + 2) floats
-    assert lib.paged_attn_decode_workspace_bytes(64, 32, 128, 128, 16, 512) == 64 * 32 * 4 * 130 * 4
-    assert lib.paged_attn_decode_workspace_bytes(4, 8, 64, 2, 16, 512) == 0  # one partition: no partials
-    assert lib.paged_attn_decode_workspace_bytes(4, 8, 64, 2, 16, 100) == 0  # invalid partition size
-    assert lib.paged_attn_default_partition(32, 32, 128, 16, 0) % 64 == 0
+    assert lib.paged_attn_decode_workspace_bytes(64, 32, 32, 128, 128, 16, 512) == 64 * 32 * 4 * 130 * 4
+    assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 2, 16, 512) == 0  # one partition: no partials
+    assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 2, 16, 100) == 0  # invalid partition size
+    # default partition: largest power of two in [256, 2048] <= max_ctx/4 (MHA) or max_ctx/2 (GQA)
+    assert lib.paged_attn_default_partition(32, 32, 128, 16, 131, 0) == 512     # 2096 tokens
+    assert lib.paged_attn_default_partition(40, 40, 128, 32, 129, 0) == 1024    # 4128 tokens
+    assert lib.paged_attn_default_partition(16, 8, 128, 16, 256, 0) == 2048     # 4096 tokens, GQA
+    assert lib.paged_attn_default_partition(64, 8, 128, 64, 35, 1) == 1024      # 2240 tokens, GQA
+    assert lib.paged_attn_default_partition(8, 8, 64, 16, 16, 0) == 256         # small: clamped
+    assert lib.paged_attn_default_partition(8, 0, 64, 16, 16, 0) == -1
 
 
 def test_write_and_copy_validation():

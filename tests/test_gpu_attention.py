@@ -133,7 +133,7 @@ def test_zero_length_and_single_token():
     tables = torch.tensor([[3, -1], [5, -1], [0, 1]], dtype=torch.int32, device=DEV)
     ctx = torch.tensor([0, 1, 20], dtype=torch.int32, device=DEV)
     out = torch.full((B, hq, d), 7.0, dtype=torch.float16, device=DEV)
-    ws = torch.empty(max(ops.workspace_bytes(B, hq, d, 2, bs, 64), 4), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(ops.workspace_bytes(B, hq, hkv, d, 2, bs, 64), 4), dtype=torch.uint8, device=DEV)
     ops.paged_attn_decode(out, q, kc, vc, tables, ctx, 0.125, partition_tokens=64, workspace=ws)
     torch.cuda.synchronize()
     assert (out[0] == 0).all()
