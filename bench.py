@@ -5,7 +5,8 @@
 One step = the whole hot path for one batch: host block-manager bookkeeping
 (append one token per sequence), one host-to-device copy of the step's
 metadata, copy-on-write block copies (if any), paged_kv_write of the new
-tokens, paged_attn_decode (partition pass + reduce pass). Inputs are resident
+tokens, paged_attn_decode (pass 1 over equal shares of the KV, pass 2 combining
+split segments). Inputs are resident
 in HBM before the timed region; the setup (prompt writes) is untimed.
 
 Default workload: Llama-2-7B-shaped single layer, batch 64, 32/32 heads,
@@ -14,9 +15,9 @@ head_dim 128, block size 16, fp16 KV, context lengths uniform in [128, 2048].
 Printed: one JSON line. `value` is the whole-step throughput in GB/s of
 algorithmic bytes (K/V read by attention, queries, block tables, context
 lengths, output, plus the bytes paged_kv_write and paged_block_copy move) over
-the wall time of the timed steps. `roofline` is for the dominant kernel, the
-attention partition pass: its algorithmic bytes per launch over its average
-launch duration measured with HIP events on the stream it runs on.
+the wall time of the timed steps. `roofline` is for the dominant kernel,
+attention pass 1: its algorithmic bytes per launch over its average launch
+duration measured with HIP events on the stream it runs on.
 `cpu_baseline` is the CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
@@ -154,7 +155,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1-5 (2 = Llama-2-7B batch 64)")
-    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="tokens per attention worker (0 = one worker per resident wave, the default)")
     ap.add_argument("--flush", action="store_true", help="evict L2/MALL between steps (time by events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -163,15 +165,27 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path does not "
-              f"shard across GPUs in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              f"runs on a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     import workloads
     from paged_kv_cache_60_amd import _lib, harness
+    from paged_kv_cache_60_amd import ops
     _lib.load()  # fail loudly if the HIP library is missing
+
+    if args.calibrate:
+        # a plain copy of known size: the counter runs scale FETCH_SIZE / WRITE_SIZE by what
+        # they read for this dispatch
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     total_steps = args.warmup + args.steps
     wl = workloads.make(args.config, max_steps=total_steps + 1)
@@ -180,9 +194,10 @@ def main():
     eng = harness.make_engine(wl, poison=False)
     harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
     eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, args.partition)
-    part = args.partition or int(_lib.load().paged_attn_default_partition(
-        wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.max_blocks_per_seq,
-        1 if wl.kv_dtype == "fp8" else 0))
+    workers = ops.decode_workers(len(wl.batch), wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                                 wl.max_blocks_per_seq, wl.kv_dtype, args.partition)
+    group = wl.num_q_heads // wl.num_kv_heads
+    kernel = "attn_partition_mfma_kernel" if group >= 4 else "attn_partition_kernel"
 
     # stage every step's inputs in HBM before timing
     B = len(wl.batch)
@@ -263,7 +278,8 @@ def main():
         "config": {
             **wl.summary(),
             "mean_ctx_len": round(float(np.mean([c.mean() for c in ctx_steps])), 1),
-            "partition_tokens": part,
+            "partition_tokens": args.partition,
+            "attention_workers": workers,
             "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
         },
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
@@ -277,7 +293,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attn_partition_kernel",
+            "kernel": kernel,
         },
     }
     if not args.no_cpu_baseline:

@@ -113,24 +113,39 @@ int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int num
  * paged_attn_decode -- one query token per sequence attends over its paged
  * K/V: out[s][h] = sum_t softmax_t(sm_scale * q[s][h].K_t) V_t over the
  * ctx_lens[s] tokens reached through block_tables[s] ([OOM] §2.1-2.3,
- * [ENGINE] §2.2). Split-sequence: pass 1 handles partitions of
- * `partition_tokens` tokens per (sequence, KV head) with an online softmax and
- * writes (max, sum, unnormalised output) partials; pass 2 combines them.
- * A sequence that fits in one partition is finished by pass 1.
+ * [ENGINE] §2.2).
+ * Split-sequence, stream-K style: the (sequence, KV head) segments are laid
+ * end to end in units of 16 tokens (32 for 4 or 8 query heads per KV head)
+ * and cut into equal contiguous shares, one per worker (a wave). Pass 1: each
+ * worker runs an online softmax over its share; a segment it holds whole is
+ * written to `out`, a segment split between workers leaves (max, sum,
+ * unnormalised output) partials. Pass 2 combines the partials of split
+ * segments and writes zeros for sequences with ctx_len 0.
  *
  *   out            device, fp16 [num_seqs][num_q_heads][head_dim]
  *   q              device, fp16 [num_seqs][num_q_heads][head_dim]
  *   block_tables   device, int32 [num_seqs][max_blocks_per_seq]; entries past
- *                  ceil(ctx_len/block_size) are never read.
+ *                  ceil(ctx_len/block_size) are never read; entries outside
+ *                  [0, num_blocks) are never followed (their tokens are skipped).
  *   ctx_lens       device, int32 [num_seqs], tokens to attend (includes the
  *                  token written this step). Clamped to
- *                  max_blocks_per_seq*block_size; 0 gives a zero output.
+ *                  [0, max_blocks_per_seq*block_size]; 0 gives a zero output.
  *   sm_scale       softmax scale (1/sqrt(head_dim) usually).
  *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale).
- *   partition_tokens 0 = library default; else a multiple of 64, >= 64.
+ *   partition_tokens 0 = as many workers as are resident on the device at
+ *                  once; else a multiple of 16: each worker takes about this
+ *                  many tokens of the longest possible batch (at most 8192
+ *                  workers either way).
  *   workspace      device, >= paged_attn_decode_workspace_bytes(...) bytes
- *                  (fp32 partials; contents on entry are ignored).
- * Results are deterministic: they do not depend on block placement.
+ *                  (fp32 partials and the unit prefix; contents on entry are
+ *                  ignored). Calls that share a workspace must not overlap.
+ * Shapes: head_dim 64 or 128; block_size 16, 32 or 64; num_q_heads a multiple
+ * of num_kv_heads with 1, 2, 4 or 8 query heads per KV head. Batches of more
+ * than 4096 sequences run as consecutive launches.
+ * Results are deterministic: they depend only on the inputs, the shape and the
+ * worker count, not on block placement.
+ * Returns PKV_ERR_INVALID for a bad shape, null pointer or short workspace
+ * (nothing is queued), PKV_ERR_HIP if a launch fails.
  */
 size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                          int head_dim, int max_blocks_per_seq, int block_size,
@@ -146,8 +161,8 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
 
 /* Same as paged_attn_decode, restricted to pass 1 (passes = 1), pass 2
  * (passes = 2) or both (passes = 3). Queuing pass 1 then pass 2 with the
- * same arguments is identical to paged_attn_decode; it exists so that each
- * pass can be timed on its own. */
+ * same arguments is identical to paged_attn_decode for batches of up to 4096
+ * sequences; it exists so that each pass can be timed on its own. */
 int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int max_blocks_per_seq,
                              const int32_t* ctx_lens, int num_seqs, int num_q_heads,
@@ -156,11 +171,12 @@ int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, cons
                              int partition_tokens, void* workspace, size_t workspace_bytes,
                              int passes, void* stream);
 
-/* The partition size the library uses when partition_tokens is 0: the largest
- * power of two in [256, 2048] that is at most max_blocks_per_seq * block_size
- * divided by 4 (one query head per KV head) or by 2 (grouped heads). */
-int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
-                                 int block_size, int max_blocks_per_seq, int kv_dtype);
+/* The number of workers (waves) pass 1 uses for this shape on the current
+ * device (for one launch of up to 4096 sequences), or a negative status for an
+ * invalid shape or a failed device query. */
+int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int max_blocks_per_seq, int kv_dtype,
+                              int partition_tokens);
 
 /*
  * paged_step_metadata -- bring a decode step's metadata to the device.

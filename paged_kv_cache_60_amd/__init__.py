@@ -8,8 +8,8 @@ marshalling of torch tensors and a small engine that drives one decode step.
 """
 from ._lib import PkvError, load  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
-from .ops import (default_partition, paged_attn_decode, paged_block_copy,  # noqa: F401
+from .ops import (decode_workers, paged_attn_decode, paged_block_copy,  # noqa: F401
                   paged_kv_write, workspace_bytes)
 
 __all__ = ["BlockManager", "PkvError", "load", "paged_attn_decode", "paged_block_copy",
-           "paged_kv_write", "workspace_bytes", "default_partition"]
+           "paged_kv_write", "workspace_bytes", "decode_workers"]

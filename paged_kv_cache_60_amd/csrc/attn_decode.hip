@@ -7,36 +7,45 @@
 // With an fp8 e4m3 cache K and V are dequantised with one scale per tensor
 // ("Where Did the VRAM Go (KV cache tutorial)", §6.1-6.3).
 //
-// Pass 1 (partition kernel). One workgroup per (partition, sequence, KV
-// head); the KV head index varies fastest across workgroup ids, so that the
-// round-robin dispatch of workgroups over the eight XCDs spreads heads (and
-// not partitions) over XCDs: every XCD gets an equal share of long and short
-// partitions, and the workgroups that read one KV head of a shared prefix
-// land on the same XCD and share its L2.
-//   - A partition is `part_tokens` consecutive tokens, cut into 16-token
-//     tiles; a tile never straddles two blocks (block sizes are multiples of
-//     16), so each tile needs one block-table entry (wave-uniform).
-//   - Lane mapping: each lane loads 16 contiguous bytes of a token row, so one
-//     wave load covers 64 x 16 B = 1 KiB of contiguous K (or V) rows of one
-//     block: LPR = row bytes / 16 lanes per token, 64 / LPR tokens per load.
-//   - q.k: per-lane fp16 dot products (fp8 rows are first widened to fp16
-//     exactly by the hardware conversion) and a DPP butterfly over the LPR
-//     lanes of the row.
-//   - Each group of LPR lanes keeps its own online softmax state (running
-//     max m, sum l, unnormalised output slice) over the tokens it sees, so the
-//     hot loop has no cross-row traffic; rows, then waves (through LDS), are
-//     merged once at the end of the partition.
-//   - All query heads of a GQA group are handled by the workgroup that loads
-//     their KV head, so K/V are read once per group. Groups of 4 or 8 heads
-//     run on the matrix cores instead (attn_gqa_mfma.hpp).
-//   - A sequence that fits in one partition is normalised and written here.
-// Pass 2 (reduce kernel). One wave per (sequence, query head): combines the
-// partitions' (m, l, o) with weights exp(m_p - max m) and writes fp16.
+// Work decomposition (split-sequence, stream-K style). A segment is one
+// (sequence, KV head); its tokens are cut into units of 16 tokens (32 on the
+// matrix-core path). The segments are laid end to end, sequence-major, and the
+// unit range is divided into equal contiguous shares, one per worker. A worker
+// is one wave; by default there are as many workers as fit on the chip at
+// once. A worker walks its share piece by piece (a piece = the part of one
+// segment inside the share):
+//   - a piece that is its whole segment is normalised and written to the
+//     output directly;
+//   - otherwise the piece's online-softmax state (max m, sum l, unnormalised
+//     output o) goes to one of the worker's two partial slots: slot 0 for the
+//     first piece of the share, slot 1 for the last (any piece between them
+//     is a whole segment).
+// Pass 2 combines, for every (sequence, query head) whose segment was split,
+// the pieces of the consecutive workers that hold it, with weights
+// exp(m_p - max m), and writes zeros for empty sequences. The split depends
+// only on the context lengths and the worker count, so results are
+// deterministic and independent of block placement. Every worker streams the
+// same number of tokens, no workgroup is idle and none waits on another.
+//
+// Pass 1, vector path (1 or 2 query heads per KV head):
+//   - a 16-token tile never straddles two blocks (block sizes are multiples
+//     of 16), so one table entry serves a tile; the block ids of up to 64
+//     tiles are fetched together (one lane each) and broadcast with readlane;
+//   - lane mapping: each lane loads 16 contiguous bytes of a token row, LPR =
+//     row bytes / 16 lanes per row, 64 / LPR rows per wave load (1 KiB);
+//   - q.k: per-lane fp16 dot products (fp8 rows widened to fp16 exactly by
+//     the hardware conversion) and a DPP butterfly over the row's LPR lanes;
+//   - each group of LPR lanes keeps its own online softmax over the rows it
+//     sees; the groups are merged once per piece;
+//   - K/V loads are non-temporal: streamed once, not kept in the caches.
+// Groups of 4 or 8 query heads run on the matrix cores (attn_gqa_mfma.hpp).
 //
 // Exponentials are taken base 2 with log2(e) folded into the logit scale.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/pagedkv.h"
 #include "device_common.hpp"
@@ -45,7 +54,9 @@ namespace pkv {
 namespace {
 
 constexpr int kTile = 16;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;          // waves (workers) per workgroup
+constexpr int kMaxWorkers = 8192;  // the workspace holds partials for this many workers
+constexpr int kMaxSeqs = 4096;     // sequences per launch (their unit prefix lives in LDS)
 
 struct AttnArgs {
   const f16* q;
@@ -53,8 +64,9 @@ struct AttnArgs {
   const uint8_t* vc;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* ws_o;   // [B][Hq][max_parts][D]
-  float* ws_ml;  // [B][Hq][max_parts][2] = (max, sum)
+  float* ws_o;     // [kMaxWorkers][2][G][D]  unnormalised outputs of partial pieces
+  float* ws_ml;    // [kMaxWorkers][2][G][2]  (max, sum) of partial pieces
+  int32_t* ws_pt;  // [B + 1]                 unit prefix over sequences (pass 1 -> pass 2)
   f16* out;
   int max_blocks;
   int B;
@@ -62,8 +74,8 @@ struct AttnArgs {
   int Hq;
   int bs_log2;
   int num_blocks;
-  int part_tokens;
-  int max_parts;
+  int unit_tokens;    // 16 (vector path) or 32 (matrix cores)
+  int workers;        // W, a multiple of kWaves
   float qk_scale;     // sm_scale * log2(e), times k_scale for fp8
   float v_out_scale;  // v_scale for fp8, else 1
 };
@@ -71,6 +83,100 @@ struct AttnArgs {
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
 
 __device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
+
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t W) { return w * total / W; }
+
+// A value the caller knows is equal on all lanes of the wave, moved to a scalar
+// register so that the arithmetic that depends on it stays scalar.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Dynamic LDS of a pass-1 workgroup: pt[B + 1] then scan[blockDim]. pt[0] = 0
+// and pt[s + 1] = pt[s] + ceil(len(s) / unit), len(s) = the clamped context
+// length of sequence s. Ends with a barrier.
+__device__ __forceinline__ int seq_len(const AttnArgs& a, int s) {
+  return clamp_len(a.ctx_lens[s], a.max_blocks << a.bs_log2);
+}
+
+__device__ void build_prefix(const AttnArgs& a, int* pt, int* scan) {
+  const int n = a.B;
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n; i += T) pt[i + 1] = (seq_len(a, i) + a.unit_tokens - 1) / a.unit_tokens;
+  __syncthreads();
+  // each thread sums a run of consecutive sequences; the runs are scanned
+  const int per = (n + T - 1) / T;
+  const int b0 = min(n, tid * per);
+  const int b1 = min(n, b0 + per);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += pt[i + 1];
+  scan[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < T; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int run = scan[tid] - s;
+  for (int i = b0; i < b1; ++i) {
+    run += pt[i + 1];
+    pt[i + 1] = run;
+  }
+  if (tid == 0) pt[0] = 0;
+  __syncthreads();
+}
+
+// The last sequence s in [0, B) with pt[s] <= q; pt is non-decreasing, so
+// empty sequences before a non-empty one are skipped.
+__device__ __forceinline__ int find_seq(const int* pt, int B, int64_t q) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wave_uniform(pt[mid]) <= q) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The piece of a share that starts at flattened unit t (< end). The unit
+// space is head-major: KV head h holds units [h P, (h + 1) P), P = pt[B], and
+// within a head the sequences follow one another.
+struct Piece {
+  int seq;
+  int head;  // KV head
+  int u0;    // first unit within the segment
+  int u1;    // one past the last unit within the segment
+  int n_u;   // units of the whole segment
+  int64_t next_t;
+};
+
+__device__ __forceinline__ Piece locate(const int* pt, int B, int P, int64_t t, int64_t end) {
+  Piece p;
+  p.head = (int)(t / P);
+  const int rem = (int)(t - (int64_t)p.head * P);
+  p.seq = find_seq(pt, B, rem);
+  const int p0 = wave_uniform(pt[p.seq]);
+  p.n_u = wave_uniform(pt[p.seq + 1]) - p0;
+  p.u0 = rem - p0;
+  const int64_t seg_end = t - p.u0 + p.n_u;
+  p.next_t = end < seg_end ? end : seg_end;
+  p.u1 = p.u0 + (int)(p.next_t - t);
+  return p;
+}
+
+// Worker index of wave `wave` of this workgroup. Workgroups are dispatched to
+// the eight XCDs round-robin (workgroup g runs on XCD g % 8), so workgroups
+// g, g + 8, g + 16, ... share one L2. They are given consecutive worker
+// indices, which puts one contiguous slice of the head-major unit space -- a
+// few KV heads of every sequence -- on each XCD: K/V blocks that several
+// sequences share (a common prefix, beams of one prompt) are then read
+// through a single L2.
+__device__ __forceinline__ int64_t worker_index(int wave, int NW) {
+  const int n = gridDim.x;
+  const int xcd = blockIdx.x % 8;
+  const int q = n / 8, r = n % 8;
+  const int wg = xcd * q + min(xcd, r) + (int)(blockIdx.x / 8);
+  return (int64_t)wg * NW + wave;
+}
 
 template <int D, int G, bool FP8, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
@@ -83,225 +189,200 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
   constexpr int W = E / 2;           // fp16 pairs per lane per row
   static_assert(NLD >= 1 && kTile % RPL == 0, "tile shape");
 
-  const int wg = blockIdx.x;
-  const int head = wg % a.Hkv;
-  const int rest = wg / a.Hkv;
-  const int seq = rest % a.B;
-  const int part = rest / a.B;
+  extern __shared__ int dyn_smem[];
+  int* pt = dyn_smem;
+  build_prefix(a, pt, pt + a.B + 1);
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_uniform(threadIdx.x >> 6);
   const int r = lane / LPR;
   const int c = lane % LPR;
-  const int hq0 = head * G;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.B; i += NW * 64) a.ws_pt[i] = pt[i];
+  const int P = wave_uniform(pt[a.B]);
+  const int64_t total = (int64_t)a.Hkv * P;
+  const int64_t w = worker_index(wave, NW);
+  const int64_t start = share_start(w, total, a.workers);
+  const int64_t end = share_start(w + 1, total, a.workers);
 
-  const int L = clamp_len(a.ctx_lens[seq], a.max_blocks << a.bs_log2);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (L == 0) {
-    if (part == 0)
-      for (int i = threadIdx.x; i < G * D; i += NW * 64)
-        a.out[((size_t)seq * a.Hq + hq0) * D + i] = (f16)0.0f;
-    return;
-  }
-  if (part >= nparts) return;
-  const int t_begin = part * a.part_tokens;
-  const int t_end = min(L, t_begin + a.part_tokens);
-
-  // Query fragments: head hq0+g, elements c*E .. c*E+E-1, as fp16 pairs.
-  uint32_t qf[G][W];
-  {
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + ((size_t)seq * a.Hq + hq0) * D);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int w = 0; w < W; w += 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + g * (D / 2) + c * W + w);
-        qf[g][w] = v[0];
-        qf[g][w + 1] = v[1];
-        qf[g][w + 2] = v[2];
-        qf[g][w + 3] = v[3];
-      }
-  }
-
-  float m[G], l[G], acc[G][E];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
-  }
-
-  const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  // this wave takes tiles wave, wave + NW, wave + 2 NW, ...
-  const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
   const size_t head_bytes = (size_t)RB << a.bs_log2;
   const size_t blk_stride = (size_t)a.Hkv * head_bytes;
-  const uint8_t* kc_head = a.kc + (size_t)head * head_bytes;
-  const uint8_t* vc_head = a.vc + (size_t)head * head_bytes;
   const int bs_mask = (1 << a.bs_log2) - 1;
   const uint32_t lane_off = (uint32_t)(r * RB + c * 16);
 
-  for (int j0 = 0; j0 < my_tiles; j0 += 64) {
-    // Block ids of up to 64 of this wave's tiles, one per lane, fetched
-    // together so that no tile waits on its own table read.
-    int my_blk = -1;
-    if (j0 + lane < my_tiles) {
-      const int t = t_begin + (wave + NW * (j0 + lane)) * kTile;
-      my_blk = tab[t >> a.bs_log2];
+  for (int64_t t = start; t < end;) {
+    const Piece pc = locate(pt, a.B, P, t, end);
+    const int seq = pc.seq;
+    const int hq0 = pc.head * G;
+    const int L = wave_uniform(seq_len(a, seq));
+
+    // Query fragments: head hq0+g, elements c*E .. c*E+E-1, as fp16 pairs.
+    uint32_t qf[G][W];
+    {
+      const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + ((size_t)seq * a.Hq + hq0) * D);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int x = 0; x < W; x += 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + g * (D / 2) + c * W + x);
+          qf[g][x] = v[0];
+          qf[g][x + 1] = v[1];
+          qf[g][x + 2] = v[2];
+          qf[g][x + 3] = v[3];
+        }
     }
-    const int nj = min(64, my_tiles - j0);
-    for (int j = 0; j < nj; ++j) {
-      const int blk = __builtin_amdgcn_readlane(my_blk, j);
-      if ((unsigned)blk >= (unsigned)a.num_blocks) continue;  // never followed
-      const int t0 = t_begin + (wave + NW * (j0 + j)) * kTile;
-      // A tile lies inside one block, so all 16 rows are in bounds even past
-      // the sequence end; rows at or past t_end are masked below.
-      const bool full = t0 + kTile <= t_end;
-      const size_t boff = (size_t)blk * blk_stride + (size_t)(t0 & bs_mask) * RB;
-      const uint8_t* kb = kc_head + boff;
-      const uint8_t* vb = vc_head + boff;
 
-      u32x4 kr[NLD], vr[NLD];
-      bool valid[NLD];
+    float m[G], l[G], acc[G][E];
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        // non-temporal: K/V are streamed once per step; not allocating them in
-        // the caches measured 12% faster than default loads on this path
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + lane_off + i * RPL * RB));
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + lane_off + i * RPL * RB));
-        valid[i] = full || (t0 + i * RPL + r < t_end);
-      }
-      if (!full) {
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          if (!valid[i]) vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
+    }
 
-      // logits z[i][g] (log2 domain)
-      float z[NLD][G];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        uint32_t kw[W];
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          if constexpr (FP8)
-            kw[w] = (w & 1) ? fp8x2_hi_to_f16x2(kr[i][w / 2]) : fp8x2_lo_to_f16x2(kr[i][w / 2]);
-          else
-            kw[w] = kr[i][w];
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float s = 0.0f;
-#pragma unroll
-          for (int w = 0; w < W; ++w) s = dot2(qf[g][w], kw[w], s);
-          s = group_sum<LPR>(s);
-          z[i][g] = valid[i] ? s * a.qk_scale : -INFINITY;
-        }
-      }
+    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
+    const uint8_t* kc_head = a.kc + (size_t)pc.head * head_bytes;
+    const uint8_t* vc_head = a.vc + (size_t)pc.head * head_bytes;
+    for (int j0 = pc.u0; j0 < pc.u1; j0 += 64) {
+      // block ids of up to 64 tiles, one per lane, fetched together so that
+      // no tile waits on its own table read
+      int my_blk = -1;
+      if (j0 + lane < pc.u1) my_blk = tab[((j0 + lane) * kTile) >> a.bs_log2];
+      const int nj = min(64, pc.u1 - j0);
+      for (int j = 0; j < nj; ++j) {
+        const int blk = __builtin_amdgcn_readlane(my_blk, j);
+        if ((unsigned)blk >= (unsigned)a.num_blocks) continue;  // never followed
+        const int t0 = (j0 + j) * kTile;
+        // A tile lies inside one block, so all 16 rows are in bounds even past
+        // the sequence end; rows at or past L are masked below.
+        const bool full = t0 + kTile <= L;
+        const size_t boff = (size_t)blk * blk_stride + (size_t)(t0 & bs_mask) * RB;
+        const uint8_t* kb = kc_head + boff;
+        const uint8_t* vb = vc_head + boff;
 
-      // online softmax update and P.V for each head of the group
-      float p[NLD][G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mt = z[0][g];
-#pragma unroll
-        for (int i = 1; i < NLD; ++i) mt = fmaxf(mt, z[i][g]);
-        const float mn = fmaxf(m[g], mt);
-        const float ms = safe_max(mn);
-        const float alpha = fast_exp2(m[g] - ms);
-        float ps = 0.0f;
+        u32x4 kr[NLD], vr[NLD];
+        bool valid[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-          p[i][g] = fast_exp2(z[i][g] - ms);
-          ps += p[i][g];
+          // non-temporal: K/V are streamed once per step; not allocating them
+          // in the caches measured 12% faster than default loads on this path
+          kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + lane_off + i * RPL * RB));
+          vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + lane_off + i * RPL * RB));
+          valid[i] = full || (t0 + i * RPL + r < L);
         }
-        l[g] = l[g] * alpha + ps;
+        if (!full) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+          for (int i = 0; i < NLD; ++i)
+            if (!valid[i]) vr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+
+        // logits z[i][g] (log2 domain)
+        float z[NLD][G];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          uint32_t kw[W];
+#pragma unroll
+          for (int x = 0; x < W; ++x) {
+            if constexpr (FP8)
+              kw[x] = (x & 1) ? fp8x2_hi_to_f16x2(kr[i][x / 2]) : fp8x2_lo_to_f16x2(kr[i][x / 2]);
+            else
+              kw[x] = kr[i][x];
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float s = 0.0f;
+#pragma unroll
+            for (int x = 0; x < W; ++x) s = dot2(qf[g][x], kw[x], s);
+            s = group_sum<LPR>(s);
+            z[i][g] = valid[i] ? s * a.qk_scale : -INFINITY;
+          }
+        }
+
+        // online softmax update and P.V for each head of the group
+        float p[NLD][G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float mt = z[0][g];
+#pragma unroll
+          for (int i = 1; i < NLD; ++i) mt = fmaxf(mt, z[i][g]);
+          const float mn = fmaxf(m[g], mt);
+          const float ms = safe_max(mn);
+          const float alpha = fast_exp2(m[g] - ms);
+          float ps = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) {
+            p[i][g] = fast_exp2(z[i][g] - ms);
+            ps += p[i][g];
+          }
+          l[g] = l[g] * alpha + ps;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+          m[g] = mn;
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          float vf[E];
+#pragma unroll
+          for (int x = 0; x < W; ++x) {
+            uint32_t pw;
+            if constexpr (FP8)
+              pw = (x & 1) ? fp8x2_hi_to_f16x2(vr[i][x / 2]) : fp8x2_lo_to_f16x2(vr[i][x / 2]);
+            else
+              pw = vr[i][x];
+            vf[2 * x] = h_lo(pw);
+            vf[2 * x + 1] = h_hi(pw);
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p[i][g], vf[e], acc[g][e]);
+        }
+      }
+    }
+
+    // merge the RPL row states (lanes with equal c hold equal output slices)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = shfl_xor_f32(m[g], off);
+        const float lo = shfl_xor_f32(l[g], off);
+        const float mn = fmaxf(m[g], mo);
+        const float ms = safe_max(mn);
+        const float a1 = fast_exp2(m[g] - ms);
+        const float a2 = fast_exp2(mo - ms);
+        l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = acc[g][e] * a1 + shfl_xor_f32(acc[g][e], off) * a2;
         m[g] = mn;
       }
+    }
+
+    // the whole segment -> output; part of one -> this worker's slot
+    const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
+    const int slot = t == start ? 0 : 1;
+    if (lane < LPR) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        float vf[E];
+      for (int g = 0; g < G; ++g) {
+        if (whole) {
+          const float sc = l[g] > 0.0f ? a.v_out_scale / l[g] : 0.0f;
+          f16* o = a.out + ((size_t)seq * a.Hq + hq0 + g) * D + c * E;
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          uint32_t pw;
-          if constexpr (FP8)
-            pw = (w & 1) ? fp8x2_hi_to_f16x2(vr[i][w / 2]) : fp8x2_lo_to_f16x2(vr[i][w / 2]);
-          else
-            pw = vr[i][w];
-          vf[2 * w] = h_lo(pw);
-          vf[2 * w + 1] = h_hi(pw);
+          for (int e = 0; e < E; ++e) o[e] = (f16)(acc[g][e] * sc);
+        } else {
+          const size_t pi = ((size_t)w * 2 + slot) * G + g;
+          float* o = a.ws_o + pi * D + c * E;
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = acc[g][e] * a.v_out_scale;
+          if (lane == 0) {
+            a.ws_ml[2 * pi] = m[g];
+            a.ws_ml[2 * pi + 1] = l[g];
+          }
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p[i][g], vf[e], acc[g][e]);
       }
     }
-  }
-
-  // merge the RPL row states of this wave (lanes with equal c hold equal slices)
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = shfl_xor_f32(m[g], off);
-      const float lo = shfl_xor_f32(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float ms = safe_max(mn);
-      const float a1 = fast_exp2(m[g] - ms);
-      const float a2 = fast_exp2(mo - ms);
-      l[g] = l[g] * a1 + lo * a2;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[g][e] = acc[g][e] * a1 + shfl_xor_f32(acc[g][e], off) * a2;
-      m[g] = mn;
-    }
-  }
-
-  // merge the waves through LDS and write
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
-  if (lane < LPR) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) s_acc[wave][g][c * E + e] = acc[g][e];
-      if (lane == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-  const bool single = nparts == 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-    const float Ms = safe_max(M);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(s_m[w][g] - Ms);
-      lsum += s_l[w][g] * f;
-      o += s_acc[w][g][d] * f;
-    }
-    const size_t hrow = (size_t)seq * a.Hq + hq0 + g;
-    if (single) {
-      a.out[hrow * D + d] = (f16)(lsum > 0.0f ? o * a.v_out_scale / lsum : 0.0f);
-    } else {
-      const size_t pi = hrow * a.max_parts + part;
-      a.ws_o[pi * D + d] = o * a.v_out_scale;
-      if (d == 0) {
-        a.ws_ml[2 * pi] = M;
-        a.ws_ml[2 * pi + 1] = lsum;
-      }
-    }
+    t = pc.next_t;
   }
 }
 
@@ -321,61 +402,80 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
-// One wave per (sequence, query head). Lane p holds partition p's (m, l) for
-// up to 64 partitions at a time; each lane owns D/64 output elements and
-// issues the loads of all partitions' slices before summing.
-template <int D>
+// Pass 2. One wave per (sequence, query head). Lane k holds the weight of
+// piece k (64 pieces at a time); each lane owns D/64 output elements.
+template <int D, int G>
 __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
-  constexpr int DL = D / 64;  // output elements per lane
+  constexpr int DL = D / 64;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid >= a.B * a.Hq) return;
   const int lane = threadIdx.x & 63;
   const int seq = wid / a.Hq;
-  const int L = clamp_len(a.ctx_lens[seq], a.max_blocks << a.bs_log2);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;  // finished by pass 1
-  const size_t pbase = (size_t)wid * a.max_parts;
-  const float* ml = a.ws_ml + 2 * pbase;
-  const float* o = a.ws_o + pbase * D + lane * DL;
+  const int hq = wid - seq * a.Hq;
+  const int kvh = hq / G;
+  const int g = hq - kvh * G;
+  const int p0 = a.ws_pt[seq];
+  const int n_u = a.ws_pt[seq + 1] - p0;
+  f16* out = a.out + (size_t)wid * D + lane * DL;
+  if (n_u == 0) {
+#pragma unroll
+    for (int e = 0; e < DL; ++e) out[e] = (f16)0.0f;
+    return;
+  }
+  const int P = a.ws_pt[a.B];
+  const int64_t total = (int64_t)a.Hkv * P;
+  const int64_t W = a.workers;
+  const int64_t s0 = (int64_t)kvh * P + p0;  // the segment's units: [s0, s1)
+  const int64_t s1 = s0 + n_u;
+  // worker holding unit u: the largest w with share_start(w) <= u
+  const int64_t wa = ((s0 + 1) * W - 1) / total;
+  const int64_t wb = (s1 * W - 1) / total;
+  if (wa == wb) return;  // held whole by one worker: written by pass 1
+  const int np = (int)(wb - wa + 1);
+  // a piece sits in slot 0 if it starts its worker's share, else in slot 1
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
+  for (int k = lane; k < np; k += 64) {
+    const int64_t wk = wa + k;
+    const int64_t st = share_start(wk, total, W);
+    if (share_start(wk + 1, total, W) == st) continue;  // empty share
+    const int slot = st >= s0 ? 0 : 1;
+    M = fmaxf(M, a.ws_ml[2 * ((wk * 2 + slot) * G + g)]);
+  }
   M = wave_max(M);
   const float Ms = safe_max(M);
   float lsum = 0.0f;
   float acc[DL];
 #pragma unroll
   for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-  for (int p0 = 0; p0 < nparts; p0 += 64) {
-    float w = 0.0f;
-    if (p0 + lane < nparts) {
-      w = fast_exp2(ml[2 * (p0 + lane)] - Ms);
-      lsum += ml[2 * (p0 + lane) + 1] * w;
-    }
-    const int np = min(64, nparts - p0);
-    int q = 0;
-    for (; q + 4 <= np; q += 4) {
-      float v[4][DL];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < DL; ++e) v[u][e] = o[(size_t)(p0 + q + u) * D + e];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wu = readlane_f32(w, q + u);
-#pragma unroll
-        for (int e = 0; e < DL; ++e) acc[e] = fmaf(wu, v[u][e], acc[e]);
+  for (int k0 = 0; k0 < np; k0 += 64) {
+    float wgt = 0.0f;
+    int slot_k = 0;
+    const int k = k0 + lane;
+    if (k < np) {
+      const int64_t wk = wa + k;
+      const int64_t st = share_start(wk, total, W);
+      if (share_start(wk + 1, total, W) != st) {
+        slot_k = st >= s0 ? 0 : 1;
+        const int64_t pi = (wk * 2 + slot_k) * G + g;
+        wgt = fast_exp2(a.ws_ml[2 * pi] - Ms);
+        lsum += a.ws_ml[2 * pi + 1] * wgt;
       }
     }
-    for (; q < np; ++q) {
-      const float wq = readlane_f32(w, q);
+    const int nk = min(64, np - k0);
+    for (int j = 0; j < nk; ++j) {
+      const float wj = readlane_f32(wgt, j);
+      if (wj == 0.0f) continue;  // empty share, or a weight that underflowed
+      const int slot = __builtin_amdgcn_readlane(slot_k, j);
+      const int64_t pi = ((wa + k0 + j) * 2 + slot) * G + g;
+      const float* o = a.ws_o + pi * D + lane * DL;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] = fmaf(wq, o[(size_t)(p0 + q) * D + e], acc[e]);
+      for (int e = 0; e < DL; ++e) acc[e] = fmaf(wj, o[e], acc[e]);
     }
   }
   lsum = wave_sum(lsum);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-  for (int e = 0; e < DL; ++e) a.out[(size_t)wid * D + lane * DL + e] = (f16)(acc[e] * inv);
+  for (int e = 0; e < DL; ++e) out[e] = (f16)(acc[e] * inv);
 }
 
 }  // namespace
@@ -386,10 +486,10 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
 namespace pkv {
 namespace {
 
-typedef void (*PartFn)(AttnArgs);
+typedef void (*KernFn)(AttnArgs);
 
 template <int D, bool FP8>
-PartFn pick_partition_kernel(int G) {
+KernFn pick_partition_kernel(int G) {
   switch (G) {
     case 1: return attn_partition_kernel<D, 1, FP8, kWaves>;
     case 2: return attn_partition_kernel<D, 2, FP8, kWaves>;
@@ -399,9 +499,26 @@ PartFn pick_partition_kernel(int G) {
   }
 }
 
-PartFn pick(int D, int G, bool fp8) {
+KernFn pick(int D, int G, bool fp8) {
   if (D == 64) return fp8 ? pick_partition_kernel<64, true>(G) : pick_partition_kernel<64, false>(G);
   if (D == 128) return fp8 ? pick_partition_kernel<128, true>(G) : pick_partition_kernel<128, false>(G);
+  return nullptr;
+}
+
+template <int D>
+KernFn pick_reduce_d(int G) {
+  switch (G) {
+    case 1: return attn_reduce_kernel<D, 1>;
+    case 2: return attn_reduce_kernel<D, 2>;
+    case 4: return attn_reduce_kernel<D, 4>;
+    case 8: return attn_reduce_kernel<D, 8>;
+    default: return nullptr;
+  }
+}
+
+KernFn pick_reduce(int D, int G) {
+  if (D == 64) return pick_reduce_d<64>(G);
+  if (D == 128) return pick_reduce_d<128>(G);
   return nullptr;
 }
 
@@ -411,52 +528,116 @@ int log2_exact(int v) {
   return (1 << k) == v ? k : -1;
 }
 
-// Default partition: the largest power of two in [256, 2048] that is at most
-// a quarter (one query head per KV head) or half (grouped heads) of the
-// largest context the block table can hold. Measured on MI355X: 512 for the
-// Llama-2-7B batch-64 workload, 1024-2048 for 4k contexts and for grouped heads.
-int default_partition(int group, int max_blocks, int block_size) {
-  const int64_t max_ctx = (int64_t)max_blocks * block_size;
-  const int64_t target = max_ctx / (group >= 2 ? 2 : 4);
-  int p = 256;
-  while (p < 2048 && 2 * (int64_t)p <= target) p *= 2;
-  return p;
+int unit_tokens_for(int group) { return group >= 4 ? 32 : kTile; }
+
+size_t dyn_lds_bytes(int B) { return (size_t)(B + 1 + kWaves * 64) * sizeof(int); }
+
+// Workgroups of a pass-1 kernel resident at once on the current device
+// (occupancy x compute units), cached per (kernel, LDS size, device); 0 on error.
+int resident_workgroups(KernFn fn, size_t dyn_lds) {
+  struct Entry {
+    KernFn fn;
+    size_t lds;
+    int dev;
+    int wgs;
+  };
+  static std::mutex mu;
+  static Entry cache[128];
+  static int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].fn == fn && cache[i].lds == dyn_lds && cache[i].dev == dev) return cache[i].wgs;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWaves * 64,
+                                                   dyn_lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int wgs = per_cu * cus;
+  if (n_cache < 128) cache[n_cache++] = Entry{fn, dyn_lds, dev, wgs};
+  return wgs;
 }
 
-int resolve_partition(int partition_tokens, int group, int max_blocks, int block_size) {
-  if (partition_tokens == 0) return default_partition(group, max_blocks, block_size);
-  if (partition_tokens < 64 || partition_tokens % 64 != 0) return -1;
-  return partition_tokens;
-}
-
-int max_partitions(int max_blocks, int block_size, int part) {
+// Units of B sequences of the longest context the block table can hold.
+int64_t unit_upper_bound(int B, int max_blocks, int block_size, int unit) {
   const int64_t lmax = (int64_t)max_blocks * block_size;
-  return (int)((lmax + part - 1) / part);
+  return (int64_t)B * ((lmax + unit - 1) / unit);
+}
+
+struct Plan {
+  KernFn fn;
+  KernFn reduce;
+  int unit;
+  int workers;  // for a launch of kMaxSeqs sequences or fewer
+};
+
+// Validates the shape and picks the kernels and the worker count; returns a
+// status code.
+int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+         int max_blocks_per_seq, int kv_dtype, int partition_tokens, bool need_workers, Plan* p) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
+  if (partition_tokens < 0 || partition_tokens % kTile != 0) return PKV_ERR_INVALID;
+  const int G = num_q_heads / num_kv_heads;
+  p->fn = pick(head_dim, G, kv_dtype == PKV_KV_FP8_E4M3);
+  p->reduce = pick_reduce(head_dim, G);
+  if (!p->fn || !p->reduce) return PKV_ERR_INVALID;
+  p->unit = unit_tokens_for(G);
+  const int B = num_seqs < kMaxSeqs ? num_seqs : kMaxSeqs;
+  // unit counts and prefixes are int32 on the device
+  const int64_t ub = unit_upper_bound(B, max_blocks_per_seq, block_size, p->unit);
+  if ((int64_t)max_blocks_per_seq * block_size > 0x7FFFFFFF || ub > 0x7FFFFFFF) return PKV_ERR_INVALID;
+  p->workers = 0;
+  if (!need_workers || B == 0) return PKV_OK;
+  const int64_t ub_all = ub * num_kv_heads;
+  int64_t W;
+  if (partition_tokens > 0) {
+    const int64_t per = (partition_tokens + p->unit - 1) / p->unit;
+    W = (ub_all + per - 1) / per;
+  } else {
+    const int wgs = resident_workgroups(p->fn, dyn_lds_bytes(B));
+    if (wgs <= 0) return PKV_ERR_HIP;
+    W = (int64_t)wgs * kWaves;
+  }
+  if (W > ub_all) W = ub_all;
+  if (W > kMaxWorkers) W = kMaxWorkers;
+  if (W < 1) W = 1;
+  W = (W + kWaves - 1) / kWaves * kWaves;  // every wave of the grid is a worker
+  p->workers = (int)W;
+  return PKV_OK;
 }
 
 }  // namespace
 }  // namespace pkv
 
-extern "C" int paged_attn_default_partition(int num_q_heads, int num_kv_heads, int head_dim,
-                                            int block_size, int max_blocks_per_seq, int kv_dtype) {
-  (void)head_dim;
-  (void)kv_dtype;
-  if (num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return -1;
-  return pkv::default_partition(num_q_heads / num_kv_heads, max_blocks_per_seq, block_size);
+extern "C" int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_blocks_per_seq, int kv_dtype,
+                                         int partition_tokens) {
+  pkv::Plan p;
+  if (num_seqs <= 0) return PKV_ERR_INVALID;
+  const int rc = pkv::plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                           kv_dtype, partition_tokens, true, &p);
+  return rc == PKV_OK ? p.workers : rc;
 }
 
 extern "C" size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                                     int head_dim, int max_blocks_per_seq,
                                                     int block_size, int partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_blocks_per_seq <= 0 || block_size <= 0)
-    return 0;
-  const int part = pkv::resolve_partition(partition_tokens, num_q_heads / num_kv_heads,
-                                          max_blocks_per_seq, block_size);
-  if (part < 0) return 0;
-  const int mp = pkv::max_partitions(max_blocks_per_seq, block_size, part);
-  if (mp <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * mp * (size_t)(head_dim + 2) * sizeof(float);
+  (void)max_blocks_per_seq;
+  (void)block_size;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  if (partition_tokens < 0 || partition_tokens % pkv::kTile != 0) return 0;
+  const int G = num_q_heads / num_kv_heads;
+  const int b = num_seqs < pkv::kMaxSeqs ? num_seqs : pkv::kMaxSeqs;
+  const size_t pieces = (size_t)pkv::kMaxWorkers * 2 * G;
+  const size_t bytes = pieces * (size_t)(head_dim + 2) * sizeof(float) + (size_t)(b + 1) * sizeof(int32_t);
+  return (bytes + 255) / 256 * 256;
 }
 
 extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_cache,
@@ -468,65 +649,56 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
                                         float v_scale, int partition_tokens, void* workspace,
                                         size_t workspace_bytes, int passes, void* stream) {
   using namespace pkv;
-  if (passes < 1 || passes > 3) return PKV_ERR_INVALID;
-  if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0)
-    return PKV_ERR_INVALID;
-  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
-  if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
-  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
-  const int G = num_q_heads / num_kv_heads;
-  const int part = resolve_partition(partition_tokens, G, max_blocks_per_seq, block_size);
-  if (part < 0) return PKV_ERR_INVALID;
-  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
-  PartFn fn = pick(head_dim, G, fp8);
-  if (!fn) return PKV_ERR_INVALID;
+  if (passes < 1 || passes > 3 || num_blocks <= 0) return PKV_ERR_INVALID;
+  Plan pl;
+  int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
+                partition_tokens, false, &pl);
+  if (rc != PKV_OK) return rc;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
-  const int mp = max_partitions(max_blocks_per_seq, block_size, part);
   const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                        max_blocks_per_seq, block_size, part);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_INVALID;
-  const int64_t grid1 = (int64_t)num_kv_heads * num_seqs * mp;
-  if (grid1 > 0x7FFFFFFF) return PKV_ERR_INVALID;
+                                                        max_blocks_per_seq, block_size, partition_tokens);
+  if (!workspace || workspace_bytes < need) return PKV_ERR_INVALID;
+  rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
+            partition_tokens, true, &pl);
+  if (rc != PKV_OK) return rc;
 
-  AttnArgs a;
-  a.q = static_cast<const f16*>(q);
-  a.kc = static_cast<const uint8_t*>(k_cache);
-  a.vc = static_cast<const uint8_t*>(v_cache);
-  a.tables = block_tables;
-  a.ctx_lens = ctx_lens;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                (size_t)num_seqs * num_q_heads * mp * head_dim * sizeof(float))
-                     : nullptr;
-  a.out = static_cast<f16*>(out);
-  a.max_blocks = max_blocks_per_seq;
-  a.B = num_seqs;
-  a.Hkv = num_kv_heads;
-  a.Hq = num_q_heads;
-  a.bs_log2 = log2_exact(block_size);
-  a.num_blocks = num_blocks;
-  a.part_tokens = part;
-  a.max_parts = mp;
+  const int G = num_q_heads / num_kv_heads;
+  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
   const float kLog2e = 1.4426950408889634f;
-  a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
-  a.v_out_scale = fp8 ? v_scale : 1.0f;
-
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (passes & 1) {
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid1), dim3(kWaves * 64), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
-  }
-  if ((passes & 2) && mp > 1) {
-    const int waves = num_seqs * num_q_heads;
-    const unsigned grid2 = (unsigned)((waves + 3) / 4);
-    if (head_dim == 64)
-      hipLaunchKernelGGL(attn_reduce_kernel<64>, dim3(grid2), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_reduce_kernel<128>, dim3(grid2), dim3(256), 0, s, a);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  // more than kMaxSeqs sequences: consecutive launches, in order on the stream
+  for (int b0 = 0; b0 < num_seqs; b0 += kMaxSeqs) {
+    const int B = num_seqs - b0 < kMaxSeqs ? num_seqs - b0 : kMaxSeqs;
+    AttnArgs a;
+    a.q = static_cast<const f16*>(q) + (size_t)b0 * num_q_heads * head_dim;
+    a.kc = static_cast<const uint8_t*>(k_cache);
+    a.vc = static_cast<const uint8_t*>(v_cache);
+    a.tables = block_tables + (size_t)b0 * max_blocks_per_seq;
+    a.ctx_lens = ctx_lens + b0;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + (size_t)kMaxWorkers * 2 * G * head_dim;
+    a.ws_pt = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)kMaxWorkers * 2 * G * 2);
+    a.out = static_cast<f16*>(out) + (size_t)b0 * num_q_heads * head_dim;
+    a.max_blocks = max_blocks_per_seq;
+    a.B = B;
+    a.Hkv = num_kv_heads;
+    a.Hq = num_q_heads;
+    a.bs_log2 = log2_exact(block_size);
+    a.num_blocks = num_blocks;
+    a.unit_tokens = pl.unit;
+    a.workers = pl.workers;
+    a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
+    a.v_out_scale = fp8 ? v_scale : 1.0f;
+    if (passes & 1) {
+      hipLaunchKernelGGL(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64), dyn_lds_bytes(B), s, a);
+      if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    }
+    if (passes & 2) {
+      const int waves = B * num_q_heads;
+      hipLaunchKernelGGL(pl.reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+      if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    }
   }
   return PKV_OK;
 }

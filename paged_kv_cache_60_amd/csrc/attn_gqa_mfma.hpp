@@ -1,6 +1,6 @@
 // Pass 1 of paged decode attention for grouped-query heads (G = 4 or 8 query
 // heads per KV head), on the matrix cores. Included by attn_decode.hip, whose
-// AttnArgs, helpers and pass 2 it shares; the partials it writes are the same.
+// AttnArgs, work split (shares, pieces, partial slots) and pass 2 it shares.
 //
 // With G query heads per KV head, q.K over a 16-token tile is a small dense
 // contraction (16 tokens x G heads x D), so it runs as v_mfma_f32_16x16x32_f16:
@@ -20,10 +20,9 @@
 //     row e; lane i receives element i of rows e = 0..3).
 //   - The O^T accumulator puts head h in lane column h, where that head's
 //     online-softmax max and rescale factor already live.
-// Each wave processes 32-token chunks (two 16-token tiles, each inside one
-// block) of the partition; the partition's waves then merge through LDS as in
-// the VALU kernel. Rows at or past the end of the sequence are masked in the
-// logits and written to LDS as zeros.
+// A unit is a 32-token chunk (two 16-token tiles, each inside one block). Each
+// wave is a worker with its own LDS buffer for V; rows at or past the end of
+// the sequence are masked in the logits and written to LDS as zeros.
 
 namespace pkv {
 namespace {
@@ -60,63 +59,29 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   constexpr int RPL = 64 / LPR;         // rows per V load
   constexpr int VLD = 32 / RPL;         // V loads per lane per 32-token chunk
   constexpr int VS = D + 16;            // LDS row stride of V, halves (16-byte aligned)
-  constexpr int V_LDS = NW * 32 * VS * 2;
-  constexpr int M_LDS = NW * G * D * 4 + 2 * NW * 16 * 4;
-  constexpr int SMEM = V_LDS > M_LDS ? V_LDS : M_LDS;
   static_assert(RPL <= 16 && 16 % RPL == 0, "a V load stays inside one tile");
 
-  __shared__ __align__(16) char smem[SMEM];
+  __shared__ __align__(16) _Float16 vlds[NW * 32 * VS];
+  extern __shared__ int dyn_smem[];
+  int* pt = dyn_smem;
+  build_prefix(a, pt, pt + a.B + 1);
 
-  const int wg = blockIdx.x;
-  const int head = wg % a.Hkv;
-  const int rest = wg / a.Hkv;
-  const int seq = rest % a.B;
-  const int part = rest / a.B;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_uniform(threadIdx.x >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int hq0 = head * G;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.B; i += NW * 64) a.ws_pt[i] = pt[i];
+  const int P = wave_uniform(pt[a.B]);
+  const int64_t total = (int64_t)a.Hkv * P;
+  const int64_t w = worker_index(wave, NW);
+  const int64_t start = share_start(w, total, a.workers);
+  const int64_t end = share_start(w + 1, total, a.workers);
 
-  const int L = clamp_len(a.ctx_lens[seq], a.max_blocks << a.bs_log2);
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
-  if (L == 0) {
-    if (part == 0)
-      for (int i = threadIdx.x; i < G * D; i += NW * 64)
-        a.out[((size_t)seq * a.Hq + hq0) * D + i] = (f16)0.0f;
-    return;
-  }
-  if (part >= nparts) return;
-  const int t_begin = part * a.part_tokens;
-  const int t_end = min(L, t_begin + a.part_tokens);
-
-  // Q^T as the B operand: head = col (zero past G), d = grp * DQ + 8m + slot
-  f16x8 qb[KM];
-#pragma unroll
-  for (int m = 0; m < KM; ++m) {
-    if (col < G) {
-      const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + col) * D + grp * DQ + 8 * m;
-      qb[m] = *reinterpret_cast<const f16x8*>(qrow);
-    } else {
-      qb[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  f32x4 o[NT];
-#pragma unroll
-  for (int c = 0; c < NT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_part = 0.0f;
-
-  const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
-  const int nchunks = (t_end - t_begin + 31) / 32;
-  const int my_chunks = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;
   const size_t head_bytes = (size_t)RB << a.bs_log2;
   const size_t blk_stride = (size_t)a.Hkv * head_bytes;
-  const uint8_t* kc_head = a.kc + (size_t)head * head_bytes;
-  const uint8_t* vc_head = a.vc + (size_t)head * head_bytes;
   const int bs_mask = (1 << a.bs_log2) - 1;
-  _Float16* vbuf = reinterpret_cast<_Float16*>(smem) + wave * 32 * VS;
+  _Float16* vbuf = vlds + wave * 32 * VS;
   const uint32_t k_lane_off = (uint32_t)(col * RB + grp * DQ * ELEM);
   const int v_row = lane / LPR;        // row within a V load
   const int v_cb = (lane % LPR) * 16;  // byte offset within the row
@@ -125,169 +90,178 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   const int tr_row = 4 * grp + (col >> 2);
   const int tr_col = 4 * (col & 3);
 
-  for (int j0 = 0; j0 < my_chunks; j0 += 32) {
-    // block ids of up to 32 chunks (two tiles each), one per lane
-    int my_blk = -1;
-    {
-      const int jj = j0 + (lane >> 1);
-      if (jj < my_chunks) {
-        const int t = t_begin + 32 * (wave + NW * jj) + 16 * (lane & 1);
-        if (t < t_end) my_blk = tab[t >> a.bs_log2];
+  for (int64_t t = start; t < end;) {
+    const Piece pc = locate(pt, a.B, P, t, end);
+    const int seq = pc.seq;
+    const int hq0 = pc.head * G;
+    const int L = wave_uniform(seq_len(a, seq));
+
+    // Q^T as the B operand: head = col (zero past G), d = grp * DQ + 8m + slot
+    f16x8 qb[KM];
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      if (col < G) {
+        const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + col) * D + grp * DQ + 8 * m;
+        qb[m] = *reinterpret_cast<const f16x8*>(qrow);
+      } else {
+        qb[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    const int nj = min(32, my_chunks - j0);
-    for (int j = 0; j < nj; ++j) {
-      const int ta = t_begin + 32 * (wave + NW * (j0 + j));
-      const int blk_a = __builtin_amdgcn_readlane(my_blk, 2 * j);
-      const int blk_b = __builtin_amdgcn_readlane(my_blk, 2 * j + 1);
-      const bool ok_a = (unsigned)blk_a < (unsigned)a.num_blocks;
-      const bool ok_b = (unsigned)blk_b < (unsigned)a.num_blocks;
-      const size_t off_a = (size_t)blk_a * blk_stride + (size_t)(ta & bs_mask) * RB;
-      const size_t off_b = (size_t)blk_b * blk_stride + (size_t)((ta + 16) & bs_mask) * RB;
 
-      // K rows (A operand of S) and V rows (to LDS)
-      u32x4 ka[KLD], kb[KLD], vv[VLD];
+    f32x4 o[NT];
 #pragma unroll
-      for (int i = 0; i < KLD; ++i) {
-        ka[i] = ok_a ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i))
-                     : u32x4{0u, 0u, 0u, 0u};
-        kb[i] = ok_b ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i))
-                     : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const bool in_b = i * RPL >= 16;
-        const bool ok = in_b ? ok_b : ok_a;
-        const size_t off = in_b ? off_b : off_a;
-        const int r = (i * RPL + v_row) & 15;
-        vv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc_head + off + r * RB + v_cb))
-                   : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int c = 0; c < NT; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_part = 0.0f;
 
-      // S = K . Q^T for both tiles
-      f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
+    const uint8_t* kc_head = a.kc + (size_t)pc.head * head_bytes;
+    const uint8_t* vc_head = a.vc + (size_t)pc.head * head_bytes;
+    for (int j0 = pc.u0; j0 < pc.u1; j0 += 32) {
+      // block ids of up to 32 chunks (two tiles each), one per lane
+      int my_blk = -1;
+      {
+        const int jj = j0 + (lane >> 1);
+        const int tt = 32 * jj + 16 * (lane & 1);
+        if (jj < pc.u1 && tt < L) my_blk = tab[tt >> a.bs_log2];
+      }
+      const int nj = min(32, pc.u1 - j0);
+      for (int j = 0; j < nj; ++j) {
+        const int ta = 32 * (j0 + j);
+        const int blk_a = __builtin_amdgcn_readlane(my_blk, 2 * j);
+        const int blk_b = __builtin_amdgcn_readlane(my_blk, 2 * j + 1);
+        const bool ok_a = (unsigned)blk_a < (unsigned)a.num_blocks;
+        const bool ok_b = (unsigned)blk_b < (unsigned)a.num_blocks;
+        const size_t off_a = (size_t)blk_a * blk_stride + (size_t)(ta & bs_mask) * RB;
+        const size_t off_b = (size_t)blk_b * blk_stride + (size_t)((ta + 16) & bs_mask) * RB;
+
+        // K rows (A operand of S) and V rows (to LDS)
+        u32x4 ka[KLD], kb[KLD], vv[VLD];
 #pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        f16x8 aa, ab;
-        if constexpr (FP8) {
-          aa = fp8x8_to_f16x8(ka[m / 2][(m % 2) * 2], ka[m / 2][(m % 2) * 2 + 1]);
-          ab = fp8x8_to_f16x8(kb[m / 2][(m % 2) * 2], kb[m / 2][(m % 2) * 2 + 1]);
-        } else {
-          aa = f16x8_from_u32x4(ka[m]);
-          ab = f16x8_from_u32x4(kb[m]);
+        for (int i = 0; i < KLD; ++i) {
+          ka[i] = ok_a ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i))
+                       : u32x4{0u, 0u, 0u, 0u};
+          kb[i] = ok_b ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i))
+                       : u32x4{0u, 0u, 0u, 0u};
         }
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa, qb[m], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(ab, qb[m], sb, 0, 0, 0);
-      }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+          const bool in_b = i * RPL >= 16;
+          const bool ok = in_b ? ok_b : ok_a;
+          const size_t off = in_b ? off_b : off_a;
+          const int r = (i * RPL + v_row) & 15;
+          vv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc_head + off + r * RB + v_cb))
+                     : u32x4{0u, 0u, 0u, 0u};
+        }
 
-      // online softmax per head (lane column); tokens of this lane: ta+4grp+v, ta+16+4grp+v
-      float z[8];
+        // S = K . Q^T for both tiles
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tka = ta + 4 * grp + v;
-        const int tkb = ta + 16 + 4 * grp + v;
-        z[v] = (ok_a && tka < t_end) ? sa[v] * a.qk_scale : -INFINITY;
-        z[4 + v] = (ok_b && tkb < t_end) ? sb[v] * a.qk_scale : -INFINITY;
-      }
-      float mt = z[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
-      mt = fmaxf(mt, shfl_xor_f32(mt, 16));
-      mt = fmaxf(mt, shfl_xor_f32(mt, 32));
-      const float mn = fmaxf(m_run, mt);
-      const float ms = safe_max(mn);
-      const float alpha = fast_exp2(m_run - ms);
-      f16x8 pb;
-      float ps = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(z[i] - ms);
-        ps += p;
-        pb[i] = (_Float16)p;
-      }
-      l_part = l_part * alpha + ps;
-      m_run = mn;
-#pragma unroll
-      for (int c = 0; c < NT; ++c) o[c] *= alpha;
+        for (int m = 0; m < KM; ++m) {
+          f16x8 aa, ab;
+          if constexpr (FP8) {
+            aa = fp8x8_to_f16x8(ka[m / 2][(m % 2) * 2], ka[m / 2][(m % 2) * 2 + 1]);
+            ab = fp8x8_to_f16x8(kb[m / 2][(m % 2) * 2], kb[m / 2][(m % 2) * 2 + 1]);
+          } else {
+            aa = f16x8_from_u32x4(ka[m]);
+            ab = f16x8_from_u32x4(kb[m]);
+          }
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa, qb[m], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(ab, qb[m], sb, 0, 0, 0);
+        }
 
-      // V rows -> LDS as fp16 (rows past the end as zeros)
+        // online softmax per head (lane column); tokens of this lane: ta+4grp+v, ta+16+4grp+v
+        float z[8];
 #pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int r = i * RPL + v_row;  // 0..31
-        const bool ok = (r < 16 ? ok_a : ok_b) && (ta + r < t_end);
-        _Float16* dst = vbuf + r * VS + v_cb / ELEM;
-        if constexpr (FP8) {
-          const f16x8 lo = ok ? fp8x8_to_f16x8(vv[i][0], vv[i][1]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          const f16x8 hi = ok ? fp8x8_to_f16x8(vv[i][2], vv[i][3]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          *reinterpret_cast<f16x8*>(dst) = lo;
-          *reinterpret_cast<f16x8*>(dst + 8) = hi;
-        } else {
-          *reinterpret_cast<u32x4*>(dst) = ok ? vv[i] : u32x4{0u, 0u, 0u, 0u};
+        for (int v = 0; v < 4; ++v) {
+          const int tka = ta + 4 * grp + v;
+          const int tkb = ta + 16 + 4 * grp + v;
+          z[v] = (ok_a && tka < L) ? sa[v] * a.qk_scale : -INFINITY;
+          z[4 + v] = (ok_b && tkb < L) ? sb[v] * a.qk_scale : -INFINITY;
+        }
+        float mt = z[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
+        mt = fmaxf(mt, shfl_xor_f32(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f32(mt, 32));
+        const float mn = fmaxf(m_run, mt);
+        const float ms = safe_max(mn);
+        const float alpha = fast_exp2(m_run - ms);
+        f16x8 pb;
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = fast_exp2(z[i] - ms);
+          ps += p;
+          pb[i] = (_Float16)p;
+        }
+        l_part = l_part * alpha + ps;
+        m_run = mn;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) o[c] *= alpha;
+
+        // V rows -> LDS as fp16 (rows past the end as zeros)
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+          const int r = i * RPL + v_row;  // 0..31
+          const bool ok = (r < 16 ? ok_a : ok_b) && (ta + r < L);
+          _Float16* dst = vbuf + r * VS + v_cb / ELEM;
+          if constexpr (FP8) {
+            const f16x8 lo = ok ? fp8x8_to_f16x8(vv[i][0], vv[i][1]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            const f16x8 hi = ok ? fp8x8_to_f16x8(vv[i][2], vv[i][3]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            *reinterpret_cast<f16x8*>(dst) = lo;
+            *reinterpret_cast<f16x8*>(dst + 8) = hi;
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = ok ? vv[i] : u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+
+        // O^T += V^T . P^T, one 16-wide d tile at a time
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const _Float16* p1 = vbuf + tr_row * VS + 16 * c + tr_col;
+          const _Float16* p2 = vbuf + (16 + tr_row) * VS + 16 * c + tr_col;
+          // whole-vector casts: a bit_cast of single vector elements was lowered
+          // to element 0 by this compiler
+          const f16x4 r1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
+          const f16x4 r2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2)));
+          const f16x8 va = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[c], 0, 0, 0);
         }
       }
+    }
 
-      // O^T += V^T . P^T, one 16-wide d tile at a time
+    // per-head sum over the four lane groups; the max is already common
+    l_part += shfl_xor_f32(l_part, 16);
+    l_part += shfl_xor_f32(l_part, 32);
+
+    // lane (head col, group grp) holds d = 16c + 4grp + v of its head
+    const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
+    const int slot = t == start ? 0 : 1;
+    if (col < G) {
+      if (whole) {
+        const float sc = l_part > 0.0f ? a.v_out_scale / l_part : 0.0f;
+        f16* orow = a.out + ((size_t)seq * a.Hq + hq0 + col) * D + 4 * grp;
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const _Float16* p1 = vbuf + tr_row * VS + 16 * c + tr_col;
-        const _Float16* p2 = vbuf + (16 + tr_row) * VS + 16 * c + tr_col;
-        // whole-vector casts: a bit_cast of single vector elements was lowered
-        // to element 0 by this compiler
-        const f16x4 r1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
-        const f16x4 r2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2)));
-        const f16x8 va = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[c], 0, 0, 0);
+        for (int c = 0; c < NT; ++c) {
+          f16x4 h;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = (f16)(o[c][v] * sc);
+          *reinterpret_cast<f16x4*>(orow + 16 * c) = h;
+        }
+      } else {
+        const size_t pi = ((size_t)w * 2 + slot) * G + col;
+        float* orow = a.ws_o + pi * D + 4 * grp;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * a.v_out_scale;
+        if (grp == 0) {
+          a.ws_ml[2 * pi] = m_run;
+          a.ws_ml[2 * pi + 1] = l_part;
+        }
       }
     }
-  }
-
-  // per-head sum over the four lane groups; the max is already common
-  l_part += shfl_xor_f32(l_part, 16);
-  l_part += shfl_xor_f32(l_part, 32);
-
-  // merge the waves through LDS (reusing the V buffers) and write
-  __syncthreads();
-  float* s_o = reinterpret_cast<float*>(smem);               // [NW][G][D]
-  float* s_m = s_o + NW * G * D;                              // [NW][16]
-  float* s_l = s_m + NW * 16;                                 // [NW][16]
-  if (col < G) {
-#pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s_o[(wave * G + col) * D + 16 * c + 4 * grp + v] = o[c][v];
-    if (grp == 0) {
-      s_m[wave * 16 + col] = m_run;
-      s_l[wave * 16 + col] = l_part;
-    }
-  }
-  __syncthreads();
-  const bool single = nparts == 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = s_m[g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + g]);
-    const float Ms = safe_max(M);
-    float lsum = 0.0f, acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(s_m[w * 16 + g] - Ms);
-      lsum += s_l[w * 16 + g] * f;
-      acc += s_o[(w * G + g) * D + d] * f;
-    }
-    const size_t hrow = (size_t)seq * a.Hq + hq0 + g;
-    if (single) {
-      a.out[hrow * D + d] = (f16)(lsum > 0.0f ? acc * a.v_out_scale / lsum : 0.0f);
-    } else {
-      const size_t pi = hrow * a.max_parts + part;
-      a.ws_o[pi * D + d] = acc * a.v_out_scale;
-      if (d == 0) {
-        a.ws_ml[2 * pi] = M;
-        a.ws_ml[2 * pi + 1] = lsum;
-      }
-    }
+    t = pc.next_t;
   }
 }
 

@@ -15,7 +15,7 @@ copy-on-write):
   3. paged_block_copy for the copy-on-write pairs, if any;
   4. paged_kv_write_step: the new tokens' K/V plus the step's context lengths
      and table entries, in one kernel;
-  5. paged_attn_decode (partition pass and reduce pass).
+  5. paged_attn_decode (pass 1 over equal shares of the KV, pass 2 for split segments).
 
 Pinned metadata buffers alternate between two halves so the host can prepare
 step k+1 while step k's kernels may still be queued; an event per half keeps

@@ -124,16 +124,21 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_pe
                                                              partition_tokens))
 
 
-def default_partition(num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                      kv_dtype=F16) -> int:
-    return int(_lib.load().paged_attn_default_partition(num_q_heads, num_kv_heads, head_dim, block_size,
-                                                        max_blocks_per_seq, kv_dtype_code(kv_dtype)))
+def decode_workers(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   kv_dtype=F16, partition_tokens=0) -> int:
+    """Workers (waves) that pass 1 of paged_attn_decode uses for this shape on the current device."""
+    n = int(_lib.load().paged_attn_decode_workers(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                  max_blocks_per_seq, kv_dtype_code(kv_dtype),
+                                                  partition_tokens))
+    check(min(n, 0), "paged_attn_decode_workers")
+    return n
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale, kv_dtype=F16,
                       k_scale=1.0, v_scale=1.0, partition_tokens=0, workspace=None, passes=3,
                       stream=None):
-    """out/q [B, Hq, D] fp16; block_tables [B, max_blocks] int32; ctx_lens [B] int32."""
+    """out/q [B, Hq, D] fp16; block_tables [B, max_blocks] int32; ctx_lens [B] int32.
+    workspace: device buffer of at least workspace_bytes(...) bytes; allocated here if None."""
     w = "paged_attn_decode"
     _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
     _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")
@@ -147,11 +152,13 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
     _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
              and ctx_lens.is_contiguous(), w, "ctx_lens")
     maxb = block_tables.shape[1]
-    need = workspace_bytes(B, hq, hkv, d, maxb, bs, partition_tokens) if B > 0 and maxb > 0 else 0
+    need = workspace_bytes(B, hq, hkv, d, maxb, bs, partition_tokens) if B > 0 else 0
     ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
     if need:
-        _require(workspace is not None and workspace.is_cuda
-                 and workspace.numel() * workspace.element_size() >= need, w, "workspace too small")
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _require(workspace.is_cuda and workspace.numel() * workspace.element_size() >= need, w,
+                 "workspace too small")
         ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
     lib = _lib.load()
     check(lib.paged_attn_decode_passes(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), maxb,

@@ -56,7 +56,8 @@ def attn(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d=96), dict(bs=8), dict(bs=48), dict(hq=12, hkv=8), dict(hq=24, hkv=8),
-                                 dict(dt=2), dict(part=100), dict(part=32), dict(passes=0), dict(passes=4),
+                                 dict(dt=2), dict(part=100), dict(part=8), dict(part=-16), dict(passes=0),
+                                 dict(passes=4),
                                  dict(hkv=0), dict(nb=0), dict(maxb=0), dict(out=N), dict(q=N),
                                  dict(ws=N, maxb=64), dict(wsb=16, maxb=64), dict(B=-1)])
 def test_attention_rejects_bad_arguments(bad):
@@ -69,17 +70,34 @@ def test_attention_empty_batch_is_ok():
 
 def test_workspace_bytes():
     lib = _lib.load()
-    # 128 blocks of 16 = 2048 tokens, 512-token partitions -> 4 partials of (D + 2) floats
-    assert lib.paged_attn_decode_workspace_bytes(64, 32, 32, 128, 128, 16, 512) == 64 * 32 * 4 * 130 * 4
-    assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 2, 16, 512) == 0  # one partition: no partials
-    assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 2, 16, 100) == 0  # invalid partition size
-    # default partition: largest power of two in [256, 2048] <= max_ctx/4 (MHA) or max_ctx/2 (GQA)
-    assert lib.paged_attn_default_partition(32, 32, 128, 16, 131, 0) == 512     # 2096 tokens
-    assert lib.paged_attn_default_partition(40, 40, 128, 32, 129, 0) == 1024    # 4128 tokens
-    assert lib.paged_attn_default_partition(16, 8, 128, 16, 256, 0) == 2048     # 4096 tokens, GQA
-    assert lib.paged_attn_default_partition(64, 8, 128, 64, 35, 1) == 1024      # 2240 tokens, GQA
-    assert lib.paged_attn_default_partition(8, 8, 64, 16, 16, 0) == 256         # small: clamped
-    assert lib.paged_attn_default_partition(8, 0, 64, 16, 16, 0) == -1
+    # partials for 8192 workers x 2 slots x G heads of (D + 2) floats, then B + 1 prefix ints, 256-aligned
+    def expect(b, g, d):
+        n = 8192 * 2 * g * (d + 2) * 4 + (min(b, 4096) + 1) * 4
+        return -(-n // 256) * 256
+    assert lib.paged_attn_decode_workspace_bytes(64, 32, 32, 128, 131, 16, 0) == expect(64, 1, 128)
+    assert lib.paged_attn_decode_workspace_bytes(256, 64, 8, 128, 35, 64, 0) == expect(256, 8, 128)
+    assert lib.paged_attn_decode_workspace_bytes(9000, 8, 8, 64, 4, 16, 32) == expect(9000, 1, 64)
+    assert lib.paged_attn_decode_workspace_bytes(4, 8, 8, 64, 2, 16, 100) == 0  # partition not a multiple of 16
+    assert lib.paged_attn_decode_workspace_bytes(4, 12, 8, 64, 2, 16, 0) == 0   # heads not a multiple
+    assert lib.paged_attn_decode_workspace_bytes(0, 8, 8, 64, 2, 16, 0) == 0
+
+
+def test_worker_count_for_a_given_partition():
+    """With partition_tokens > 0 the worker count is a host computation: ceil(units of the
+    longest possible batch / units per worker), capped at 8192, rounded up to whole
+    workgroups of 4 waves."""
+    lib = _lib.load()
+    w = lib.paged_attn_decode_workers
+    assert w(4, 8, 8, 64, 16, 2, 0, 16) == 64            # 4 seqs x 8 heads x 2 units, 1 unit each
+    assert w(4, 8, 2, 64, 16, 2, 0, 16) == 8             # G = 4: 32-token units, 1 per segment
+    assert w(4, 8, 2, 64, 16, 2, 0, 48) == 4             # 2 units per worker -> 4, one workgroup
+    assert w(3, 8, 8, 64, 16, 3, 0, 32) == 36            # 3 x 8 x 3 = 72 units, 2 each
+    assert w(3, 8, 8, 64, 16, 3, 0, 48) == 24            # 3 each -> 24
+    assert w(3, 8, 8, 64, 16, 3, 0, 80) == 16            # 5 each -> 15, rounded up to 16
+    assert w(64, 32, 32, 128, 16, 131, 0, 512) == 8192   # capped
+    assert w(4, 8, 8, 96, 16, 2, 0, 16) == _lib.PKV_ERR_INVALID
+    assert w(0, 8, 8, 64, 16, 2, 0, 16) == _lib.PKV_ERR_INVALID
+    assert w(4, 8, 8, 64, 16, 2, 0, 24) == _lib.PKV_ERR_INVALID
 
 
 def test_write_and_copy_validation():
