@@ -156,7 +156,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1-5 (2 = Llama-2-7B batch 64)")
     ap.add_argument("--partition", type=int, default=0,
-                    help="tokens per attention worker (0 = one worker per resident wave, the default)")
+                    help="tokens per attention worker (0 = the library default worker count)")
     ap.add_argument("--flush", action="store_true", help="evict L2/MALL between steps (time by events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

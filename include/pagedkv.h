@@ -132,10 +132,11 @@ int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int num
  *                  [0, max_blocks_per_seq*block_size]; 0 gives a zero output.
  *   sm_scale       softmax scale (1/sqrt(head_dim) usually).
  *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale).
- *   partition_tokens 0 = as many workers as are resident on the device at
- *                  once; else a multiple of 16: each worker takes about this
- *                  many tokens of the longest possible batch (at most 8192
- *                  workers either way).
+ *   partition_tokens 0 = one worker per SIMD of the device (fp16 KV with one
+ *                  query head per KV head) or two (other shapes), within
+ *                  what the device can hold at once; else a multiple of 16:
+ *                  each worker takes about this many tokens of the longest
+ *                  possible batch (at most 8192 workers either way).
  *   workspace      device, >= paged_attn_decode_workspace_bytes(...) bytes
  *                  (fp32 partials and the unit prefix; contents on entry are
  *                  ignored). Calls that share a workspace must not overlap.

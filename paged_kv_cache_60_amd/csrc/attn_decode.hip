@@ -532,32 +532,50 @@ int unit_tokens_for(int group) { return group >= 4 ? 32 : kTile; }
 
 size_t dyn_lds_bytes(int B) { return (size_t)(B + 1 + kWaves * 64) * sizeof(int); }
 
-// Workgroups of a pass-1 kernel resident at once on the current device
-// (occupancy x compute units), cached per (kernel, LDS size, device); 0 on error.
-int resident_workgroups(KernFn fn, size_t dyn_lds) {
+// Workgroups of a pass-1 kernel that can be resident at once on the current
+// device (occupancy x compute units) and the compute-unit count, cached per
+// (kernel, LDS size, device); false on error.
+bool device_capacity(KernFn fn, size_t dyn_lds, int* resident_wgs, int* cus) {
   struct Entry {
     KernFn fn;
     size_t lds;
     int dev;
     int wgs;
+    int cus;
   };
   static std::mutex mu;
   static Entry cache[128];
   static int n_cache = 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < n_cache; ++i)
-    if (cache[i].fn == fn && cache[i].lds == dyn_lds && cache[i].dev == dev) return cache[i].wgs;
-  int per_cu = 0, cus = 0;
+    if (cache[i].fn == fn && cache[i].lds == dyn_lds && cache[i].dev == dev) {
+      *resident_wgs = cache[i].wgs;
+      *cus = cache[i].cus;
+      return true;
+    }
+  int per_cu = 0, n_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWaves * 64,
                                                    dyn_lds) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  const int wgs = per_cu * cus;
-  if (n_cache < 128) cache[n_cache++] = Entry{fn, dyn_lds, dev, wgs};
-  return wgs;
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  if (n_cache < 128) cache[n_cache++] = Entry{fn, dyn_lds, dev, per_cu * n_cu, n_cu};
+  *resident_wgs = per_cu * n_cu;
+  *cus = n_cu;
+  return per_cu > 0 && n_cu > 0;
 }
+
+// Default workers per SIMD. The SIMD issues for its resident waves in slot
+// order, so with several streaming waves per SIMD the low slots run ahead and
+// an equal share per wave leaves the last slots finishing long after the first
+// (measured on MI355X with 7 waves per SIMD: median finish 65 us for slot 0 vs
+// 182 us for slot 6). One wave per SIMD removes that skew and still keeps
+// enough loads in flight when a tile's arithmetic is light (fp16, one query
+// head per KV head: pass 1 of the Llama-2-7B batch-64 workload went from 201
+// to 185 us); heavier tiles (grouped heads, fp8 widening, matrix cores) need a
+// second wave per SIMD to overlap arithmetic with loads.
+int waves_per_simd(int group, bool fp8) { return group == 1 && !fp8 ? 1 : 2; }
 
 // Units of B sequences of the longest context the block table can hold.
 int64_t unit_upper_bound(int B, int max_blocks, int block_size, int unit) {
@@ -600,9 +618,11 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
     const int64_t per = (partition_tokens + p->unit - 1) / p->unit;
     W = (ub_all + per - 1) / per;
   } else {
-    const int wgs = resident_workgroups(p->fn, dyn_lds_bytes(B));
-    if (wgs <= 0) return PKV_ERR_HIP;
+    int wgs = 0, cus = 0;
+    if (!device_capacity(p->fn, dyn_lds_bytes(B), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
+    const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype == PKV_KV_FP8_E4M3) * 4 * cus;
+    if (W > by_simd) W = by_simd;
   }
   if (W > ub_all) W = ub_all;
   if (W > kMaxWorkers) W = kMaxWorkers;
