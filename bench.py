@@ -17,7 +17,9 @@ algorithmic bytes (K/V read by attention, queries, block tables, context
 lengths, output, plus the bytes paged_kv_write and paged_block_copy move) over
 the wall time of the timed steps. `roofline` is for the dominant kernel,
 attention pass 1: its algorithmic bytes per launch over its average launch
-duration measured with HIP events on the stream it runs on.
+duration, measured with HIP events on the stream it runs on around every
+EVENT_EVERY-th timed launch (an event in the stream idles the GPU for a few
+microseconds, so bracketing every launch would slow the steps being timed).
 `cpu_baseline` is the CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + KV tokens read/sec"
 PEAK_GBS = 8000.0  # MI355X HBM3E
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+EVENT_EVERY = 5  # timed steps per pass-1 event pair
 
 
 KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "device_common.hpp")
@@ -208,10 +211,10 @@ def main():
     torch.cuda.synchronize()
 
     def one_step(s, ev=None):
-        half, n_cow, n_upd = eng.host_step()
+        slot, n_cow, n_upd = eng.host_step()
         k, v, q = inputs[s]
         between = None if ev is None else (lambda i: ev[i].record())
-        eng.device_step(half, n_cow, n_upd, k, v, q, out, between=between)
+        eng.device_step(slot, n_cow, n_upd, k, v, q, out, between=between)
         return n_cow
 
     log(f"bench: warmup {args.warmup}")
@@ -222,8 +225,9 @@ def main():
     torch.cuda.synchronize()
 
     cow_total = 0
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
+    ev_steps = [i for i in range(args.steps) if i % EVENT_EVERY == EVENT_EVERY - 1] or [args.steps - 1]
+    ev_pairs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for i in ev_steps}
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
     log(f"bench: timing {args.steps} steps")
@@ -233,7 +237,7 @@ def main():
         s = args.warmup + i
         if flush_buf is not None:
             step_ev[i][0].record()
-        cow_total += one_step(s, ev_pairs[i])
+        cow_total += one_step(s, ev_pairs.get(i))
         if flush_buf is not None:
             step_ev[i][1].record()
             flush_buf.zero_()
@@ -243,10 +247,10 @@ def main():
     # context lengths of the timed steps: the final lengths minus the steps after each
     _, ctx_final = eng.host_tables()
     ctx_steps = [ctx_final - (args.steps - 1 - i) for i in range(args.steps)]
-    p1_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+    p1_ms = [a.elapsed_time(b) for a, b in ev_pairs.values()]
     step_ms = [a.elapsed_time(b) for a, b in step_ev] if flush_buf is not None else [wall / args.steps * 1e3]
-    p1_bytes = [attention_bytes(c, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, elem)[0]
-                for c in ctx_steps]
+    p1_bytes = [attention_bytes(ctx_steps[i], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                                elem)[0] for i in ev_pairs]
     tot_bytes = [attention_bytes(c, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, elem)[1]
                  + write_bytes(B, wl.num_kv_heads, wl.head_dim, elem) for c in ctx_steps]
     tot_bytes[-1] += cow_total * eng.block_bytes * 4  # read + write, K and V
@@ -285,6 +289,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
         "kv_tokens_per_s": round(kv_tokens / elapsed, 1),
         "attention_pass1_us": round(p1_avg_s * 1e6, 2),
+        "attention_pass1_launches_timed": len(p1_ms),
         "step_gpu_us": round(float(np.mean(step_ms)) * 1e3, 2),
         "roofline": {
             "bound": "hbm",

@@ -17,9 +17,12 @@ copy-on-write):
      and table entries, in one kernel;
   5. paged_attn_decode (pass 1 over equal shares of the KV, pass 2 for split segments).
 
-Pinned metadata buffers alternate between two halves so the host can prepare
-step k+1 while step k's kernels may still be queued; an event per half keeps
-the host from overwriting a half before the kernels that read it have run.
+Pinned metadata buffers form a ring of RING slots, so the host can prepare
+the next steps while earlier steps' kernels are still queued. Before the host
+overwrites a slot it waits for an event recorded after the step that last
+read it. An event in the stream idles the GPU for a few microseconds (about
+5 us per event measured on MI355X), so one event covers EVENT_EVERY steps and
+is recorded after the step's last kernel, never between its kernels.
 """
 from __future__ import annotations
 
@@ -31,6 +34,8 @@ from .block_manager import BlockManager
 
 F16_NAN_BITS = 0x7E00
 FP8_NAN_BITS = 0x7F
+RING = 8          # pinned metadata slots
+EVENT_EVERY = 4   # steps covered by one completion event; RING is a multiple of it
 
 
 class PagedKVEngine:
@@ -108,6 +113,7 @@ class PagedKVEngine:
         """Set up a decode batch: device-resident block tables (uploaded once
         here), the per-step metadata buffers (two pinned halves on the host,
         one set on the device) and the attention workspace."""
+        torch.cuda.synchronize(self.device)  # queued kernels may still read the previous buffers
         B = len(batch_seqs)
         self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
         self.max_blocks = int(max_blocks)
@@ -119,12 +125,14 @@ class PagedKVEngine:
         o_upd = o_cow + 8 * B
         total = (o_upd + 12 * B + 255) // 256 * 256
         self._layout = (o_slots, o_ctx, o_cow, o_upd)
-        self._pinned = [torch.empty(max(total, 256), dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self._pinned = [torch.empty(max(total, 256), dtype=torch.uint8, pin_memory=True) for _ in range(RING)]
         self._views = []
         for t in self._pinned:
             self._views.append((t[o_slots:o_ctx].view(torch.int64), t[o_ctx:o_cow].view(torch.int32),
                                 t[o_cow:o_upd].view(torch.int32), t[o_upd:o_upd + 12 * B].view(torch.int32)))
-        self._events = [None, None]
+        self._events = [None] * (RING // EVENT_EVERY)
+        self._host_steps = 0
+        self._device_steps = 0
         self.slots_dev = torch.empty(B, dtype=torch.int64, device=self.device)
         self.ctx_dev = torch.empty(B, dtype=torch.int32, device=self.device)
         self.cow_dev = torch.empty((B, 2), dtype=torch.int32, device=self.device)
@@ -133,47 +141,53 @@ class PagedKVEngine:
         self.ctx_dev.copy_(torch.from_numpy(ctx))
         wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
-        self._parity = 0
         torch.cuda.synchronize(self.device)
 
     def host_step(self):
-        """Step part 1: host bookkeeping into the next pinned half.
-        Returns (half, n_cow, n_updates)."""
-        half = self._parity
-        self._parity ^= 1
-        ev = self._events[half]
-        if ev is not None:
+        """Step part 1: host bookkeeping into the next pinned slot.
+        Returns (slot, n_cow, n_updates)."""
+        k = self._host_steps
+        self._host_steps += 1
+        slot = k % RING
+        if k >= RING:
+            # the event of the group holding step k - RING, the slot's last reader
+            ev = self._events[((k - RING) // EVENT_EVERY) % len(self._events)]
             ev.synchronize()
-        slots, ctx, cow, upd = (v.numpy() for v in self._views[half])
+        slots, ctx, cow, upd = (v.numpy() for v in self._views[slot])
         n_cow, n_upd = self.bm.decode_step(self.batch, slots, cow, upd, ctx)
-        return half, n_cow, n_upd
+        return slot, n_cow, n_upd
 
-    def upload(self, half, n_cow, n_upd):
-        """Step part 2 on its own: one small kernel reads the pinned half and
+    def _end_device_step(self):
+        """Called after a step's last kernel: every EVENT_EVERY steps, record the
+        event that releases the pinned slots of that group of steps."""
+        k = self._device_steps
+        self._device_steps += 1
+        if k % EVENT_EVERY == EVENT_EVERY - 1:
+            ev = torch.cuda.Event()
+            ev.record()
+            self._events[(k // EVENT_EVERY) % len(self._events)] = ev
+
+    def upload(self, slot, n_cow, n_upd):
+        """Step part 2 on its own: one small kernel reads the pinned slot and
         updates the device slot mapping, context lengths, copy pairs and table
         entries (paged_step_metadata). device_step() does this inside the write
-        kernel instead; this form serves callers that write tokens separately."""
-        slots, ctx, cow, upd = self._views[half]
+        kernel instead; this form serves callers that write tokens separately
+        (it ends the step for the slot ring)."""
+        slots, ctx, cow, upd = self._views[slot]
         ops.paged_step_metadata(slots, self.slots_dev, ctx, self.ctx_dev, len(self.batch), cow,
                                 self.cow_dev, n_cow, upd, n_upd, self.tables_dev)
-        self._mark_read(half)
+        self._end_device_step()
 
-    def _mark_read(self, half):
-        ev = torch.cuda.Event()
-        ev.record()
-        self._events[half] = ev
-
-    def device_step(self, half, n_cow, n_upd, k_new, v_new, q, out, passes=3, between=None):
+    def device_step(self, slot, n_cow, n_upd, k_new, v_new, q, out, passes=3, between=None):
         """Step parts 2-5 on the current stream: copy-on-write copies (pairs read
-        from the pinned half), then one kernel that writes the new tokens and
+        from the pinned slot), then one kernel that writes the new tokens and
         applies the step's metadata, then attention. `between` (optional) is
         called after the write, before attention, and again between the passes."""
-        slots, ctx, cow, upd = self._views[half]
+        slots, ctx, cow, upd = self._views[slot]
         if n_cow:
             ops.paged_block_copy(self.k_cache, self.v_cache, cow[:2 * n_cow].view(n_cow, 2))
         ops.paged_kv_write_step(k_new, v_new, self.k_cache, self.v_cache, slots, ctx, self.ctx_dev, upd,
                                 n_upd, self.tables_dev, self.kv_dtype, self.k_inv_scale, self.v_inv_scale)
-        self._mark_read(half)
         if between is None:
             self.attend(q, out, passes)
         else:
@@ -181,6 +195,7 @@ class PagedKVEngine:
             self.attend(q, out, 1)
             between(1)
             self.attend(q, out, 2)
+        self._end_device_step()
 
     def attend(self, q, out, passes=3):
         ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
@@ -189,8 +204,8 @@ class PagedKVEngine:
 
     def decode_step(self, k_new, v_new, q, out):
         """Full decode step: append one token per batch sequence, write it, attend."""
-        half, n_cow, n_upd = self.host_step()
-        self.device_step(half, n_cow, n_upd, k_new, v_new, q, out)
+        slot, n_cow, n_upd = self.host_step()
+        self.device_step(slot, n_cow, n_upd, k_new, v_new, q, out)
         return n_cow
 
     def host_tables(self):
