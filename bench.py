@@ -15,7 +15,10 @@ head_dim 128, block size 16, fp16 KV, context lengths uniform in [128, 2048].
 Printed: one JSON line. `value` is the whole-step throughput in GB/s of
 algorithmic bytes (K/V read by attention, queries, block tables, context
 lengths, output, plus the bytes paged_kv_write and paged_block_copy move) over
-the wall time of the timed steps. `roofline` is for the dominant kernel,
+the wall time of the timed steps. K/V blocks that several sequences share
+count once (at the most rows any sequence reads from them): that is the HBM
+lower bound; `value_logical_gbs` counts every sequence's reads. Without shared
+blocks the two are equal. `roofline` is for the dominant kernel,
 attention pass 1: its algorithmic bytes per launch over its average launch
 duration, measured with HIP events on the stream it runs on around every
 EVENT_EVERY-th timed launch (an event in the stream idles the GPU for a few
@@ -56,7 +59,8 @@ def kernel_source_hash() -> str:
 
 
 def attention_bytes(ctx, hq, hkv, d, bs, elem):
-    """Algorithmic bytes of one decode-attention call: (partition pass, total)."""
+    """Algorithmic bytes of one decode-attention call: (pass 1, total), counting
+    every sequence's K/V reads (logical bytes)."""
     ctx = np.asarray(ctx, dtype=np.int64)
     B = len(ctx)
     kv = int((ctx * hkv * d * 2 * elem).sum())
@@ -65,6 +69,21 @@ def attention_bytes(ctx, hq, hkv, d, bs, elem):
     out = B * hq * d * 2
     p1 = kv + q_in + tables + 4 * B
     return p1, p1 + out
+
+
+def unique_kv_bytes(tables, ctx, hkv, d, bs, elem):
+    """K/V bytes of one call counting each physical block once, at the largest
+    number of its rows any sequence reads: the HBM lower bound when sequences
+    share blocks (a common prefix, the prompt of a beam group)."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    nblk = (ctx + bs - 1) // bs
+    idx = np.arange(tables.shape[1], dtype=np.int64)
+    live = idx[None, :] < nblk[:, None]
+    used = np.clip(ctx[:, None] - idx[None, :] * bs, 0, bs)
+    phys = tables[live].astype(np.int64)
+    rows = np.zeros(int(phys.max()) + 1 if phys.size else 1, dtype=np.int64)
+    np.maximum.at(rows, phys, used[live])
+    return int(rows.sum()) * hkv * d * 2 * elem
 
 
 def write_bytes(T, hkv, d, elem):
@@ -245,15 +264,28 @@ def main():
     wall = time.perf_counter() - t0
 
     # context lengths of the timed steps: the final lengths minus the steps after each
-    _, ctx_final = eng.host_tables()
+    tab_final, ctx_final = eng.host_tables()
     ctx_steps = [ctx_final - (args.steps - 1 - i) for i in range(args.steps)]
     p1_ms = [a.elapsed_time(b) for a, b in ev_pairs.values()]
     step_ms = [a.elapsed_time(b) for a, b in step_ev] if flush_buf is not None else [wall / args.steps * 1e3]
-    p1_bytes = [attention_bytes(ctx_steps[i], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-                                elem)[0] for i in ev_pairs]
-    tot_bytes = [attention_bytes(c, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, elem)[1]
-                 + write_bytes(B, wl.num_kv_heads, wl.head_dim, elem) for c in ctx_steps]
-    tot_bytes[-1] += cow_total * eng.block_bytes * 4  # read + write, K and V
+    hq, hkv, d, bs = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+
+    def step_bytes(c, unique):
+        """(pass-1 bytes, whole-step bytes) of a step with context lengths c."""
+        p1, tot = attention_bytes(c, hq, hkv, d, bs, elem)
+        if unique:
+            delta = int((np.asarray(c, dtype=np.int64) * hkv * d * 2 * elem).sum()) - \
+                unique_kv_bytes(tab_final, c, hkv, d, bs, elem)
+            p1, tot = p1 - delta, tot - delta
+        return p1, tot + write_bytes(B, hkv, d, elem)
+
+    uniq = [step_bytes(c, True) for c in ctx_steps]
+    logi = [step_bytes(c, False) for c in ctx_steps]
+    cow_bytes = cow_total * eng.block_bytes * 4  # read + write, K and V
+    tot_bytes = sum(t for _, t in uniq) + cow_bytes
+    tot_bytes_logical = sum(t for _, t in logi) + cow_bytes
+    p1_bytes = [uniq[i][0] for i in ev_pairs]
+    p1_bytes_logical = [logi[i][0] for i in ev_pairs]
     kv_tokens = sum(int(c.sum()) for c in ctx_steps)
 
     if args.flush:
@@ -261,9 +293,10 @@ def main():
     else:
         elapsed = wall
     ms_per_step = elapsed / args.steps * 1e3
-    value = sum(tot_bytes) / elapsed / 1e9
+    value = tot_bytes / elapsed / 1e9
     p1_avg_s = sum(p1_ms) / len(p1_ms) / 1e3
     achieved = (sum(p1_bytes) / len(p1_bytes)) / p1_avg_s / 1e9
+    achieved_logical = (sum(p1_bytes_logical) / len(p1_bytes_logical)) / p1_avg_s / 1e9
     traffic = load_counters(wl.name)
 
     result = {
@@ -287,8 +320,10 @@ def main():
             "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
         },
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "value_logical_gbs": round(tot_bytes_logical / elapsed / 1e9, 2),
         "kv_tokens_per_s": round(kv_tokens / elapsed, 1),
         "attention_pass1_us": round(p1_avg_s * 1e6, 2),
+        "attention_pass1_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(p1_ms, [10, 50, 90])],
         "attention_pass1_launches_timed": len(p1_ms),
         "step_gpu_us": round(float(np.mean(step_ms)) * 1e3, 2),
         "roofline": {
@@ -299,6 +334,7 @@ def main():
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": kernel,
+            "achieved_logical": round(achieved_logical, 2),
         },
     }
     if not args.no_cpu_baseline:

@@ -183,11 +183,11 @@ class PagedKVEngine:
         from the pinned slot), then one kernel that writes the new tokens and
         applies the step's metadata, then attention. `between` (optional) is
         called after the write, before attention, and again between the passes."""
-        slots, ctx, cow, upd = self._views[slot]
         if n_cow:
+            cow = self._views[slot][2]
             ops.paged_block_copy(self.k_cache, self.v_cache, cow[:2 * n_cow].view(n_cow, 2))
-        ops.paged_kv_write_step(k_new, v_new, self.k_cache, self.v_cache, slots, ctx, self.ctx_dev, upd,
-                                n_upd, self.tables_dev, self.kv_dtype, self.k_inv_scale, self.v_inv_scale)
+        self.write_step(slot, n_upd, k_new, v_new)
+        self.last_step = (slot, n_cow, n_upd)
         if between is None:
             self.attend(q, out, passes)
         else:
@@ -196,6 +196,14 @@ class PagedKVEngine:
             between(1)
             self.attend(q, out, 2)
         self._end_device_step()
+
+    def write_step(self, slot, n_upd, k_new, v_new):
+        """The write kernel of a step: new K/V rows to their slots, plus the
+        step's context lengths and block-table entries, all read from pinned
+        slot `slot`. Applying it twice is harmless (same values, same places)."""
+        slots, ctx, _, upd = self._views[slot]
+        ops.paged_kv_write_step(k_new, v_new, self.k_cache, self.v_cache, slots, ctx, self.ctx_dev, upd,
+                                n_upd, self.tables_dev, self.kv_dtype, self.k_inv_scale, self.v_inv_scale)
 
     def attend(self, q, out, passes=3):
         ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
