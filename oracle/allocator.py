@@ -15,6 +15,12 @@ Sources
     allocates a new block, copies the shared block into it, writes the new one
     and decrements the original's count.
   * "From OOM to Smooth Inference", §6.1: forked beams copy only the last block.
+  * "Where Did the VRAM Go (KV cache tutorial)", §4.2-4.4: prefix caching. Each
+    block gets a key built from its own token ids and everything before it; a
+    new request looks its blocks up and maps hits straight into its block
+    table, so only the missed part is prefilled; shared blocks carry reference
+    counts and a block whose count reaches zero waits for reuse; eviction is
+    least-recently-used; matching is exact at token level.
 
 Readings taken where the pages are silent or garbled (each is tested):
   R1  Block ids are 0-based; the initial free order is caller-supplied
@@ -39,6 +45,27 @@ Readings taken where the pages are silent or garbled (each is tested):
   R8  free() walks the table in order; every block whose count reaches zero is
       appended to the back of the free queue.
   R9  A failing call changes no state: every check runs before any mutation.
+  R10 Prefix cache. Only full blocks are cached. A block's key is (parent
+      block, its bs token ids), parent = the previous block of the same prompt
+      or -1: the chain "everything before it" is carried by the parent block,
+      whose own key carries its parent, so a match is exact (no hash
+      collisions can alias two contents). allocate_prompt(seq, tokens) maps
+      the longest run of leading full blocks found in the cache, stops at the
+      first miss, takes fresh blocks for the rest and registers every fresh
+      full block under its parent. The partial last block is never cached.
+  R11 A cached block whose count reaches zero keeps its key and joins the
+      evictable list instead of the free queue; a later hit revives it. Fresh
+      blocks come from the free queue first; when it is empty the oldest
+      evictable block is evicted (its key dropped) and reused. The capacity
+      check before any mutation counts free + evictable blocks, minus the
+      evictable blocks the same call revives.
+  R12 free() releases in table order; uncached blocks reaching zero go to the
+      back of the free queue as before (R8), cached ones join the evictable
+      list deepest block first. Since every sequence holding a block also
+      holds its parent, a block never reaches zero after its parent, so the
+      evictable list always holds a block's cached descendants before it and
+      eviction removes children before parents (no key can name a parent
+      block that was reused for other content).
 """
 from __future__ import annotations
 
@@ -86,16 +113,35 @@ class BlockAllocatorModel:
         self.tables: dict[int, list[int]] = {}
         self.counts: dict[int, int] = {}
         self.ref = [0] * num_blocks
+        # prefix cache (R10-R12): key -> block, block -> key, evictable blocks oldest first
+        self.cache: dict[tuple, int] = {}
+        self.key_of: dict[int, tuple] = {}
+        self.evictable: deque = deque()
+        self.prefix_query_tokens = 0
+        self.prefix_hit_tokens = 0
 
     # ----------------------------------------------------------- helpers
     def _needed(self, tokens: int) -> int:
         # ceil(tokens / block_size), "From OOM to Smooth Inference", §2.3
         return (tokens + self.bs - 1) // self.bs
 
+    def _capacity(self) -> int:
+        return len(self.free) + len(self.evictable)
+
     def _pop(self, count: int) -> list[int]:
-        if len(self.free) < count:
-            raise AllocError(ERR_OOM, f"need {count} blocks, {len(self.free)} free")
-        return [self.free.popleft() for _ in range(count)]
+        """count fresh blocks: the free queue first, then the oldest evictable
+        cached blocks, whose keys are dropped (R11)."""
+        if self._capacity() < count:
+            raise AllocError(ERR_OOM, f"need {count} blocks, {self._capacity()} available")
+        out = []
+        for _ in range(count):
+            if self.free:
+                out.append(self.free.popleft())
+            else:
+                b = self.evictable.popleft()
+                del self.cache[self.key_of.pop(b)]
+                out.append(b)
+        return out
 
     def _require(self, seq: int):
         if seq not in self.tables:
@@ -130,8 +176,8 @@ class BlockAllocatorModel:
         cow = bool(table) and count % self.bs != 0 and self.ref[table[-1]] > 1
         grow = self._needed(count + n) - len(table)
         need = grow + (1 if cow else 0)
-        if len(self.free) < need:
-            raise AllocError(ERR_OOM, f"need {need} blocks, {len(self.free)} free")
+        if self._capacity() < need:
+            raise AllocError(ERR_OOM, f"need {need} blocks, {self._capacity()} available")
         cow_src = cow_dst = -1
         if cow:
             cow_src = table[-1]
@@ -171,14 +217,63 @@ class BlockAllocatorModel:
         self.counts[dst] = min(num_blocks * self.bs, self.counts[src])
 
     def free_seq(self, seq: int) -> None:
-        """Release seq's blocks in table order (R8)."""
+        """Release seq's blocks in table order (R8); cached blocks reaching zero
+        join the evictable list deepest first (R12)."""
         self._require(seq)
         table = self.tables.pop(seq)
         del self.counts[seq]
+        cached = []
         for b in table:
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                self.free.append(b)
+                if b in self.key_of:
+                    cached.append(b)
+                else:
+                    self.free.append(b)
+        self.evictable.extend(reversed(cached))
+
+    def allocate_prompt(self, seq: int, tokens) -> tuple[int, list[int]]:
+        """New sequence for a prompt of token ids, reusing cached blocks (R10).
+
+        Returns (cached tokens, slots of the tokens after them): the caller
+        writes K/V only for those."""
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        if seq in self.tables:
+            raise AllocError(ERR_EXISTS, f"sequence {seq} exists")
+        bs = self.bs
+        matched, parent = [], -1
+        for i in range(n // bs):
+            key = (parent, tuple(tokens[i * bs:(i + 1) * bs]))
+            b = self.cache.get(key)
+            if b is None:
+                break
+            matched.append(b)
+            parent = b
+        fresh_needed = self._needed(n) - len(matched)
+        revived = sum(1 for b in matched if self.ref[b] == 0)
+        if self._capacity() - revived < fresh_needed:
+            raise AllocError(ERR_OOM, f"need {fresh_needed} blocks, {self._capacity() - revived} available")
+        for b in matched:
+            if self.ref[b] == 0:
+                self.evictable.remove(b)
+            self.ref[b] += 1
+        fresh = self._pop(fresh_needed)
+        for b in fresh:
+            self.ref[b] += 1
+        table = matched + fresh
+        for i in range(len(matched), n // bs):
+            key = (parent, tuple(tokens[i * bs:(i + 1) * bs]))
+            b = table[i]
+            self.cache[key] = b
+            self.key_of[b] = key
+            parent = b
+        self.tables[seq] = table
+        self.counts[seq] = n
+        n_cached = len(matched) * bs
+        self.prefix_query_tokens += n
+        self.prefix_hit_tokens += n_cached
+        return n_cached, [self._slot(table, p) for p in range(n_cached, n)]
 
     # ----------------------------------------------------------- queries
     def slots(self, seq: int, start: int, n: int) -> list[int]:
@@ -204,12 +299,25 @@ class BlockAllocatorModel:
     def free_list(self) -> list[int]:
         return list(self.free)
 
+    def evictable_list(self) -> list[int]:
+        """Cached blocks with no reference, oldest (next to evict) first."""
+        return list(self.evictable)
+
+    def cache_entry(self, block: int):
+        """(parent block, token ids) if the block is cached, else None."""
+        if block < 0 or block >= self.num_blocks:
+            raise AllocError(ERR_INVALID, "block id out of range")
+        key = self.key_of.get(block)
+        return None if key is None else (key[0], list(key[1]))
+
     def available_blocks(self) -> int:
-        return len(self.free)
+        """Blocks a new allocation can take: free plus evictable cached blocks."""
+        return self._capacity()
 
     def utilization(self) -> float:
-        """(total - free) / total: the second page's definition."""
-        return (self.num_blocks - len(self.free)) / self.num_blocks
+        """Blocks referenced by live sequences / total: the second page's
+        (total - free) / total, with evictable cached blocks counted as free."""
+        return (self.num_blocks - self._capacity()) / self.num_blocks
 
     def stats(self) -> dict:
         """Free blocks, live sequences, used blocks, physical utilisation,
@@ -224,7 +332,7 @@ class BlockAllocatorModel:
             for i, b in enumerate(table):
                 f = max(0, min(self.bs, c - i * self.bs))
                 filled[b] = max(filled.get(b, 0), f)
-        used = self.num_blocks - len(self.free)
+        used = self.num_blocks - self._capacity()
         total_filled = sum(filled.values())
         return {
             "free_blocks": len(self.free),
@@ -233,6 +341,10 @@ class BlockAllocatorModel:
             "utilization": used / self.num_blocks,
             "filled_slots": total_filled,
             "slot_utilization": (total_filled / (used * self.bs)) if used else 0.0,
+            "evictable_blocks": len(self.evictable),
+            "cached_blocks": len(self.key_of),
+            "prefix_query_tokens": self.prefix_query_tokens,
+            "prefix_hit_tokens": self.prefix_hit_tokens,
         }
 
     def state(self) -> dict:
@@ -242,4 +354,6 @@ class BlockAllocatorModel:
             "tables": {s: list(t) for s, t in sorted(self.tables.items())},
             "counts": dict(sorted(self.counts.items())),
             "ref": list(self.ref),
+            "evictable": list(self.evictable),
+            "cache": {b: (k[0], list(k[1])) for b, k in sorted(self.key_of.items())},
         }

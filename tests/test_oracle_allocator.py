@@ -147,10 +147,24 @@ def check_invariants(m: BlockAllocatorModel):
             refs[b] += 1
     assert refs == m.ref
     free = m.free_list()
+    evictable = m.evictable_list()
     assert len(set(free)) == len(free)
-    for b in free:
+    assert len(set(evictable)) == len(evictable)
+    for b in free + evictable:
         assert refs[b] == 0
-    assert set(free) | {b for b in range(m.num_blocks) if refs[b] > 0} == set(range(m.num_blocks))
+    live = {b for b in range(m.num_blocks) if refs[b] > 0}
+    assert not set(free) & set(evictable)
+    assert set(free) | set(evictable) | live == set(range(m.num_blocks))
+    # prefix cache: evictable blocks are cached, free ones are not; the chain of parents is closed
+    for b in evictable:
+        assert m.cache_entry(b) is not None
+    for b in free:
+        assert m.cache_entry(b) is None
+    for b in range(m.num_blocks):
+        e = m.cache_entry(b)
+        if e is not None:
+            assert e[0] == -1 or m.cache_entry(e[0]) is not None
+            assert len(e[1]) == m.bs
 
 
 op_strategy = st.tuples(
