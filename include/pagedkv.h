@@ -198,20 +198,36 @@ int paged_step_metadata(const int64_t* slots_src, int64_t* slots_dst, const int3
  * Host block manager
  * A FIFO pool of physical blocks, per-sequence block tables and token
  * counts, per-block reference counts ([OOM] §2.3; [ENGINE] §3;
- * [VLLM] §3.2-3.3). Host memory only; not thread-safe per handle. Output
- * arrays are copies into caller buffers. A failing call changes no state.
+ * [VLLM] §3.2-3.3), and a prefix cache of full blocks ([VRAM] §4.2-4.4).
+ * Host memory only; not thread-safe per handle. Output arrays are copies
+ * into caller buffers. A failing call changes no state.
+ *
+ * Prefix cache. A full block written through pkv_bm_allocate_prompt is keyed
+ * by (parent block, its block_size token ids): the parent is the previous
+ * block of the same prompt (-1 for the first), and its own key carries its
+ * parent, so a key stands for the block's tokens and everything before them
+ * and a match is exact (hashes only speed up the lookup). A cached block
+ * whose refcount reaches 0 keeps its key on an evictable list until it is
+ * reused by a hit or evicted. Fresh blocks come from the free queue first,
+ * then from the oldest evictable block (its key is dropped). Sequences made
+ * by the other calls are never cached; without pkv_bm_allocate_prompt the
+ * manager behaves exactly as a plain FIFO pool.
  * ==================================================================== */
 
 typedef struct pkv_bm pkv_bm;
 
 typedef struct {
   int32_t total_blocks;
-  int32_t free_blocks;
-  int32_t used_blocks;    /* total - free                                    */
+  int32_t free_blocks;    /* in the free queue                               */
+  int32_t used_blocks;    /* referenced by live sequences: total - free - evictable */
   int32_t live_seqs;
   int64_t filled_slots;   /* token slots holding data, shared blocks once    */
   double utilization;     /* used / total ([ENGINE] §3 utilisation)          */
   double slot_utilization;/* filled_slots / (used * block_size), 0 if unused */
+  int32_t evictable_blocks;    /* cached, refcount 0                         */
+  int32_t cached_blocks;       /* holding a prefix-cache key                 */
+  int64_t prefix_query_tokens; /* tokens passed to pkv_bm_allocate_prompt    */
+  int64_t prefix_hit_tokens;   /* of those, found in the cache               */
 } pkv_bm_stats_t;
 
 /* New manager over blocks 0..num_blocks-1. free_order (host, may be NULL =
@@ -223,6 +239,20 @@ void pkv_bm_destroy(pkv_bm* bm);
  * the front of the pool. slots_out (host, may be NULL) receives the n slots.
  * EXISTS if seq is live, OOM if the pool is short. [ENGINE] §3, [OOM] §2.3. */
 int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out);
+
+/* New sequence for a prompt of n_tokens token ids (host), reusing cached
+ * blocks ([VRAM] §4.2: a request maps the blocks it finds into its table and
+ * prefills only the rest). The longest run of leading full blocks whose keys
+ * are cached is mapped (refcount +1, evictable ones revived); the first miss
+ * ends the match; the remaining blocks are fresh and every fresh full block
+ * is registered under its parent. The partial last block is never cached.
+ * *n_cached = tokens covered by the mapped blocks (a multiple of block_size);
+ * slots_out (host, room for n_tokens entries) receives the slots of tokens
+ * n_cached .. n_tokens-1, the ones whose K/V the caller must write.
+ * EXISTS if seq is live; OOM (nothing changed) if the free queue plus the
+ * evictable blocks not revived by this call are too few. */
+int pkv_bm_allocate_prompt(pkv_bm* bm, int64_t seq, const int32_t* tokens, int n_tokens,
+                           int* n_cached, int64_t* slots_out);
 
 /* Append n_tokens (>= 0) to seq. If the first new position falls inside the
  * current last block and that block is shared (refcount > 1), a fresh block
@@ -258,8 +288,11 @@ int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
  * table. [ENGINE] §3 share_prefix. */
 int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst);
 
-/* Release seq: refcount -1 on each block in table order; blocks reaching 0
- * go to the back of the pool. [OOM] §2.3, [ENGINE] §3, [VLLM] §3.2. */
+/* Release seq: refcount -1 on each block in table order; uncached blocks
+ * reaching 0 go to the back of the pool, cached ones to the back of the
+ * evictable list, deepest block first (so eviction, oldest first, always
+ * takes a block's cached descendants before the block). [OOM] §2.3,
+ * [ENGINE] §3, [VLLM] §3.2, [VRAM] §4.3-4.4. */
 int pkv_bm_free(pkv_bm* bm, int64_t seq);
 
 /* Queries. Arrays are host buffers of `cap` entries; *n gets the count. */
@@ -268,6 +301,12 @@ int pkv_bm_block_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int
 int pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq, int* n);
 int pkv_bm_refcount(const pkv_bm* bm, int32_t block, int* rc);
 int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n); /* FIFO order */
+/* Evictable cached blocks, oldest (next to evict) first. */
+int pkv_bm_evictable_list(const pkv_bm* bm, int32_t* out, int cap, int* n);
+/* *cached = 1 and (*parent, tokens_out[block_size]) = the block's key if it is
+ * cached, else *cached = 0. tokens_out (host) needs block_size entries. */
+int pkv_bm_cache_entry(const pkv_bm* bm, int32_t block, int* cached, int32_t* parent,
+                       int32_t* tokens_out);
 int pkv_bm_num_free(const pkv_bm* bm);
 int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out);
 

@@ -36,6 +36,7 @@ def empty_cache(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype):
 class RoundResult:
     slots: list
     cow_pairs: list
+    prompts: list = field(default_factory=list)  # (op, cached tokens, slots of the other tokens)
 
 
 @dataclass
@@ -50,7 +51,7 @@ class OracleRun:
 
 
 def apply_ops(alloc: BlockAllocatorModel, ops) -> RoundResult:
-    slots, pairs = [], []
+    slots, pairs, prompts = [], [], []
     for op in ops:
         if op.kind == "allocate":
             slots += alloc.allocate(op.seq, op.n)
@@ -65,9 +66,14 @@ def apply_ops(alloc: BlockAllocatorModel, ops) -> RoundResult:
             alloc.fork(op.src, op.seq)
         elif op.kind == "free":
             alloc.free_seq(op.seq)
+        elif op.kind == "prompt":
+            # prefix cache ("Where Did the VRAM Go (KV cache tutorial)", §4.2): only
+            # the tokens after the cached blocks are written
+            c, sl = alloc.allocate_prompt(op.seq, op.tokens)
+            prompts.append((op, c, list(sl)))
         else:
             raise ValueError(op.kind)
-    return RoundResult(slots, pairs)
+    return RoundResult(slots, pairs, prompts)
 
 
 def run_round(wl, alloc, k_cache, v_cache, ops) -> RoundResult:
@@ -76,6 +82,9 @@ def run_round(wl, alloc, k_cache, v_cache, ops) -> RoundResult:
     K, V = wl.round_kv(ops)
     scatter(k_cache, v_cache, K, V, res.slots, wl.block_size, wl.kv_dtype,
             wl.k_inv_scale, wl.v_inv_scale)
+    for op, c, sl in res.prompts:
+        K, V = wl.prompt_kv(op, c)
+        scatter(k_cache, v_cache, K, V, sl, wl.block_size, wl.kv_dtype, wl.k_inv_scale, wl.v_inv_scale)
     return res
 
 

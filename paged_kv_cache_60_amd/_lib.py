@@ -41,6 +41,10 @@ class PkvStats(ctypes.Structure):
         ("filled_slots", ctypes.c_int64),
         ("utilization", ctypes.c_double),
         ("slot_utilization", ctypes.c_double),
+        ("evictable_blocks", ctypes.c_int32),
+        ("cached_blocks", ctypes.c_int32),
+        ("prefix_query_tokens", ctypes.c_int64),
+        ("prefix_hit_tokens", ctypes.c_int64),
     ]
 
 
@@ -66,6 +70,7 @@ SIGNATURES = {
     "pkv_bm_create": (_c_int, [_c_int, _c_int, _p_i32, ctypes.POINTER(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_allocate": (_c_int, [_vp, _c_i64, _c_int, _p_i64]),
+    "pkv_bm_allocate_prompt": (_c_int, [_vp, _c_i64, _p_i32, _c_int, _p_int, _p_i64]),
     "pkv_bm_append": (_c_int, [_vp, _c_i64, _c_int, _p_i64, _p_i32, _p_i32]),
     "pkv_bm_append_batch": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int]),
     "pkv_bm_decode_step": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int, _p_i32, _p_int, _p_i32]),
@@ -77,6 +82,8 @@ SIGNATURES = {
     "pkv_bm_num_tokens": (_c_int, [_vp, _c_i64, _p_int]),
     "pkv_bm_refcount": (_c_int, [_vp, ctypes.c_int32, _p_int]),
     "pkv_bm_free_list": (_c_int, [_vp, _p_i32, _c_int, _p_int]),
+    "pkv_bm_evictable_list": (_c_int, [_vp, _p_i32, _c_int, _p_int]),
+    "pkv_bm_cache_entry": (_c_int, [_vp, ctypes.c_int32, _p_int, _p_i32, _p_i32]),
     "pkv_bm_num_free": (_c_int, [_vp]),
     "pkv_bm_stats": (_c_int, [_vp, ctypes.POINTER(PkvStats)]),
     "pkv_bm_export": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_i32]),

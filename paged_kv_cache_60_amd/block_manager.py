@@ -26,7 +26,8 @@ def _i64p(a):
 
 
 class BlockManager:
-    """FIFO pool of physical blocks, block tables, refcounts (host, C++)."""
+    """FIFO pool of physical blocks, block tables, refcounts and a prefix cache of
+    full blocks (host, C++)."""
 
     def __init__(self, num_blocks: int, block_size: int, free_order=None):
         lib = _lib.load()
@@ -67,6 +68,17 @@ class BlockManager:
         check(self._lib.pkv_bm_allocate(self._h, seq, num_tokens, _i64p(slots) if num_tokens > 0 else None),
               "pkv_bm_allocate")
         return slots
+
+    def allocate_prompt(self, seq: int, tokens) -> tuple:
+        """New sequence for a prompt of token ids, reusing cached blocks.
+        Returns (cached tokens, slots of the remaining tokens as an int64 array)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        n = len(toks)
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        c = ctypes.c_int(0)
+        check(self._lib.pkv_bm_allocate_prompt(self._h, seq, _i32p(toks) if n else None, n, ctypes.byref(c),
+                                               _i64p(slots) if n else None), "pkv_bm_allocate_prompt")
+        return c.value, slots[:n - c.value]
 
     def append(self, seq: int, n: int = 1) -> AppendResult:
         slots = np.empty(max(n, 0), dtype=np.int64)
@@ -134,8 +146,27 @@ class BlockManager:
               "pkv_bm_free_list")
         return out[:n.value].tolist()
 
+    def evictable_list(self) -> list:
+        """Cached blocks with no reference, oldest (next to evict) first."""
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_evictable_list(self._h, _i32p(out), self.num_blocks, ctypes.byref(n)),
+              "pkv_bm_evictable_list")
+        return out[:n.value].tolist()
+
+    def cache_entry(self, block: int):
+        """(parent block, token ids) if the block is cached, else None."""
+        cached = ctypes.c_int(0)
+        parent = ctypes.c_int32(-1)
+        toks = np.empty(self.block_size, dtype=np.int32)
+        check(self._lib.pkv_bm_cache_entry(self._h, block, ctypes.byref(cached), ctypes.byref(parent),
+                                           _i32p(toks)), "pkv_bm_cache_entry")
+        return (parent.value, toks.tolist()) if cached.value else None
+
     def available_blocks(self) -> int:
-        return self._lib.pkv_bm_num_free(self._h)
+        """Blocks a new allocation can take: the free queue plus evictable cached blocks."""
+        st = self.stats()
+        return st["free_blocks"] + st["evictable_blocks"]
 
     def stats(self) -> dict:
         s = _lib.PkvStats()
@@ -147,6 +178,10 @@ class BlockManager:
             "utilization": s.utilization,
             "filled_slots": s.filled_slots,
             "slot_utilization": s.slot_utilization,
+            "evictable_blocks": s.evictable_blocks,
+            "cached_blocks": s.cached_blocks,
+            "prefix_query_tokens": s.prefix_query_tokens,
+            "prefix_hit_tokens": s.prefix_hit_tokens,
         }
 
     def export(self, seqs: np.ndarray, tables_out: np.ndarray, ctx_out: np.ndarray) -> None:
@@ -158,9 +193,16 @@ class BlockManager:
         """Snapshot comparable with the oracle model's state() for the given live ids."""
         tables = {int(s): self.block_table(int(s)) for s in sorted(seqs)}
         counts = {int(s): self.num_tokens(int(s)) for s in sorted(seqs)}
+        cache = {}
+        for b in range(self.num_blocks):
+            e = self.cache_entry(b)
+            if e is not None:
+                cache[b] = e
         return {
             "free": self.free_list(),
             "tables": tables,
             "counts": counts,
             "ref": [self.refcount(b) for b in range(self.num_blocks)],
+            "evictable": self.evictable_list(),
+            "cache": cache,
         }

@@ -9,14 +9,28 @@
 //     "Inference Engine Memory Optimisation (KV Cache to Continuous Batching)", §3.
 //   - Forked sequences share blocks; copy-on-write of a shared block:
 //     "vLLM Architecture and Memory Use, ch. 3", §3.2-3.3.
+//   - Prefix cache: a full block's key covers its token ids and everything
+//     before it; hits are mapped into the new request's table; zero-count
+//     cached blocks wait for reuse; eviction is least-recently-used:
+//     "Where Did the VRAM Go (KV cache tutorial)", §4.2-4.4.
 // The last block's fill is derived from the sequence's own token count, so two
 // sequences sharing a block never update a common counter. Every call checks
 // before it mutates: a failing call leaves the state as it was.
+//
+// A cache key is (parent block, block_size token ids); the parent's own key
+// carries its parent, so equal keys mean equal token prefixes. Keys are found
+// through a 64-bit hash and then compared in full, so a hash collision can
+// never map a block with other content. Cached blocks reaching refcount 0 are
+// appended to the evictable list deepest first; since a block never reaches 0
+// after its parent, eviction (oldest first) removes children before parents,
+// and no key can name a parent block that has been reused for other tokens.
 
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <deque>
+#include <iterator>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -31,6 +45,21 @@ struct Seq {
   int64_t count = 0;
 };
 
+// Prefix-cache key of a cached block.
+struct CacheKey {
+  int32_t parent = -1;
+  uint64_t hash = 0;
+  std::vector<int32_t> tokens;
+};
+
+// A block handed out by take(): where it came from, so that a failed batch can
+// put it back exactly (an evicted block gets its key and list position back).
+struct Taken {
+  int32_t block;
+  bool evicted;
+  CacheKey key;
+};
+
 // What one append changed, so that a failed batch can be rolled back exactly.
 struct AppendUndo {
   int64_t seq;
@@ -38,7 +67,21 @@ struct AppendUndo {
   int grown;        // blocks pushed at the end of the table
   int32_t cow_src;  // -1: no copy-on-write
   int32_t cow_dst;
+  std::vector<Taken> taken;  // in the order taken: the copy-on-write block, then grown ones
 };
+
+uint64_t mix64(uint64_t x) {  // splitmix64 finaliser
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+uint64_t key_hash(int32_t parent, const int32_t* tokens, int n) {
+  uint64_t h = mix64(static_cast<uint64_t>(static_cast<int64_t>(parent)) + 1);
+  for (int i = 0; i < n; ++i) h = mix64(h ^ static_cast<uint32_t>(tokens[i]));
+  return h;
+}
 
 }  // namespace
 
@@ -48,17 +91,93 @@ struct pkv_bm {
   std::deque<int32_t> free_q;
   std::unordered_map<int64_t, Seq> seqs;
   std::vector<int32_t> ref;
+  // prefix cache
+  std::vector<char> cached;
+  std::vector<CacheKey> key;
+  std::unordered_multimap<uint64_t, int32_t> index;  // key hash -> block
+  std::list<int32_t> evictable;                      // oldest first
+  std::vector<std::list<int32_t>::iterator> ev_pos;
+  std::vector<char> in_ev;
+  int64_t prefix_query_tokens = 0;
+  int64_t prefix_hit_tokens = 0;
 
   int64_t needed(int64_t tokens) const { return (tokens + bs - 1) / bs; }
+
+  int64_t capacity() const { return static_cast<int64_t>(free_q.size() + evictable.size()); }
 
   int64_t slot(const std::vector<int32_t>& t, int64_t pos) const {
     return static_cast<int64_t>(t[pos / bs]) * bs + pos % bs;
   }
 
-  int32_t pop() {
-    int32_t b = free_q.front();
-    free_q.pop_front();
+  int32_t lookup(int32_t parent, const int32_t* tokens) const {
+    const uint64_t h = key_hash(parent, tokens, bs);
+    auto range = index.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it) {
+      const CacheKey& k = key[it->second];
+      if (k.parent == parent && std::equal(k.tokens.begin(), k.tokens.end(), tokens)) return it->second;
+    }
+    return -1;
+  }
+
+  void add_key(int32_t b, CacheKey k) {
+    index.emplace(k.hash, b);
+    key[b] = std::move(k);
+    cached[b] = 1;
+  }
+
+  CacheKey drop_key(int32_t b) {
+    auto range = index.equal_range(key[b].hash);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    cached[b] = 0;
+    CacheKey k = std::move(key[b]);
+    key[b] = CacheKey();
+    return k;
+  }
+
+  void ev_push_back(int32_t b) {
+    evictable.push_back(b);
+    ev_pos[b] = std::prev(evictable.end());
+    in_ev[b] = 1;
+  }
+
+  void ev_remove(int32_t b) {
+    evictable.erase(ev_pos[b]);
+    in_ev[b] = 0;
+  }
+
+  // One fresh block: the free queue's front, else the oldest evictable block
+  // (its key is dropped). The caller has checked capacity().
+  int32_t take(std::vector<Taken>* log) {
+    if (!free_q.empty()) {
+      int32_t b = free_q.front();
+      free_q.pop_front();
+      if (log) log->push_back(Taken{b, false, CacheKey()});
+      return b;
+    }
+    int32_t b = evictable.front();
+    evictable.pop_front();
+    in_ev[b] = 0;
+    CacheKey k = drop_key(b);
+    if (log) log->push_back(Taken{b, true, std::move(k)});
     return b;
+  }
+
+  // Undo take() calls, most recent first.
+  void untake(std::vector<Taken>& log) {
+    for (auto it = log.rbegin(); it != log.rend(); ++it) {
+      if (it->evicted) {
+        add_key(it->block, std::move(it->key));
+        evictable.push_front(it->block);
+        ev_pos[it->block] = evictable.begin();
+        in_ev[it->block] = 1;
+      } else {
+        free_q.push_front(it->block);
+      }
+    }
   }
 
   // Append n tokens to s; the caller has checked that s exists.
@@ -69,22 +188,24 @@ struct pkv_bm {
     if (n == 0) {
       if (cow_src) *cow_src = -1;
       if (cow_dst) *cow_dst = -1;
-      if (undo) *undo = AppendUndo{id, s.count, 0, -1, -1};
+      if (undo) *undo = AppendUndo{id, s.count, 0, -1, -1, {}};
       return PKV_OK;
     }
     const bool cow = !s.table.empty() && (s.count % bs) != 0 && ref[s.table.back()] > 1;
     const int64_t grow = needed(s.count + n) - static_cast<int64_t>(s.table.size());
     const int64_t need = grow + (cow ? 1 : 0);
-    if (static_cast<int64_t>(free_q.size()) < need) return PKV_ERR_OOM;
+    if (capacity() < need) return PKV_ERR_OOM;
+    std::vector<Taken> log;
+    std::vector<Taken>* lp = undo ? &log : nullptr;
     if (cow) {
       csrc = s.table.back();
-      cdst = pop();
+      cdst = take(lp);
       ref[csrc] -= 1;
       ref[cdst] += 1;
       s.table.back() = cdst;
     }
     for (int64_t i = 0; i < grow; ++i) {
-      int32_t b = pop();
+      int32_t b = take(lp);
       ref[b] += 1;
       s.table.push_back(b);
     }
@@ -94,26 +215,22 @@ struct pkv_bm {
       for (int64_t p = prev; p < s.count; ++p) slots[p - prev] = slot(s.table, p);
     if (cow_src) *cow_src = csrc;
     if (cow_dst) *cow_dst = cdst;
-    if (undo) *undo = AppendUndo{id, prev, static_cast<int>(grow), csrc, cdst};
+    if (undo) *undo = AppendUndo{id, prev, static_cast<int>(grow), csrc, cdst, std::move(log)};
     return PKV_OK;
   }
 
-  void undo_append(const AppendUndo& u) {
+  void undo_append(AppendUndo& u) {
     Seq& s = seqs.at(u.seq);
-    // Blocks were popped in the order: cow dst, then grown blocks. Put them
-    // back at the front in reverse order so the pool is exactly as before.
     for (int i = 0; i < u.grown; ++i) {
-      int32_t b = s.table.back();
+      ref[s.table.back()] -= 1;
       s.table.pop_back();
-      ref[b] -= 1;
-      free_q.push_front(b);
     }
     if (u.cow_src >= 0) {
       s.table.back() = u.cow_src;
       ref[u.cow_src] += 1;
       ref[u.cow_dst] -= 1;
-      free_q.push_front(u.cow_dst);
     }
+    untake(u.taken);
     s.count = u.prev_count;
   }
 };
@@ -154,6 +271,10 @@ int pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order, pkv
   bm->bs = block_size;
   bm->free_q.assign(order.begin(), order.end());
   bm->ref.assign(num_blocks, 0);
+  bm->cached.assign(num_blocks, 0);
+  bm->key.resize(num_blocks);
+  bm->ev_pos.resize(num_blocks);
+  bm->in_ev.assign(num_blocks, 0);
   *out = bm;
   return PKV_OK;
 }
@@ -164,11 +285,11 @@ int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out)
   if (!bm || num_tokens < 0) return PKV_ERR_INVALID;
   if (bm->seqs.count(seq)) return PKV_ERR_EXISTS;
   const int64_t nb = bm->needed(num_tokens);
-  if (static_cast<int64_t>(bm->free_q.size()) < nb) return PKV_ERR_OOM;
+  if (bm->capacity() < nb) return PKV_ERR_OOM;
   Seq s;
   s.table.reserve(nb);
   for (int64_t i = 0; i < nb; ++i) {
-    int32_t b = bm->pop();
+    int32_t b = bm->take(nullptr);
     bm->ref[b] += 1;
     s.table.push_back(b);
   }
@@ -176,6 +297,54 @@ int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out)
   if (slots_out)
     for (int64_t p = 0; p < num_tokens; ++p) slots_out[p] = bm->slot(s.table, p);
   bm->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_bm_allocate_prompt(pkv_bm* bm, int64_t seq, const int32_t* tokens, int n_tokens, int* n_cached,
+                           int64_t* slots_out) {
+  if (!bm || n_tokens < 0 || !n_cached || (n_tokens > 0 && (!tokens || !slots_out))) return PKV_ERR_INVALID;
+  if (bm->seqs.count(seq)) return PKV_ERR_EXISTS;
+  const int bs = bm->bs;
+  const int full = n_tokens / bs;
+  std::vector<int32_t> matched;
+  int32_t parent = -1;
+  for (int i = 0; i < full; ++i) {
+    const int32_t b = bm->lookup(parent, tokens + static_cast<int64_t>(i) * bs);
+    if (b < 0) break;
+    matched.push_back(b);
+    parent = b;
+  }
+  const int64_t fresh = bm->needed(n_tokens) - static_cast<int64_t>(matched.size());
+  int64_t revived = 0;
+  for (int32_t b : matched) revived += bm->ref[b] == 0;
+  if (bm->capacity() - revived < fresh) return PKV_ERR_OOM;
+  for (int32_t b : matched) {
+    if (bm->ref[b] == 0) bm->ev_remove(b);
+    bm->ref[b] += 1;
+  }
+  Seq s;
+  s.table = matched;
+  for (int64_t i = 0; i < fresh; ++i) {
+    const int32_t b = bm->take(nullptr);
+    bm->ref[b] += 1;
+    s.table.push_back(b);
+  }
+  for (int i = static_cast<int>(matched.size()); i < full; ++i) {
+    const int32_t* t = tokens + static_cast<int64_t>(i) * bs;
+    CacheKey k;
+    k.parent = parent;
+    k.hash = key_hash(parent, t, bs);
+    k.tokens.assign(t, t + bs);
+    bm->add_key(s.table[i], std::move(k));
+    parent = s.table[i];
+  }
+  s.count = n_tokens;
+  const int64_t c = static_cast<int64_t>(matched.size()) * bs;
+  for (int64_t p = c; p < n_tokens; ++p) slots_out[p - c] = bm->slot(s.table, p);
+  bm->seqs.emplace(seq, std::move(s));
+  *n_cached = static_cast<int>(c);
+  bm->prefix_query_tokens += n_tokens;
+  bm->prefix_hit_tokens += c;
   return PKV_OK;
 }
 
@@ -215,7 +384,7 @@ int append_batch_impl(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot
       for (auto r = log.rbegin(); r != log.rend(); ++r) bm->undo_append(*r);
       return st;
     }
-    log.push_back(u);
+    log.push_back(std::move(u));
     if (cow_row) cow_row[i] = cs >= 0;
     if (cs >= 0) {
       cow_pairs_out[2 * ncow] = cs;
@@ -298,10 +467,17 @@ int pkv_bm_free(pkv_bm* bm, int64_t seq) {
   if (!bm) return PKV_ERR_INVALID;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+  std::vector<int32_t> to_cache;
   for (int32_t b : it->second.table) {
     bm->ref[b] -= 1;
-    if (bm->ref[b] == 0) bm->free_q.push_back(b);
+    if (bm->ref[b] == 0) {
+      if (bm->cached[b])
+        to_cache.push_back(b);
+      else
+        bm->free_q.push_back(b);
+    }
   }
+  for (auto r = to_cache.rbegin(); r != to_cache.rend(); ++r) bm->ev_push_back(*r);
   bm->seqs.erase(it);
   return PKV_OK;
 }
@@ -350,6 +526,26 @@ int pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n) {
   return PKV_OK;
 }
 
+int pkv_bm_evictable_list(const pkv_bm* bm, int32_t* out, int cap, int* n) {
+  if (!bm || !n || cap < 0) return PKV_ERR_INVALID;
+  if (static_cast<int>(bm->evictable.size()) > cap || (!bm->evictable.empty() && !out))
+    return PKV_ERR_INVALID;
+  std::copy(bm->evictable.begin(), bm->evictable.end(), out);
+  *n = static_cast<int>(bm->evictable.size());
+  return PKV_OK;
+}
+
+int pkv_bm_cache_entry(const pkv_bm* bm, int32_t block, int* cached, int32_t* parent, int32_t* tokens_out) {
+  if (!bm || !cached || !parent || block < 0 || block >= bm->num_blocks) return PKV_ERR_INVALID;
+  *cached = bm->cached[block];
+  *parent = -1;
+  if (!*cached) return PKV_OK;
+  if (!tokens_out) return PKV_ERR_INVALID;
+  *parent = bm->key[block].parent;
+  std::copy(bm->key[block].tokens.begin(), bm->key[block].tokens.end(), tokens_out);
+  return PKV_OK;
+}
+
 int pkv_bm_num_free(const pkv_bm* bm) {
   return bm ? static_cast<int>(bm->free_q.size()) : PKV_ERR_INVALID;
 }
@@ -369,7 +565,12 @@ int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out) {
   for (int32_t f : filled) total_filled += f;
   out->total_blocks = bm->num_blocks;
   out->free_blocks = static_cast<int32_t>(bm->free_q.size());
-  out->used_blocks = bm->num_blocks - out->free_blocks;
+  out->evictable_blocks = static_cast<int32_t>(bm->evictable.size());
+  out->used_blocks = bm->num_blocks - out->free_blocks - out->evictable_blocks;
+  out->cached_blocks = 0;
+  for (char c : bm->cached) out->cached_blocks += c;
+  out->prefix_query_tokens = bm->prefix_query_tokens;
+  out->prefix_hit_tokens = bm->prefix_hit_tokens;
   out->live_seqs = static_cast<int32_t>(bm->seqs.size());
   out->filled_slots = total_filled;
   out->utilization = static_cast<double>(out->used_blocks) / bm->num_blocks;

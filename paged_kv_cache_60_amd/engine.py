@@ -71,8 +71,11 @@ class PagedKVEngine:
 
     # ------------------------------------------------------ scripted rounds
     def apply_ops(self, ops_list):
-        """Run block-manager ops in order; returns (slots int64 array, cow pairs list)."""
-        slots, pairs = [], []
+        """Run block-manager ops in order; returns (slots int64 array of the
+        allocate / append ops, cow pairs list, prompts list). A prompt op goes
+        through the prefix cache; its entry is (op, cached tokens, slots of the
+        tokens after them), the ones whose K/V must still be written."""
+        slots, pairs, prompts = [], [], []
         bm = self.bm
         for op in ops_list:
             if op.kind == "allocate":
@@ -88,10 +91,13 @@ class PagedKVEngine:
                 bm.fork(op.src, op.seq)
             elif op.kind == "free":
                 bm.free_seq(op.seq)
+            elif op.kind == "prompt":
+                c, sl = bm.allocate_prompt(op.seq, op.tokens)
+                prompts.append((op, c, sl))
             else:
                 raise ValueError(op.kind)
         s = np.concatenate(slots) if slots else np.zeros(0, dtype=np.int64)
-        return s, pairs
+        return s, pairs, prompts
 
     def copy_blocks(self, pairs):
         if pairs:

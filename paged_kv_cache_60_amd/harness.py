@@ -25,8 +25,11 @@ def make_engine(wl, device="cuda", poison=True) -> PagedKVEngine:
 
 
 def replay_round(eng: PagedKVEngine, wl, ops, chunk_tokens: int = 1 << 18):
-    slots, pairs = eng.apply_ops(ops)
+    slots, pairs, prompts = eng.apply_ops(ops)
     eng.copy_blocks(pairs)
+    for op, c, sl in prompts:  # rows after the cached blocks only
+        K, V = wl.prompt_kv(op, c)
+        eng.write(sl, K, V)
     creating = [o for o in ops if o.kind in ("allocate", "append") and o.n > 0]
     pos = i = 0
     while i < len(creating):

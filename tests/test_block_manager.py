@@ -42,6 +42,8 @@ class _Both:
             assert (res_o.slots, res_o.cow_src, res_o.cow_dst) == (res_c.slots, res_c.cow_src, res_c.cow_dst)
         elif err_o is None and name == "allocate":
             assert res_o == res_c
+        elif err_o is None and name == "allocate_prompt":
+            assert res_o[0] == res_c[0] and list(res_o[1]) == res_c[1].tolist()
         self.compare()
 
     def compare(self):
@@ -164,18 +166,24 @@ def test_append_batch_is_atomic():
     assert before != c.state([0, 1, 2])
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, "3cached"])
 def test_workload_scripts_bit_exact(cfg):
     kw = {"max_steps": 3}
-    wl = workloads.make(cfg, **kw)
+    wl = workloads.qwen3_prefix_cached(**kw) if cfg == "3cached" else workloads.make(cfg, **kw)
     o = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
     c = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
     from paged_kv_cache_60_amd.engine import PagedKVEngine
     for ops in wl.setup_rounds:
         ro = apply_ops(o, ops)
-        sc, pc = PagedKVEngine.apply_ops(type("E", (), {"bm": c})(), ops)
+        sc, pc, prc = PagedKVEngine.apply_ops(type("E", (), {"bm": c})(), ops)
         assert ro.slots == sc.tolist()
         assert ro.cow_pairs == pc
+        assert [(op, n, list(sl)) for op, n, sl in ro.prompts] == [(op, n, sl.tolist()) for op, n, sl in prc]
+    if cfg == "3cached":
+        # the system prompt is found for every sequence after the first
+        prefix = wl.meta["prefix_tokens"]
+        assert c.stats()["prefix_hit_tokens"] == (len(wl.batch) - 1) * prefix
+        assert [cc for _, cc, _ in ro.prompts] == [0] + [prefix] * (len(wl.batch) - 1)
     batch = np.asarray(wl.batch, dtype=np.int64)
     for s in range(3):
         ro = apply_ops(o, wl.step_ops(s))
@@ -237,3 +245,90 @@ def test_decode_step_updates_reproduce_tables(cfg):
     assert total_upd > 0
     if cfg == "5cow":
         assert total_cow > 0  # beams whose tail starts in the decode step copy their block
+
+
+# ------------------------------------------------------------------ prefix cache
+def test_prefix_cache_scenarios_bit_exact():
+    b = _Both(12, 4)
+    b.call("allocate_prompt", 0, list(range(10)))          # 2 cached blocks + a partial one
+    b.call("allocate_prompt", 1, list(range(10)))          # hits 8 tokens
+    b.call("allocate_prompt", 2, list(range(6)) + [99, 98, 97])   # diverges inside block 1
+    b.call("allocate_prompt", 1, [1])                      # EXISTS
+    b.call("free_seq", 0)
+    b.call("free_seq", 1)                                  # block 1 now evictable
+    b.call("append", 2, 5)
+    b.call("allocate", 3, 20)                              # drains the queue, evicts oldest cached
+    b.call("allocate_prompt", 4, list(range(10)))          # what is left of the chain still hits
+    b.call("allocate_prompt", 5, list(range(200)))         # OOM, nothing changes
+    b.call("fork", 4, 6)
+    b.call("free_seq", 4)
+    b.call("free_seq", 6)
+    so, sc = b.o.stats(), b.c.stats()
+    for k in so:
+        assert so[k] == pytest.approx(sc[k]), k
+
+
+prompt_ops = st.tuples(
+    st.sampled_from(["prompt", "prompt", "prompt", "append", "fork", "free_seq", "allocate", "share_prefix"]),
+    st.integers(0, 5), st.integers(0, 5), st.lists(st.integers(0, 2), max_size=13))
+
+
+@settings(max_examples=300, deadline=None)
+@given(bs=st.sampled_from([1, 2, 3, 4]), nb=st.integers(1, 20), ops=st.lists(prompt_ops, max_size=50))
+def test_random_prompt_ops_bit_exact(bs, nb, ops):
+    b = _Both(nb, bs)
+    for kind, a, c, toks in ops:
+        if kind == "prompt":
+            b.call("allocate_prompt", a, toks)
+        elif kind == "append":
+            b.call("append", a, 1 + len(toks) % 4)
+        elif kind == "fork":
+            b.call("fork", a, c)
+        elif kind == "allocate":
+            b.call("allocate", a, len(toks))
+        elif kind == "share_prefix":
+            b.call("share_prefix", a, len(toks) % 3, c)
+        else:
+            b.call("free_seq", a)
+    so, sc = b.o.stats(), b.c.stats()
+    for k in so:
+        assert so[k] == pytest.approx(sc[k]), k
+
+
+def test_append_batch_rollback_restores_evicted_blocks():
+    """A batch that evicts cached blocks and then runs out rolls back exactly:
+    the evicted blocks get their keys and their places on the evictable list back."""
+    c = BlockManager(6, 2)
+    o = BlockAllocatorModel(6, 2)
+    for m in (c, o):
+        m.allocate_prompt(0, [1, 1, 2, 2])       # blocks 0, 1 cached
+        m.allocate_prompt(1, [3, 3, 4, 4])       # blocks 2, 3 cached
+        m.allocate(2, 3)                         # blocks 4, 5 (5 half full)
+        m.free_seq(0)                            # evictable [1, 0]
+        m.free_seq(1)                            # evictable [1, 0, 3, 2]; the free queue is empty
+        m.fork(2, 4)                             # 4 and 5 shared: seq 2's next token copies block 5
+        for s in (3, 5, 6, 7):
+            m.allocate(s, 0)                     # empty sequences: their first token takes a block
+    live = [2, 3, 4, 5, 6, 7]
+    before = c.state(live)
+    assert before == o.state()
+    assert c.evictable_list() == [1, 0, 3, 2]
+    slots = np.empty(8, dtype=np.int64)
+    cow = np.empty(16, dtype=np.int32)
+    # 2: copy-on-write takes 1; 3 takes 0; 5 takes 3; 6 takes 2; 7 finds nothing -> OOM, all undone
+    with pytest.raises(PkvError) as e:
+        c.append_batch(np.array([2, 3, 5, 6, 7], dtype=np.int64), slots, cow)
+    assert e.value.code == -2
+    assert c.state(live) == before
+    assert c.cache_entry(1) == (0, [2, 2]) and c.cache_entry(2) == (-1, [3, 3])
+    # without the last sequence the batch fits; the oracle, appending one by one, agrees
+    n = c.append_batch(np.array([2, 3, 5, 6], dtype=np.int64), slots, cow)
+    exp_slots, exp_pairs = [], []
+    for sq in (2, 3, 5, 6):
+        r = o.append(sq, 1)
+        exp_slots += r.slots
+        if r.cow_src >= 0:
+            exp_pairs += [r.cow_src, r.cow_dst]
+    assert slots[:4].tolist() == exp_slots and cow[:2 * n].tolist() == exp_pairs
+    assert c.state(live) == o.state()
+    assert c.evictable_list() == [] and c.cache_entry(1) is None

@@ -209,3 +209,20 @@ def test_batch_of_more_than_4096_sequences(hq, hkv):
     ref = oattn.decode_attention(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), tables, ctx.tolist(),
                                  bs, 0.125)
     assert_close_to_oracle(out.cpu().numpy(), ref, "f16", "batch 4100")
+
+
+def test_config3_prefix_cache_matches_scripted_sharing():
+    """The shared-prefix workload with its sharing found by the block manager's prefix
+    cache (every sequence allocated from its token ids) gives the same output bits as
+    with the sharing written into the script; sampled outputs match the oracle."""
+    scripted = workloads.qwen3_prefix(max_steps=1)
+    cached = workloads.qwen3_prefix_cached(max_steps=1)
+    log("config 3: scripted sharing")
+    _, o1, _ = _gpu_run(scripted, 1)
+    log("config 3: prefix-cache sharing")
+    eng, o2, _ = _gpu_run(cached, 1)
+    assert np.array_equal(o1[0].view(np.uint16), o2[0].view(np.uint16))
+    assert eng.bm.stats()["prefix_hit_tokens"] == (len(cached.batch) - 1) * cached.meta["prefix_tokens"]
+    seqs = sample_seqs(cached.meta["lengths"], 4)
+    o = runner.run(cached, steps=1, seqs=seqs)
+    assert_close_to_oracle(o2[0], o.outputs[0], "f16", "config 3 cached")

@@ -191,3 +191,22 @@ def test_random_prompt_ops_keep_invariants_and_content(bs, nb, ops):
                 e = m.cache_entry(child)
                 if e is not None and e[0] == blk:
                     assert child in pos and pos[child] < pos[blk]
+
+
+def test_cached_workload_gives_the_scripted_outputs_exactly():
+    """Sharing found by the prefix cache and sharing written into the script
+    give the same float64 attention outputs (same K/V per logical position),
+    while the cached run writes the system prompt once."""
+    import numpy as np
+
+    import workloads
+    from oracle import runner
+    scripted = runner.run(workloads.qwen3_prefix(batch=4, max_steps=1), steps=1)
+    cached_wl = workloads.qwen3_prefix_cached(batch=4, max_steps=1)
+    cached = runner.run(cached_wl, steps=1, keep_rounds=True)
+    assert np.array_equal(scripted.outputs[0], cached.outputs[0])
+    hits = [c for _, c, _ in cached.rounds[0].prompts]
+    assert hits == [0, 1024, 1024, 1024]
+    t = cached.tables[0]
+    assert all(t[s][:64] == t[0][:64] for s in range(4))
+    assert cached.alloc.stats()["prefix_hit_tokens"] == 3 * 1024

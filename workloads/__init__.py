@@ -14,6 +14,7 @@ purpose, keyed by ``SeedSequence([seed, stream, index...])``, so any piece
     stream 1  initial free-block order (a permutation of the pool)
     stream 2  queries, one draw per decode step
     stream 3  K then V rows of one token-creating operation
+    stream 4  prompt token ids
 
 K/V/Q values are float32 N(0, 1) draws rounded to float16.
 
@@ -35,6 +36,7 @@ STREAM_LENGTHS = 0
 STREAM_PERM = 1
 STREAM_Q = 2
 STREAM_KV = 3
+STREAM_TOKENS = 4
 
 
 def rng(seed: int, *key: int) -> np.random.Generator:
@@ -46,14 +48,20 @@ class Op:
     """One block-manager call.
 
     kind: "allocate" (seq, n tokens), "append" (seq, n tokens),
-          "share_prefix" (src -> seq, n blocks), "fork" (src -> seq).
-    key:  index of the op's K/V draw in stream 3 (token-creating ops only).
+          "share_prefix" (src -> seq, n blocks), "fork" (src -> seq),
+          "prompt" (seq, n = len(tokens): a new sequence through the prefix
+          cache; only the tokens after the cached ones are written).
+    key:  index of the op's K/V draw in stream 3 (allocate / append).
+    tokens: a prompt's token ids.
+    parts:  a prompt's K/V rows, in order, as (key in stream 3, rows) draws.
     """
     kind: str
     seq: int
     n: int = 0
     src: int = -1
     key: int = -1
+    tokens: tuple = ()
+    parts: tuple = ()
 
     @property
     def creates_tokens(self) -> bool:
@@ -103,13 +111,35 @@ class Workload:
         B = len(self.batch)
         return g.standard_normal((B, self.num_q_heads, self.head_dim), dtype=np.float32).astype(np.float16)
 
-    def op_kv(self, op: Op):
-        """(K, V) float16 [n, Hkv, D] for a token-creating op."""
-        g = rng(self.seed, STREAM_KV, op.key)
-        shape = (op.n, self.num_kv_heads, self.head_dim)
+    def _draw(self, key: int, n: int):
+        g = rng(self.seed, STREAM_KV, key)
+        shape = (n, self.num_kv_heads, self.head_dim)
         k = g.standard_normal(shape, dtype=np.float32).astype(np.float16)
         v = g.standard_normal(shape, dtype=np.float32).astype(np.float16)
         return k, v
+
+    def op_kv(self, op: Op):
+        """(K, V) float16 [n, Hkv, D] for a token-creating op (a prompt: all its rows)."""
+        if op.kind == "prompt":
+            return self.prompt_kv(op, 0)
+        return self._draw(op.key, op.n)
+
+    def prompt_kv(self, op: Op, start: int):
+        """(K, V) of a prompt's rows start..n-1 (the ones not found in the cache);
+        draws that lie wholly before `start` are skipped."""
+        hkv, d = self.num_kv_heads, self.head_dim
+        ks, vs, pos = [], [], 0
+        for key, rows in op.parts:
+            if rows > 0 and pos + rows > start:
+                k, v = self._draw(key, rows)
+                lo = max(0, start - pos)
+                ks.append(k[lo:])
+                vs.append(v[lo:])
+            pos += rows
+        if not ks:
+            z = np.zeros((0, hkv, d), dtype=np.float16)
+            return z, z.copy()
+        return np.concatenate(ks), np.concatenate(vs)
 
     def round_kv(self, ops, threads: int = 8):
         """Concatenated (K, V) of a round's token-creating ops, in op order."""
@@ -256,6 +286,29 @@ def qwen3_prefix(max_steps: int = 32, batch: int = 256) -> Workload:
         max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, bs),
         meta={"lengths": lengths, "prefix_tokens": prefix},
     )
+
+
+def qwen3_prefix_cached(max_steps: int = 32, batch: int = 256) -> Workload:
+    """The Qwen3-0.6B shared-prefix workload with its sharing found by the
+    prefix cache instead of scripted: every sequence arrives as one prompt of
+    token ids (the same 1024-token system prompt, then its own suffix) and is
+    allocated through the block manager's prefix cache ("Where Did the VRAM Go
+    (KV cache tutorial)", §4.2). K/V rows of each logical position are the same
+    draws as in the scripted workload, so attention outputs must be identical."""
+    base = qwen3_prefix(max_steps=max_steps, batch=batch)
+    prefix = base.meta["prefix_tokens"]
+    lengths = base.meta["lengths"]
+    g = rng(base.seed, STREAM_TOKENS, 0)
+    sys_prompt = g.integers(0, 50_000, size=prefix).tolist()
+    ops = []
+    for s in range(batch):
+        suffix = lengths[s] - prefix - 1          # the last token is written by the first decode step
+        toks = sys_prompt + rng(base.seed, STREAM_TOKENS, 1 + s).integers(0, 50_000, size=suffix).tolist()
+        ops.append(Op("prompt", s, len(toks), tokens=tuple(toks), parts=((0, prefix), (1 + s, suffix))))
+    base.name = "qwen3_0p6b_gqa_prefix_cached_b256"
+    base.description = base.description + ", sharing found by the prefix cache"
+    base.setup_rounds = [ops]
+    return base
 
 
 def opt13b_rag(max_steps: int = 32, batch: int = 128) -> Workload:
