@@ -16,6 +16,8 @@ fp8         OCP e4m3fn encode (round-to-nearest-even, saturating) and decode,
 cache_ops   slot scatter into the paged cache and whole-block copy.
 attention   gather-by-block-table then fp64 softmax attention for one decode
             token per sequence.
+prefill     chunked (multi-token, causal) attention over the same paged
+            cache: the positions a prompt did not find in the prefix cache.
 kvsize      closed forms for KV bytes, pool sizing and reservation waste.
 runner      drives a workload scenario through the functions above.
 

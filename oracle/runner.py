@@ -6,7 +6,8 @@ their slots. This is the lifecycle of "From OOM to Smooth Inference (RAG
 memory management)", §2.3 (allocate, append, release) with the sharing and
 copy-on-write of "vLLM Architecture and Memory Use, ch. 3", §3.2-3.3.
 A decode step is one such round (one appended token per sequence) followed by
-decode attention over the batch.
+decode attention over the batch. A prefill run is the setup rounds followed by
+causal attention for each sequence's chunk of query rows.
 
 Unused cache slots start as a NaN bit pattern (0x7E00 for float16, 0x7F for
 e4m3fn) so that a kernel reading past a sequence's tokens shows up.
@@ -20,6 +21,7 @@ import numpy as np
 from .allocator import BlockAllocatorModel
 from .attention import decode_attention
 from .cache_ops import block_copy, scatter
+from .prefill import prefill_attention
 
 F16_NAN_BITS = 0x7E00
 FP8_NAN_BITS = 0x7F
@@ -115,3 +117,41 @@ def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) ->
         run_.tables.append(tables)
         run_.ctx_lens.append(lens)
     return run_
+
+
+@dataclass
+class PrefillRun:
+    alloc: BlockAllocatorModel
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    cached: dict          # prompt sequence -> tokens found in the prefix cache
+    chunks: list          # query rows per batch sequence
+    q_start: np.ndarray   # int64 [B + 1]
+    q: np.ndarray         # float16 [total_q, Hq, D]
+    tables: list
+    ctx_lens: list
+    output: np.ndarray    # float64 [total_q, Hq, D] (NaN rows outside the sample)
+
+
+def run_prefill(wl, seqs=None) -> PrefillRun:
+    """Apply the setup rounds, then one prefill pass: every batch sequence's
+    chunk (the positions its prompt did not find in the prefix cache, or its
+    scripted last positions) attends causally over its context
+    ("Where Did the VRAM Go (KV cache tutorial)", §4.2). seqs restricts
+    attention to a sample of batch positions."""
+    alloc = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
+    kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+    cached = {}
+    for ops in wl.setup_rounds:
+        r = run_round(wl, alloc, kc, vc, ops)
+        for op, c, _ in r.prompts:
+            cached[op.seq] = c
+    chunks = wl.chunk_lengths(cached)
+    q_start = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    q = np.concatenate([wl.prefill_queries(s, n) for s, n in zip(wl.batch, chunks)])
+    tables = [alloc.block_table(s) for s in wl.batch]
+    lens = [alloc.num_tokens(s) for s in wl.batch]
+    out = prefill_attention(q, q_start, kc, vc, tables, lens, wl.block_size, wl.sm_scale,
+                            wl.kv_dtype, wl.k_scale, wl.v_scale, seqs=seqs)
+    return PrefillRun(alloc, kc, vc, cached, chunks, q_start, q, tables, lens, out)

@@ -15,6 +15,7 @@ purpose, keyed by ``SeedSequence([seed, stream, index...])``, so any piece
     stream 2  queries, one draw per decode step
     stream 3  K then V rows of one token-creating operation
     stream 4  prompt token ids
+    stream 5  prefill query rows, one draw per sequence
 
 K/V/Q values are float32 N(0, 1) draws rounded to float16.
 
@@ -22,7 +23,10 @@ A workload is a script: setup rounds, then decode steps. A round is a list of
 operations applied to the block manager in order; the tokens that the round
 creates are then written (after any copy-on-write block copies the round
 produced). Each decode step appends one token to every sequence of the batch
-and then runs attention for the batch.
+and then runs attention for the batch. A prefill run instead attends, after
+the setup, with one query row per position of each sequence's chunk: the
+positions a prompt wrote past its cached blocks, or the last ``meta["chunk"][s]``
+positions of a sequence built by plain allocation.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ STREAM_PERM = 1
 STREAM_Q = 2
 STREAM_KV = 3
 STREAM_TOKENS = 4
+STREAM_PREFILL_Q = 5
 
 
 def rng(seed: int, *key: int) -> np.random.Generator:
@@ -110,6 +115,29 @@ class Workload:
         g = rng(self.seed, STREAM_Q, step)
         B = len(self.batch)
         return g.standard_normal((B, self.num_q_heads, self.head_dim), dtype=np.float32).astype(np.float16)
+
+    def prefill_queries(self, seq: int, n: int) -> np.ndarray:
+        """Query rows [n, Hq, D] float16 of sequence `seq`'s prefill chunk."""
+        g = rng(self.seed, STREAM_PREFILL_Q, seq)
+        return g.standard_normal((n, self.num_q_heads, self.head_dim), dtype=np.float32).astype(np.float16)
+
+    def chunk_lengths(self, cached: dict) -> list:
+        """Query rows per batch sequence for a prefill run after the setup.
+
+        cached: {seq: tokens found in the prefix cache} for prompt sequences,
+        as the block manager reported them; such a sequence's chunk is the
+        rest of its prompt. Other sequences take meta["chunk"][batch index]."""
+        prompt_len = {o.seq: o.n for r in self.setup_rounds for o in r if o.kind == "prompt"}
+        chunk = self.meta.get("chunk")
+        out = []
+        for i, s in enumerate(self.batch):
+            if s in prompt_len:
+                out.append(prompt_len[s] - int(cached[s]))
+            elif chunk is not None:
+                out.append(int(chunk[i]))
+            else:
+                raise ValueError(f"sequence {s} has no prefill chunk")
+        return out
 
     def _draw(self, key: int, n: int):
         g = rng(self.seed, STREAM_KV, key)
@@ -311,6 +339,71 @@ def qwen3_prefix_cached(max_steps: int = 32, batch: int = 256) -> Workload:
     return base
 
 
+def prefill_tiny() -> Workload:
+    """Prefill through the prefix cache at the tiny decode shape: 8 query
+    heads = 8 KV heads, head_dim 64, block size 16, a 64-block pool in a seeded
+    order. Four prompts of 37, 100, 16 and 250 tokens; prompts 0, 1 and 3 open
+    with the same 32-token system prompt (two full blocks), so prompt 0 misses
+    and prompts 1 and 3 find both blocks; prompt 2 is 16 tokens of its own.
+    Each prompt's chunk is what it did not find: 37, 68, 16 and 218 rows."""
+    seed = 6
+    lengths = [37, 100, 16, 250]
+    common = 32
+    sys_prompt = rng(seed, STREAM_TOKENS, 0).integers(0, 50_000, size=common).tolist()
+    ops = []
+    for s, L in enumerate(lengths):
+        if L >= common and s != 2:
+            own = rng(seed, STREAM_TOKENS, 1 + s).integers(0, 50_000, size=L - common).tolist()
+            toks, parts = sys_prompt + own, ((0, common), (1 + s, L - common))
+        else:
+            toks, parts = rng(seed, STREAM_TOKENS, 1 + s).integers(0, 50_000, size=L).tolist(), ((1 + s, L),)
+        ops.append(Op("prompt", s, L, tokens=tuple(toks), parts=parts))
+    nb = 64
+    return Workload(
+        name="tiny_prefill_prefix_cache", seed=seed,
+        description="4 prompts L={37,100,16,250} (3 share a 32-token system prompt), 8/8 heads, D=64, "
+                    "bs=16, 64-block pool",
+        num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=16, kv_dtype="f16",
+        num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(4)),
+        setup_rounds=[ops], max_steps=0, max_blocks_per_seq=_ceil_div(max(lengths), 16),
+        meta={"lengths": lengths},
+    )
+
+
+def qwen3_prefill(batch: int = 256) -> Workload:
+    """Prefill of the Qwen3-0.6B-shaped shared-prefix workload through the
+    prefix cache: 16 query heads over 8 KV heads, head_dim 128, block size
+    16; every prompt is the same 1024-token system prompt plus its own suffix
+    (uniform [16, 3072] tokens, less the one a decode step would add). Prompt
+    0 misses and prefills all of its tokens; the other 255 find the 64 system
+    prompt blocks and prefill only their suffix ("Where Did the VRAM Go (KV
+    cache tutorial)", §4.2, §5)."""
+    wl = qwen3_prefix_cached(max_steps=0, batch=batch)
+    wl.name = "qwen3_0p6b_gqa_prefill_prefix_cache_b256" if batch == 256 else f"qwen3_prefill_b{batch}"
+    wl.description = ("Qwen3-0.6B-shaped GQA 16/8 heads, D=128, bs=16: prefill of 256 prompts = shared "
+                      "1024-token system prompt (cached after the first) + suffix~U[16,3072]")
+    wl.meta = dict(wl.meta, lengths=[L - 1 for L in wl.meta["lengths"]])
+    return wl
+
+
+def llama2_7b_chunked(batch: int = 64, chunk: int = 512) -> Workload:
+    """Chunked prefill at the Llama-2-7B decode shape: 32 query heads = 32
+    KV heads, head_dim 128, block size 16, batch 64 with context lengths
+    uniform on [128, 2048] (the same draws as the decode workload); each
+    sequence's last min(L, 512) positions are one prefill chunk that attends
+    the earlier positions and itself. Chunk boundaries fall inside blocks."""
+    base = llama2_7b(max_steps=1, batch=batch)
+    L = base.meta["lengths"]
+    setup = [[Op("allocate", s, l, key=s) for s, l in enumerate(L)]]
+    base.name = f"llama2_7b_chunked_prefill_b{batch}_c{chunk}"
+    base.description = f"Llama-2-7B-shaped layer, batch {batch}, L~U[128,2048], last {chunk}-token chunk prefilled"
+    base.setup_rounds = setup
+    base.max_steps = 0
+    base.max_blocks_per_seq = _ceil_div(max(L), 16)
+    base.meta = dict(base.meta, chunk=[min(l, chunk) for l in L])
+    return base
+
+
 def opt13b_rag(max_steps: int = 32, batch: int = 128) -> Workload:
     """OPT-13B-shaped RAG decode: 40 query heads = 40 KV heads, head_dim 128,
     block size 32, batch 128, attended lengths round(N(3000, 400)) clipped to
@@ -397,6 +490,28 @@ CONFIGS = {
 
 def make(config: int, **kw) -> Workload:
     return CONFIGS[config](**kw)
+
+
+def small_prefill(seed: int, lengths, chunks, num_q_heads, num_kv_heads, head_dim, block_size,
+                  kv_dtype="f16", slack=1.25) -> Workload:
+    """Independent sequences of the given context lengths, each holding all
+    its tokens, whose last chunks[s] positions are prefilled (edge cases:
+    chunks of one row, whole-sequence chunks, chunk edges inside blocks)."""
+    L = list(lengths)
+    need = sum(_ceil_div(l, block_size) for l in L)
+    nb = max(1, math.ceil(slack * need))
+    setup = [[Op("allocate", s, l, key=s) for s, l in enumerate(L)]]
+    wl = Workload(
+        name=f"prefill_{seed}", seed=seed, description="prefill edge-case workload",
+        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        block_size=block_size, kv_dtype=kv_dtype, num_blocks=nb, free_order=_perm(seed, nb),
+        batch=list(range(len(L))), setup_rounds=setup, max_steps=0,
+        max_blocks_per_seq=max(1, _ceil_div(max(L + [1]), block_size)),
+        meta={"lengths": L, "chunk": list(chunks)},
+    )
+    if kv_dtype == "fp8":
+        _fp8_scales(wl, 0)
+    return wl
 
 
 def small_custom(seed: int, lengths, num_q_heads, num_kv_heads, head_dim, block_size,
