@@ -171,6 +171,153 @@ def load_counters(config_name):
     return entry.get("hbm_bytes_per_launch")
 
 
+PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (% of MFMA fp16 dense peak) + query tokens/sec"
+PEAK_TFLOPS_F16 = 2500.0  # MI355X dense fp16 matrix peak
+PREFILL_WORKLOADS = {"qwen3": "qwen3_prefill", "llama2": "llama2_7b_chunked"}
+
+
+def prefill_flops(ctx, chunks, hq, d):
+    """Algorithmic flops of one chunked-prefill call: q.k and p.v (2 flops per
+    multiply-add each) over the positions every query row sees, causal."""
+    total = 0
+    for L, n in zip(ctx, chunks):
+        pos = np.arange(int(L) - int(n), int(L), dtype=np.int64)
+        total += int(np.maximum(pos + 1, 0).sum())
+    return 4 * hq * d * total
+
+
+def prefill_cpu_baseline(wl, target_s=15.0):
+    """Oracle prefill (gather + fp64 causal attention) on whole sequences of the
+    workload, one at a time until ~target_s of work is done, on one host core."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import runner
+
+    o = runner.run_prefill(wl, seqs=[])  # setup only: the allocator and the caches
+    done, flops, elapsed = [], 0, 0.0
+    from oracle.prefill import prefill_attention
+    with threadpool_limits(limits=1):
+        for i in range(len(wl.batch)):
+            n = o.chunks[i]
+            q = wl.prefill_queries(wl.batch[i], n)
+            t0 = time.perf_counter()
+            prefill_attention(q, [0, n], o.k_cache, o.v_cache, [o.tables[i]], [o.ctx_lens[i]], wl.block_size,
+                              wl.sm_scale, wl.kv_dtype, wl.k_scale, wl.v_scale)
+            elapsed += time.perf_counter() - t0
+            done.append(i)
+            flops += prefill_flops([o.ctx_lens[i]], [n], wl.num_q_heads, wl.head_dim)
+            if elapsed >= target_s:
+                break
+    return {
+        "value": round(flops / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"gather + fp64 causal attention of {len(done)} of {len(wl.batch)} sequences' chunks "
+                  f"({sum(o.chunks[i] for i in done)} query rows) of one prefill pass, {elapsed:.1f} s on one host core",
+        "query_tokens_per_s": round(sum(o.chunks[i] for i in done) / elapsed, 1),
+    }
+
+
+def bench_prefill(args):
+    """One step = paged_kv_write of every chunk's K/V + paged_attn_prefill over the batch."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_60_amd import _lib, harness, ops
+    _lib.load()
+
+    wl = getattr(workloads, PREFILL_WORKLOADS[args.prefill])()
+    log(f"bench: {wl.name}: setup")
+    eng = harness.make_engine(wl, poison=False)
+    cached = harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
+    q, q_start, chunks = harness.prefill_inputs(wl, cached)
+    tables, ctx = eng.prepare_prefill(wl.batch, wl.max_blocks_per_seq)
+    ctx_h = ctx.cpu().numpy()
+    # the chunks' K/V rows and slots, staged in HBM (re-written each step: same values, same slots)
+    ks, vs, sl = [], [], []
+    ops_by_seq = {o.seq: o for r in wl.setup_rounds for o in r}
+    for s, n in zip(wl.batch, chunks):
+        op = ops_by_seq[s]
+        L = int(ctx_h[wl.batch.index(s)])
+        if op.kind == "prompt":
+            K, V = wl.prompt_kv(op, L - n)
+        else:
+            K, V = wl.op_kv(op)
+            K, V = K[L - n:], V[L - n:]
+        ks.append(K)
+        vs.append(V)
+        sl.append(np.asarray(eng.bm.slots(s, L - n, n), dtype=np.int64))
+    k_new = torch.from_numpy(np.concatenate(ks)).cuda()
+    v_new = torch.from_numpy(np.concatenate(vs)).cuda()
+    slots = torch.from_numpy(np.concatenate(sl)).cuda()
+    del ks, vs
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        ops.paged_kv_write(k_new, v_new, eng.k_cache, eng.v_cache, slots, wl.kv_dtype, wl.k_inv_scale,
+                           wl.v_inv_scale)
+        if ev is not None:
+            ev[0].record()
+        eng.prefill(tables, ctx, q, q_start, out)
+        if ev is not None:
+            ev[1].record()
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    hq, hkv, d = wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    flops = prefill_flops(ctx_h, chunks, hq, d)
+    rows = int(sum(chunks))
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    achieved = flops / attn_s / 1e12
+    value = flops * args.steps / wall / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.kv_dtype == "f16" else "fp8e4m3-kv/f16",
+        "data": "synthetic",
+        "config": {**wl.summary(), "query_rows": rows, "prefix_cache_hit_tokens": int(sum(cached.values())),
+                   "timing": "wall clock per step (write + prefill); roofline from events around the prefill"},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS_F16, 2),
+        "query_tokens_per_s": round(rows * args.steps / wall, 1),
+        "prefill_us": round(attn_s * 1e6, 2),
+        "prefill_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(attn_ms, [10, 50, 90])],
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS_F16,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS_F16, 4),
+            "traffic": None,
+            "kernel": "attn_prefill_kernel",
+            "flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        result["cpu_baseline"] = prefill_cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +329,9 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict L2/MALL between steps (time by events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--prefill", choices=sorted(PREFILL_WORKLOADS),
+                    help="time chunked prefill instead of decode (qwen3: prefix-cache prefill, batch 256; "
+                         "llama2: last-512-token chunks, batch 64)")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one plain 256 MiB device copy (known bytes, for counter scaling)")
     args = ap.parse_args()
@@ -190,6 +340,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
               f"runs on a single GPU", file=sys.stderr)
         sys.exit(2)
+    if args.prefill:
+        bench_prefill(args)
+        return
 
     import torch
 

@@ -180,6 +180,41 @@ int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, i
                               int partition_tokens);
 
 /*
+ * paged_attn_prefill -- chunked (multi-token, causal) attention over the paged
+ * K/V. A request that found its leading blocks in the prefix cache prefills
+ * only the positions that missed ([VRAM] §4.2, §5); a prompt split into chunks
+ * prefills chunk by chunk. Sequence s holds L = ctx_lens[s] tokens (including
+ * the chunk, whose K/V must be in the cache already, e.g. by paged_kv_write);
+ * its n = q_start[s+1] - q_start[s] query rows are the last n positions of
+ * that context, and row i (position p = L - n + i) attends positions 0..p:
+ *   out[r][h] = sum_{t<=p} softmax_t(sm_scale * q[r][h].K_t) V_t.
+ * A row with p < 0 (a chunk longer than its context) is written as zeros.
+ *
+ *   out, q         device, fp16 [total_q][num_q_heads][head_dim]; rows of
+ *                  sequence s at q_start[s] .. q_start[s+1]-1
+ *   block_tables   device, int32 [num_seqs][max_blocks_per_seq], as in
+ *                  paged_attn_decode (entries past ceil(L/bs) never read,
+ *                  ids outside [0, num_blocks) never followed: their tokens
+ *                  are skipped)
+ *   ctx_lens       device, int32 [num_seqs]; clamped to
+ *                  [0, max_blocks_per_seq * block_size]
+ *   q_start        device, int32 [num_seqs + 1], non-decreasing from 0 to
+ *                  total_q; a sequence whose rows fall outside [0, total_q)
+ *                  is skipped (its rows are not written)
+ *   sm_scale, kv_dtype, k_scale, v_scale: as in paged_attn_decode.
+ * No workspace: one workgroup computes 128 (query token, query head) pairs of
+ * one KV head over every position they see, on the matrix cores. Batches of
+ * more than 4096 sequences run as consecutive launches. Shapes as in
+ * paged_attn_decode. Returns PKV_ERR_INVALID for a bad shape or null pointer
+ * (nothing is queued), PKV_ERR_HIP if a launch fails.
+ */
+int paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq, const int32_t* ctx_lens,
+                       const int32_t* q_start, int num_seqs, int total_q, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                       float sm_scale, int kv_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * paged_step_metadata -- bring a decode step's metadata to the device.
  * Copies slot_mapping (int64, n_seqs), ctx_lens (int32, n_seqs) and the
  * copy-on-write pairs (int32, 2*n_cow) from src buffers into dst buffers and

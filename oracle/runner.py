@@ -127,10 +127,19 @@ class PrefillRun:
     cached: dict          # prompt sequence -> tokens found in the prefix cache
     chunks: list          # query rows per batch sequence
     q_start: np.ndarray   # int64 [B + 1]
-    q: np.ndarray         # float16 [total_q, Hq, D]
     tables: list
     ctx_lens: list
-    output: np.ndarray    # float64 [total_q, Hq, D] (NaN rows outside the sample)
+    rows: dict            # batch index -> float64 [chunk, Hq, D] (sampled sequences only)
+
+    @property
+    def output(self) -> np.ndarray:
+        """[total_q, Hq, D] float64, NaN for rows of sequences outside the sample."""
+        first = next(iter(self.rows.values()), None)
+        hq, d = (first.shape[1], first.shape[2]) if first is not None else (0, 0)
+        out = np.full((int(self.q_start[-1]), hq, d), np.nan)
+        for i, r in self.rows.items():
+            out[self.q_start[i]:self.q_start[i + 1]] = r
+        return out
 
 
 def run_prefill(wl, seqs=None) -> PrefillRun:
@@ -149,9 +158,12 @@ def run_prefill(wl, seqs=None) -> PrefillRun:
             cached[op.seq] = c
     chunks = wl.chunk_lengths(cached)
     q_start = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
-    q = np.concatenate([wl.prefill_queries(s, n) for s, n in zip(wl.batch, chunks)])
     tables = [alloc.block_table(s) for s in wl.batch]
     lens = [alloc.num_tokens(s) for s in wl.batch]
-    out = prefill_attention(q, q_start, kc, vc, tables, lens, wl.block_size, wl.sm_scale,
-                            wl.kv_dtype, wl.k_scale, wl.v_scale, seqs=seqs)
-    return PrefillRun(alloc, kc, vc, cached, chunks, q_start, q, tables, lens, out)
+    rows = {}
+    for i in (range(len(wl.batch)) if seqs is None else seqs):
+        s, n = wl.batch[i], chunks[i]
+        q = wl.prefill_queries(s, n)
+        rows[i] = prefill_attention(q, [0, n], kc, vc, [tables[i]], [lens[i]], wl.block_size, wl.sm_scale,
+                                    wl.kv_dtype, wl.k_scale, wl.v_scale)
+    return PrefillRun(alloc, kc, vc, cached, chunks, q_start, tables, lens, rows)

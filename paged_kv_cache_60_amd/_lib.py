@@ -65,6 +65,8 @@ SIGNATURES = {
                                           _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f,
                                           _c_int, _vp, _c_sz, _c_int, _vp]),
     "paged_attn_decode_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "paged_attn_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _vp]),
     "paged_step_metadata": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp,
                                      _c_int, _c_int, _vp]),
     "pkv_bm_create": (_c_int, [_c_int, _c_int, _p_i32, ctypes.POINTER(_vp)]),

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-HIP_SOURCES = ["kv_write.hip", "block_copy.hip", "attn_decode.hip", "step_meta.hip"]
+HIP_SOURCES = ["kv_write.hip", "block_copy.hip", "attn_decode.hip", "attn_prefill.hip", "step_meta.hip"]
 CXX_SOURCES = ["block_manager.cpp"]
 
 ARCH = "gfx950"

@@ -1,0 +1,496 @@
+// paged_attn_prefill: chunked (multi-token, causal) attention over the paged
+// KV cache, on the matrix cores of gfx950.
+//
+// A request whose leading blocks were found in the prefix cache maps them into
+// its block table and prefills only the positions that missed ("Where Did the
+// VRAM Go (KV cache tutorial)", §4.2); a prompt cut into chunks does the same
+// chunk by chunk. Sequence s holds ctx_lens[s] = L tokens, reached through its
+// block table as in decode ("From OOM to Smooth Inference (RAG memory
+// management)", §2.1); its n query rows q[q_start[s] .. q_start[s+1]) are the
+// last n positions of the context, and row i (position p = L - n + i) attends
+// over positions 0..p.
+//
+// Work decomposition. A workgroup (4 waves) owns one tile: 128 query columns
+// of one (sequence, KV head), where a column is one (query token, query head)
+// pair of that KV head's group of G heads -- 128 / G consecutive query tokens.
+// Each wave holds 32 columns (two 16-column MFMA operands). The workgroup walks
+// the tokens the tile can see, 32 at a time (two 16-token tiles, each inside
+// one block): all 256 threads load the chunk's K and V rows from the cache
+// into LDS as fp16 (fp8 rows widened exactly), double-buffered so that the
+// next chunk's loads are in flight while this one is computed, and every wave
+// then runs, per chunk:
+//   S = K . Q^T       v_mfma_f32_16x16x32_f16, M = 16 tokens, N = 16 columns,
+//                     K rows read from LDS in the A layout (no transpose)
+//   online softmax    per column; the accumulator gives lane (column j,
+//                     group g) tokens 4g..4g+3 of each tile, so the column's
+//                     max and sum need only two cross-group shuffles
+//   O^T += V^T . P^T  M = 16 head-dim rows, K-dim = the chunk's 32 tokens; the
+//                     logits of both tiles are exactly the B operand P^T, and
+//                     V^T comes from LDS through ds_read_b64_tr_b16
+// The causal mask and the end of the sequence are applied to the logits (a
+// masked logit is -inf); V rows past the sequence are zero in LDS.
+//
+// Tiles are numbered head-major (KV head h owns tiles [h T, (h+1) T)), and
+// the workgroups that run on one XCD (g, g + 8, ...) take one contiguous range
+// of that numbering, so the K/V of a (sequence, head) is read through one L2.
+// Inside a head the tiles run in reverse order: the last tile of a sequence
+// sees the longest context and starts first.
+//
+// Exponentials are base 2 with log2(e) folded into the logit scale.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "device_common.hpp"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kCols = 32;                 // query columns per wave
+constexpr int kTileCols = kWaves * kCols; // query columns per workgroup
+constexpr int kChunk = 32;                // tokens per step of the token loop
+constexpr int kMaxSeqs = 4096;            // sequences per launch (tile prefix in LDS)
+
+struct PrefillArgs {
+  const f16* q;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  const int32_t* q_start;
+  f16* out;
+  int max_blocks;
+  int B;
+  int Hkv;
+  int Hq;
+  int bs_log2;
+  int num_blocks;
+  int total_q;
+  int tiles_bound;    // tiles per KV head the grid provides (>= the real count)
+  float qk_scale;     // sm_scale * log2(e), times k_scale for fp8
+  float v_out_scale;  // v_scale for fp8, else 1
+};
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
+
+// Query rows of sequence s: [first, first + count), or none if q_start puts
+// them outside [0, total_q).
+__device__ __forceinline__ void seq_rows(const PrefillArgs& a, int s, int* first, int* count) {
+  const int r0 = a.q_start[s];
+  const int r1 = a.q_start[s + 1];
+  const bool ok = r0 >= 0 && r1 >= r0 && r1 <= a.total_q;
+  *first = ok ? r0 : 0;
+  *count = ok ? r1 - r0 : 0;
+}
+
+// pt[0] = 0, pt[s + 1] = pt[s] + tiles of sequence s, in LDS; scan[] is
+// blockDim.x ints of scratch. Ends with a barrier.
+__device__ void build_tile_prefix(const PrefillArgs& a, int G, int* pt, int* scan) {
+  const int n = a.B;
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n; i += T) {
+    int first, count;
+    seq_rows(a, i, &first, &count);
+    pt[i + 1] = (count * G + kTileCols - 1) / kTileCols;
+  }
+  __syncthreads();
+  const int per = (n + T - 1) / T;
+  const int b0 = min(n, tid * per);
+  const int b1 = min(n, b0 + per);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += pt[i + 1];
+  scan[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < T; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int run = scan[tid] - s;
+  for (int i = b0; i < b1; ++i) {
+    run += pt[i + 1];
+    pt[i + 1] = run;
+  }
+  if (tid == 0) pt[0] = 0;
+  __syncthreads();
+}
+
+// The sequence that owns tile t (< pt[B]): the last s with pt[s] <= t.
+__device__ __forceinline__ int find_seq(const int* pt, int B, int t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pt[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Workgroup g runs on XCD g % 8; workgroups g, g + 8, ... get consecutive
+// logical indices, so each XCD takes one contiguous range of tiles.
+__device__ __forceinline__ int logical_index() {
+  const int n = gridDim.x;
+  const int xcd = blockIdx.x % 8;
+  const int q = n / 8, r = n % 8;
+  return xcd * q + min(xcd, r) + (int)(blockIdx.x / 8);
+}
+
+// 8 fp8 bytes (two dwords) -> 8 fp16 values, exactly
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = fp8x2_lo_to_f16x2(w0);
+  r[1] = fp8x2_hi_to_f16x2(w0);
+  r[2] = fp8x2_lo_to_f16x2(w1);
+  r[3] = fp8x2_hi_to_f16x2(w1);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+template <int D, bool FP8>
+struct ChunkShape {
+  static constexpr int ELEM = FP8 ? 1 : 2;
+  static constexpr int RB = D * ELEM;                  // cache bytes of one token row
+  static constexpr int LPR = RB / 16;                  // 16-byte pieces per row
+  static constexpr int PIECES = kChunk * LPR;          // pieces per chunk, per tensor
+  static constexpr int PPT = (PIECES + kWaves * 64 - 1) / (kWaves * 64);  // per thread
+  static constexpr int HPP = 16 / ELEM;                // fp16 values per piece
+  static constexpr int KS = D + 8;                     // LDS row stride of K, halves
+  static constexpr int VS = D + 16;                    // LDS row stride of V, halves
+  static constexpr int BUF = kChunk * (KS + VS);       // halves per buffer (K then V)
+};
+
+// The chunk's K and V pieces that this thread moves: global -> registers.
+template <int D, bool FP8>
+struct Stage {
+  using S = ChunkShape<D, FP8>;
+  u32x4 k[S::PPT];
+  u32x4 v[S::PPT];
+
+  __device__ __forceinline__ void load(const PrefillArgs& a, const int32_t* tab, const uint8_t* kc_head,
+                                       const uint8_t* vc_head, size_t blk_stride, int t0, int L) {
+#pragma unroll
+    for (int i = 0; i < S::PPT; ++i) {
+      const int p = threadIdx.x + i * kWaves * 64;
+      const int r = p / S::LPR;
+      const int t = t0 + r;
+      int blk = -1;
+      if (p < S::PIECES && t < L) blk = tab[t >> a.bs_log2];
+      if ((unsigned)blk < (unsigned)a.num_blocks) {
+        const size_t off = (size_t)blk * blk_stride + (size_t)(t & ((1 << a.bs_log2) - 1)) * S::RB +
+                           (p % S::LPR) * 16;
+        k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off));
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc_head + off));
+      } else {
+        k[i] = u32x4{0u, 0u, 0u, 0u};
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // registers -> LDS buffer as fp16 rows (rows past the end were loaded as zeros)
+  __device__ __forceinline__ void store(_Float16* buf) const {
+#pragma unroll
+    for (int i = 0; i < S::PPT; ++i) {
+      const int p = threadIdx.x + i * kWaves * 64;
+      if (p >= S::PIECES) continue;
+      const int r = p / S::LPR;
+      const int h = (p % S::LPR) * S::HPP;
+      _Float16* kd = buf + r * S::KS + h;
+      _Float16* vd = buf + kChunk * S::KS + r * S::VS + h;
+      if constexpr (FP8) {
+        *reinterpret_cast<f16x8*>(kd) = fp8x8_to_f16x8(k[i][0], k[i][1]);
+        *reinterpret_cast<f16x8*>(kd + 8) = fp8x8_to_f16x8(k[i][2], k[i][3]);
+        *reinterpret_cast<f16x8*>(vd) = fp8x8_to_f16x8(v[i][0], v[i][1]);
+        *reinterpret_cast<f16x8*>(vd + 8) = fp8x8_to_f16x8(v[i][2], v[i][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(kd) = k[i];
+        *reinterpret_cast<u32x4*>(vd) = v[i];
+      }
+    }
+  }
+};
+
+template <int D, int G, bool FP8>
+__global__ void __launch_bounds__(kWaves * 64) attn_prefill_kernel(PrefillArgs a) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  static_assert(D == 64 || D == 128, "head_dim");
+  using S = ChunkShape<D, FP8>;
+  constexpr int KM = D / 32;   // q.k MFMAs per 16-token tile and column group
+  constexpr int NT = D / 16;   // output head-dim tiles
+  constexpr int DQ = D / 4;    // head-dim elements per lane group in the q.k operands
+  constexpr int QT = kTileCols / G;  // query tokens per workgroup tile
+  static_assert(2 * S::BUF * 2 >= (kMaxSeqs + 1 + kWaves * 64) * 4, "the tile prefix fits in the K/V buffers");
+
+  // two K/V chunk buffers; before the token loop the same memory holds the tile prefix
+  __shared__ __align__(16) _Float16 lds[2 * S::BUF];
+  int* pt = reinterpret_cast<int*>(lds);
+  build_tile_prefix(a, G, pt, pt + a.B + 1);
+
+  const int total_tiles = pt[a.B];
+  const int li = logical_index();
+  const int head = li / a.tiles_bound;
+  const int tr = li - head * a.tiles_bound;
+  if (head >= a.Hkv || tr >= total_tiles) return;  // uniform over the workgroup
+  const int tile = total_tiles - 1 - tr;            // longest contexts first
+  const int seq = find_seq(pt, a.B, tile);
+  const int k_tile = tile - pt[seq];
+  __syncthreads();  // the prefix is dead from here on; the buffers take over
+
+  int qfirst, n;
+  seq_rows(a, seq, &qfirst, &n);
+  const int L = min(max(a.ctx_lens[seq], 0), a.max_blocks << a.bs_log2);
+  const int row0 = k_tile * QT;             // first query token of the tile, within the chunk
+  const int nt = min(QT, n - row0);         // query tokens in this tile
+  const int pos0 = L - n + row0;            // position of the tile's first query token
+  const int kend = min(L, pos0 + nt);       // tokens the tile can see: [0, kend)
+  const int nchunks = kend > 0 ? (kend + kChunk - 1) / kChunk : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // Q^T operands (B of S = K Q^T): column c = 32 wave + 16 cg + col holds query
+  // token c / G, head c % G of the group; d = grp * DQ + 8 m + slot
+  f16x8 qb[2][KM];
+  int qpos[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    const int c = wave * kCols + cg * 16 + col;
+    const int tl = c / G;
+    const bool live = tl < nt;
+    qpos[cg] = live ? pos0 + tl : -1;  // -1: every token is masked
+    const size_t qoff = live ? ((size_t)(qfirst + row0 + tl) * a.Hq + head * G + c % G) * D + grp * DQ : 0;
+#pragma unroll
+    for (int m = 0; m < KM; ++m)
+      qb[cg][m] = live ? *reinterpret_cast<const f16x8*>(a.q + qoff + 8 * m) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const bool all_live = nt == QT;
+
+  f32x4 o[2][NT];
+  float m_run[2], l_part[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) o[cg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[cg] = -INFINITY;
+    l_part[cg] = 0.0f;
+  }
+
+  const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
+  const size_t head_bytes = (size_t)S::RB << a.bs_log2;
+  const size_t blk_stride = (size_t)a.Hkv * head_bytes;
+  const uint8_t* kc_head = a.kc + (size_t)head * head_bytes;
+  const uint8_t* vc_head = a.vc + (size_t)head * head_bytes;
+
+  // tr16 read addresses for V^T (A operand of O^T += V^T P^T): lane 16g + 4e +
+  // mm names row 4g + e (tile a) or 16 + 4g + e (tile b), elements 16c + 4mm .. +3
+  const int tr_row = 4 * grp + (col >> 2);
+  const int tr_col = 4 * (col & 3);
+
+  Stage<D, FP8> st;
+  if (nchunks > 0) {
+    st.load(a, tab, kc_head, vc_head, blk_stride, 0, kend);
+    st.store(lds);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < nchunks; ++j) {
+    const int t0 = j * kChunk;
+    _Float16* buf = lds + (j & 1) * S::BUF;
+    if (j + 1 < nchunks) st.load(a, tab, kc_head, vc_head, blk_stride, t0 + kChunk, kend);
+
+    // blocks of the two tiles (wave-uniform): tokens of a block outside the pool are skipped
+    const int ba = wave_uniform(tab[t0 >> a.bs_log2]);
+    const int bb = t0 + 16 < kend ? wave_uniform(tab[(t0 + 16) >> a.bs_log2]) : -1;
+    const bool ok_a = (unsigned)ba < (unsigned)a.num_blocks;
+    const bool ok_b = (unsigned)bb < (unsigned)a.num_blocks;
+
+    // S = K . Q^T for both tiles and both column groups
+    f32x4 s[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) s[tt][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const _Float16* krow = buf + (16 * tt + col) * S::KS + grp * DQ;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 8 * m);
+        s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[0][m], s[tt][0], 0, 0, 0);
+        s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[1][m], s[tt][1], 0, 0, 0);
+      }
+    }
+
+    // online softmax per column; lane (col, grp) sees tokens t0 + 4grp + v and t0 + 16 + 4grp + v
+    const bool plain = all_live && ok_a && ok_b && t0 + kChunk - 1 <= pos0;
+    f16x8 pb[2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      float z[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        z[v] = s[0][cg][v] * a.qk_scale;
+        z[4 + v] = s[1][cg][v] * a.qk_scale;
+      }
+      if (!plain) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ta = t0 + 4 * grp + v;
+          const int tb = t0 + 16 + 4 * grp + v;
+          z[v] = (ok_a && ta <= qpos[cg]) ? z[v] : -INFINITY;
+          z[4 + v] = (ok_b && tb <= qpos[cg]) ? z[4 + v] : -INFINITY;
+        }
+      }
+      float mt = z[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
+      mt = fmaxf(mt, shfl_xor_f32(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f32(mt, 32));
+      const float mn = fmaxf(m_run[cg], mt);
+      const float ms = safe_max(mn);
+      const float alpha = fast_exp2(m_run[cg] - ms);
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(z[i] - ms);
+        ps += p;
+        pb[cg][i] = (_Float16)p;
+      }
+      l_part[cg] = l_part[cg] * alpha + ps;
+      m_run[cg] = mn;
+#pragma unroll
+      for (int c = 0; c < NT; ++c) o[cg][c] *= alpha;
+    }
+
+    // O^T += V^T . P^T, one 16-row head-dim tile at a time
+    const _Float16* vbuf = buf + kChunk * S::KS;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const _Float16* p1 = vbuf + tr_row * S::VS + 16 * c + tr_col;
+      const _Float16* p2 = vbuf + (16 + tr_row) * S::VS + 16 * c + tr_col;
+      const f16x4 r1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
+      const f16x4 r2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2)));
+      const f16x8 va = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[0], o[0][c], 0, 0, 0);
+      o[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[1], o[1][c], 0, 0, 0);
+    }
+
+    if (j + 1 < nchunks) st.store(lds + ((j + 1) & 1) * S::BUF);
+    __syncthreads();
+  }
+
+  // per-column sums over the four lane groups (the max is already common);
+  // lane (col, grp) holds d = 16c + 4grp + v of its column
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    float l = l_part[cg];
+    l += shfl_xor_f32(l, 16);
+    l += shfl_xor_f32(l, 32);
+    const int c = wave * kCols + cg * 16 + col;
+    const int tl = c / G;
+    if (tl < nt) {
+      const float sc = l > 0.0f ? a.v_out_scale / l : 0.0f;
+      f16* orow = a.out + ((size_t)(qfirst + row0 + tl) * a.Hq + head * G + c % G) * D + 4 * grp;
+#pragma unroll
+      for (int cc = 0; cc < NT; ++cc) {
+        f16x4 h;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[v] = (f16)(o[cg][cc][v] * sc);
+        *reinterpret_cast<f16x4*>(orow + 16 * cc) = h;
+      }
+    }
+  }
+}
+
+typedef void (*PrefillFn)(PrefillArgs);
+
+template <int D, bool FP8>
+PrefillFn pick_d(int G) {
+  switch (G) {
+    case 1: return attn_prefill_kernel<D, 1, FP8>;
+    case 2: return attn_prefill_kernel<D, 2, FP8>;
+    case 4: return attn_prefill_kernel<D, 4, FP8>;
+    case 8: return attn_prefill_kernel<D, 8, FP8>;
+    default: return nullptr;
+  }
+}
+
+PrefillFn pick(int D, int G, bool fp8) {
+  if (D == 64) return fp8 ? pick_d<64, true>(G) : pick_d<64, false>(G);
+  if (D == 128) return fp8 ? pick_d<128, true>(G) : pick_d<128, false>(G);
+  return nullptr;
+}
+
+int log2_exact(int v) {
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return (1 << k) == v ? k : -1;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* ctx_lens, const int32_t* q_start, int num_seqs,
+                                  int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float sm_scale, int kv_dtype,
+                                  float k_scale, float v_scale, void* stream) {
+  using namespace pkv;
+  if (num_seqs < 0 || total_q < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0)
+    return PKV_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
+  const int G = num_q_heads / num_kv_heads;
+  PrefillFn fn = pick(head_dim, G, kv_dtype == PKV_KV_FP8_E4M3);
+  if (!fn) return PKV_ERR_INVALID;
+  if ((int64_t)max_blocks_per_seq * block_size > 0x7FFFFFFF) return PKV_ERR_INVALID;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !q_start) return PKV_ERR_INVALID;
+
+  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
+  const float kLog2e = 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b0 = 0; b0 < num_seqs; b0 += kMaxSeqs) {
+    const int B = num_seqs - b0 < kMaxSeqs ? num_seqs - b0 : kMaxSeqs;
+    // tiles of one KV head: sum over sequences of ceil(n_s G / 128) <= total_q G / 128 + B
+    const int64_t tiles = ((int64_t)total_q * G + kTileCols - 1) / kTileCols + B;
+    const int64_t grid = tiles * num_kv_heads;
+    if (grid > 0x7FFFFFFF) return PKV_ERR_INVALID;
+    PrefillArgs a;
+    a.q = static_cast<const f16*>(q);
+    a.kc = static_cast<const uint8_t*>(k_cache);
+    a.vc = static_cast<const uint8_t*>(v_cache);
+    a.tables = block_tables + (size_t)b0 * max_blocks_per_seq;
+    a.ctx_lens = ctx_lens + b0;
+    a.q_start = q_start + b0;
+    a.out = static_cast<f16*>(out);
+    a.max_blocks = max_blocks_per_seq;
+    a.B = B;
+    a.Hkv = num_kv_heads;
+    a.Hq = num_q_heads;
+    a.bs_log2 = log2_exact(block_size);
+    a.num_blocks = num_blocks;
+    a.total_q = total_q;
+    a.tiles_bound = (int)tiles;
+    a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
+    a.v_out_scale = fp8 ? v_scale : 1.0f;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}

@@ -222,6 +222,22 @@ class PagedKVEngine:
         self.device_step(slot, n_cow, n_upd, k_new, v_new, q, out)
         return n_cow
 
+    # ------------------------------------------------------ prefill
+    def prepare_prefill(self, batch_seqs, max_blocks):
+        """Device block tables and context lengths of a prefill batch, read
+        from the block manager (each sequence's chunk K/V must be written)."""
+        B = len(batch_seqs)
+        seqs = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
+        tab = np.empty((B, int(max_blocks)), dtype=np.int32)
+        ctx = np.empty(B, dtype=np.int32)
+        self.bm.export(seqs, tab, ctx)
+        return torch.from_numpy(tab).to(self.device), torch.from_numpy(ctx).to(self.device)
+
+    def prefill(self, tables_dev, ctx_dev, q, q_start_dev, out):
+        """Chunked causal prefill attention for the batch (paged_attn_prefill)."""
+        ops.paged_attn_prefill(out, q, self.k_cache, self.v_cache, tables_dev, ctx_dev, q_start_dev,
+                               1.0 / float(self.d) ** 0.5, self.kv_dtype, self.k_scale, self.v_scale)
+
     def host_tables(self):
         """(tables [B, maxb], ctx [B]) of the current batch, read back from the manager."""
         B = len(self.batch)

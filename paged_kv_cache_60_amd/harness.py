@@ -8,9 +8,12 @@ block copies, then writes the round's new tokens (in chunks of at most
 order in which a serving loop would issue them.
 
 The script object is duck-typed: it needs ``setup_rounds``, ``round_kv(ops)``,
-``step_ops(i)``, ``queries(i)`` and the shape attributes used below.
+``step_ops(i)``, ``queries(i)`` (decode) or ``chunk_lengths`` and
+``prefill_queries`` (prefill) and the shape attributes used below.
 """
 from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -27,9 +30,13 @@ def make_engine(wl, device="cuda", poison=True) -> PagedKVEngine:
 def replay_round(eng: PagedKVEngine, wl, ops, chunk_tokens: int = 1 << 18):
     slots, pairs, prompts = eng.apply_ops(ops)
     eng.copy_blocks(pairs)
-    for op, c, sl in prompts:  # rows after the cached blocks only
-        K, V = wl.prompt_kv(op, c)
-        eng.write(sl, K, V)
+    # rows after the cached blocks only; the draws run in threads (the
+    # generator releases the GIL), a bounded number of prompts at a time
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for g0 in range(0, len(prompts), 32):
+            group = prompts[g0:g0 + 32]
+            for (op, c, sl), (K, V) in zip(group, ex.map(lambda p: wl.prompt_kv(p[0], p[1]), group)):
+                eng.write(sl, K, V)
     creating = [o for o in ops if o.kind in ("allocate", "append") and o.n > 0]
     pos = i = 0
     while i < len(creating):
@@ -43,13 +50,43 @@ def replay_round(eng: PagedKVEngine, wl, ops, chunk_tokens: int = 1 << 18):
         eng.write(slots[pos:pos + acc], K, V)
         pos += acc
     assert pos == len(slots)
-    return slots, pairs
+    return slots, pairs, prompts
 
 
-def replay_setup(eng: PagedKVEngine, wl, chunk_tokens: int = 1 << 18):
+def replay_setup(eng: PagedKVEngine, wl, chunk_tokens: int = 1 << 18) -> dict:
+    """Replay the setup rounds; returns {prompt seq: tokens found in the prefix cache}."""
+    cached = {}
     for ops in wl.setup_rounds:
-        replay_round(eng, wl, ops, chunk_tokens)
+        _, _, prompts = replay_round(eng, wl, ops, chunk_tokens)
+        for op, c, _ in prompts:
+            cached[op.seq] = int(c)
     torch.cuda.synchronize()
+    return cached
+
+
+def prefill_inputs(wl, cached, device="cuda"):
+    """(q [total_q, Hq, D] fp16, q_start [B + 1] int32, chunk lengths) on device
+    for a prefill run after the setup."""
+    chunks = wl.chunk_lengths(cached)
+    q_start = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = np.empty((int(q_start[-1]), wl.num_q_heads, wl.head_dim), dtype=np.float16)
+
+    def fill(i):
+        q[q_start[i]:q_start[i + 1]] = wl.prefill_queries(wl.batch[i], chunks[i])
+
+    with ThreadPoolExecutor(max_workers=8) as ex:  # the generator releases the GIL
+        list(ex.map(fill, range(len(chunks))))
+    return torch.from_numpy(q).to(device), torch.from_numpy(q_start).to(device), chunks
+
+
+def run_prefill(eng: PagedKVEngine, wl, cached, device="cuda"):
+    """One prefill pass over every batch sequence's chunk; returns (out on
+    device, q_start host array, host tables, host context lengths)."""
+    q, q_start, chunks = prefill_inputs(wl, cached, device)
+    tables, ctx = eng.prepare_prefill(wl.batch, wl.max_blocks_per_seq)
+    out = torch.empty_like(q)
+    eng.prefill(tables, ctx, q, q_start, out)
+    return out, q_start.cpu().numpy(), tables.cpu().numpy(), ctx.cpu().numpy()
 
 
 def step_inputs(wl, step, device="cuda"):

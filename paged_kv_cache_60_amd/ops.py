@@ -168,6 +168,32 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
                                        _stream_ptr(stream)), w)
 
 
+def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, sm_scale, kv_dtype=F16,
+                       k_scale=1.0, v_scale=1.0, stream=None):
+    """Chunked causal prefill. out/q [total_q, Hq, D] fp16; block_tables [B, max_blocks] int32;
+    ctx_lens [B] int32 (context including the chunk); q_start [B + 1] int32 (row offsets)."""
+    w = "paged_attn_prefill"
+    _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
+    _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype) and k_cache.shape == v_cache.shape,
+             w, "caches")
+    total, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _require(d == d2, w, "head_dim")
+    _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.is_contiguous(), w, "block_tables")
+    B = block_tables.shape[0]
+    _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
+             and ctx_lens.is_contiguous(), w, "ctx_lens")
+    _require(q_start.is_cuda and q_start.dtype == torch.int32 and q_start.shape == (B + 1,)
+             and q_start.is_contiguous(), w, "q_start")
+    lib = _lib.load()
+    check(lib.paged_attn_prefill(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                 block_tables.shape[1], _p(ctx_lens), _p(q_start), B, total, hq, hkv, d, bs,
+                                 nb, float(sm_scale), kv_dtype_code(kv_dtype), float(k_scale), float(v_scale),
+                                 _stream_ptr(stream)), w)
+
+
 def paged_step_metadata(slots_src, slots_dst, ctx_src, ctx_dst, n_seqs, cow_src, cow_dst, n_cow,
                         updates_src, n_updates, block_tables, stream=None):
     """Apply a decode step's metadata (sources: pinned host tensors or device tensors)."""
