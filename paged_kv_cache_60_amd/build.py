@@ -31,6 +31,10 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# per-source extra flags: the prefill kernel keeps its matrix-core accumulators
+# in ordinary VGPRs (the accumulator-register form made the compiler copy all 64
+# output accumulators out and back on every iteration of the token loop)
+HIP_EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
@@ -49,7 +53,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
         jobs.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
