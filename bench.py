@@ -47,12 +47,13 @@ EVENT_EVERY = 5  # timed steps per pass-1 event pair
 
 
 KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "device_common.hpp")
+PREFILL_SOURCES = ("attn_prefill.hip", "device_common.hpp")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     """sha256[:16] over the sources the attention kernels are built from."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "paged_kv_cache_60_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -157,16 +158,17 @@ def cpu_baseline(wl, target_s=15.0):
     }
 
 
-def load_counters(config_name):
-    """HBM bytes per pass-1 launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def load_counters(config_name, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
     try:
         with open(PROFILE_COUNTERS) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     entry = data.get(config_name)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -307,7 +309,7 @@ def bench_prefill(args):
             "peak": PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS_F16, 4),
-            "traffic": None,
+            "traffic": load_counters(wl.name, PREFILL_SOURCES),
             "kernel": "attn_prefill_kernel",
             "flops_per_launch": flops,
         },
@@ -340,10 +342,6 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
               f"runs on a single GPU", file=sys.stderr)
         sys.exit(2)
-    if args.prefill:
-        bench_prefill(args)
-        return
-
     import torch
 
     import workloads
@@ -361,6 +359,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.prefill:
+        bench_prefill(args)
+        return
 
     total_steps = args.warmup + args.steps
     wl = workloads.make(args.config, max_steps=total_steps + 1)
