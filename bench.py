@@ -320,6 +320,85 @@ def bench_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+SWAP_METRIC = "preemption by swapping: paged_block_swap bus GB/s (device <-> pinned host), per direction"
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args):
+    """Time paged_block_swap on the preemption workload: the 16 newest sequences
+    of the Llama-2-7B batch (their whole K/V) copied to the pinned host pool
+    (out) and back (in); each timed step is one out and one in."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_60_amd import _lib, harness, ops
+    _lib.load()
+
+    wl = workloads.llama2_7b_preempt("swap")
+    log(f"bench: {wl.name}: setup")
+    eng = harness.make_engine(wl, poison=False)
+    harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
+    tail = wl.meta["preempted"]
+    dev = []
+    for s_ in tail:
+        dev += eng.bm.block_table(s_)
+    n = len(dev)
+    assert n == wl.num_host_blocks
+    out_pairs = torch.tensor([[b, h] for h, b in enumerate(dev)], dtype=torch.int32, device="cuda")
+    in_pairs = torch.tensor([[h, b] for h, b in enumerate(dev)], dtype=torch.int32, device="cuda")
+    nbytes = 2 * n * eng.block_bytes  # K and V
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        ops.paged_block_swap(eng.k_cache, eng.v_cache, eng.k_host, eng.v_host, out_pairs, "out")
+        ops.paged_block_swap(eng.k_cache, eng.v_cache, eng.k_host, eng.v_host, in_pairs, "in")
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        ops.paged_block_swap(eng.k_cache, eng.v_cache, eng.k_host, eng.v_host, out_pairs, "out")
+        e[1].record()
+        ops.paged_block_swap(eng.k_cache, eng.v_cache, eng.k_host, eng.v_host, in_pairs, "in")
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_out = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    t_in = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / 1e3
+    value = 2 * nbytes * args.steps / wall / 1e9
+    best = max(nbytes / t_out, nbytes / t_in) / 1e9
+    result = {
+        "metric": SWAP_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "swapped_sequences": len(tail), "blocks": n,
+                   "bytes_per_direction": nbytes, "block_bytes": eng.block_bytes,
+                   "timing": "wall clock of out + in per step; per direction from events"},
+        "swap_out_gbs": round(nbytes / t_out / 1e9, 2),
+        "swap_in_gbs": round(nbytes / t_in / 1e9, 2),
+        "swap_out_us": round(t_out * 1e6, 1),
+        "swap_in_us": round(t_in * 1e6, 1),
+        "roofline": {
+            "bound": "pcie",
+            "achieved": round(best, 2),
+            "peak": PCIE_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(best / PCIE_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "block_swap_kernel",
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,6 +413,8 @@ def main():
     ap.add_argument("--prefill", choices=sorted(PREFILL_WORKLOADS),
                     help="time chunked prefill instead of decode (qwen3: prefix-cache prefill, batch 256; "
                          "llama2: last-512-token chunks, batch 64)")
+    ap.add_argument("--swap", action="store_true",
+                    help="time paged_block_swap (preemption by swapping, 16 sequences of the Llama-2-7B batch)")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one plain 256 MiB device copy (known bytes, for counter scaling)")
     args = ap.parse_args()
@@ -361,6 +442,9 @@ def main():
         del a, b
     if args.prefill:
         bench_prefill(args)
+        return
+    if args.swap:
+        bench_swap(args)
         return
 
     total_steps = args.warmup + args.steps

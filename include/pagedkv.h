@@ -49,6 +49,10 @@ typedef enum {
 
 typedef enum { PKV_KV_F16 = 0, PKV_KV_FP8_E4M3 = 1 } pkv_kv_dtype;
 
+typedef enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 } pkv_swap_dir;
+
+typedef enum { PKV_PREEMPT_RECOMPUTE = 0, PKV_PREEMPT_SWAP = 1 } pkv_preempt_mode;
+
 /* Human-readable name of a status code (static string). */
 const char* pkv_status_str(int status);
 
@@ -108,6 +112,30 @@ int paged_kv_write_step(const void* k_new, const void* v_new, void* k_cache, voi
  */
 int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                      int num_blocks, size_t block_bytes, void* stream);
+
+/*
+ * paged_block_swap -- whole-block copies between the device caches and a host
+ * pool of the same layout, for preemption by swapping: a preempted request's
+ * blocks are copied to CPU memory and back ([VRAM] §7.1-7.2; [OOM] §5 swap
+ * versus recompute; [VLLM] §3.4 swap space). Pairs come from
+ * pkv_bm_swap_out / pkv_bm_swap_in / pkv_bm_preempt_tail.
+ *
+ *   k_cache/v_cache device caches [num_blocks][Hkv][bs][D]
+ *   k_host/v_host   pinned host memory (hipHostMalloc) of the same layout,
+ *                   [num_host_blocks][Hkv][bs][D], read or written by the
+ *                   kernel directly over the bus
+ *   pairs           int32 [num_pairs][2], device or pinned host memory:
+ *                   PKV_SWAP_OUT: (device block, host block), host <- device;
+ *                   PKV_SWAP_IN:  (host block, device block), device <- host.
+ *                   A pair with an id out of range is skipped.
+ *   block_bytes     bytes of one block of one cache, a multiple of 16.
+ * No destination may appear twice. Copies are ordered on `stream` like any
+ * kernel: queue a swap-out before anything that writes the released device
+ * blocks, and a swap-in before anything that reads the sequences.
+ */
+int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, const int32_t* pairs,
+                     int num_pairs, int num_blocks, int num_host_blocks, size_t block_bytes, int direction,
+                     void* stream);
 
 /*
  * paged_attn_decode -- one query token per sequence attends over its paged
@@ -263,6 +291,9 @@ typedef struct {
   int32_t cached_blocks;       /* holding a prefix-cache key                 */
   int64_t prefix_query_tokens; /* tokens passed to pkv_bm_allocate_prompt    */
   int64_t prefix_hit_tokens;   /* of those, found in the cache               */
+  int32_t host_blocks;         /* host pool size (pkv_bm_set_host_blocks)    */
+  int32_t host_free_blocks;    /* in the host pool's free queue              */
+  int32_t swapped_seqs;        /* sequences swapped out to the host pool     */
 } pkv_bm_stats_t;
 
 /* New manager over blocks 0..num_blocks-1. free_order (host, may be NULL =
@@ -329,6 +360,61 @@ int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst);
  * takes a block's cached descendants before the block). [OOM] §2.3,
  * [ENGINE] §3, [VLLM] §3.2, [VRAM] §4.3-4.4. */
 int pkv_bm_free(pkv_bm* bm, int64_t seq);
+
+/* ----------------------------------------------------------------------
+ * Preemption and swapping ([VRAM] §7.1-7.2: when no new KV block can be had,
+ * running requests are preempted from the tail of the running set, newest
+ * first; recompute drops their cache and prefills them again later, swap
+ * copies their blocks to CPU memory and back; [OOM] §5; [VLLM] §3.4).
+ * A swapped-out sequence is not resident: calls that need its blocks on the
+ * device return NO_SEQ, its id stays taken (EXISTS) and pkv_bm_free releases
+ * its host blocks. Prefix-cache keys do not travel with swapped data.
+ * ---------------------------------------------------------------------- */
+
+/* Host pool of num_host_blocks blocks, ids 0..n-1 in a FIFO queue. INVALID
+ * while any sequence is swapped out. */
+int pkv_bm_set_host_blocks(pkv_bm* bm, int num_host_blocks);
+
+/* Swap a group of resident sequences out. Every distinct device block of the
+ * group, in order of first appearance (sequences in the order given, tables
+ * in order), takes one host block from the front of the host queue, and
+ * pairs_out[2*i], pairs_out[2*i+1] = (device block, host block) for
+ * paged_block_swap(PKV_SWAP_OUT); a block the group's sequences share is
+ * copied once. Each sequence then releases its device blocks as pkv_bm_free
+ * does (a block still held by a sequence outside the group stays resident).
+ * cap = room for pairs in pairs_out (pairs, not ints). OOM (nothing changed)
+ * if the host queue is too short; NO_SEQ if a sequence is not resident;
+ * INVALID for a duplicate id or a short cap. */
+int pkv_bm_swap_out(pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* pairs_out, int cap, int* n_pairs);
+
+/* Swap a group of swapped-out sequences back in: every distinct host block,
+ * in order of first appearance, takes a fresh device block (the free queue,
+ * then the oldest evictable cached block) and pairs_out gets (host block,
+ * device block) for paged_block_swap(PKV_SWAP_IN); host blocks whose count
+ * reaches 0 go to the back of the host queue. OOM (nothing changed) if too
+ * few device blocks are available. */
+int pkv_bm_swap_in(pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* pairs_out, int cap, int* n_pairs);
+
+/* Preempt from the tail of running[0..n_running) (index n_running-1 first)
+ * until the blocks a new allocation can take (free + evictable) reach
+ * blocks_needed, counting only the device blocks each victim would actually
+ * release. victims_out (room for n_running ids) gets the victims in order,
+ * *n_victims their count. PKV_PREEMPT_RECOMPUTE frees them (their requests
+ * are prefilled again later); PKV_PREEMPT_SWAP swaps them out as one group
+ * (pairs_out / cap / *n_pairs as in pkv_bm_swap_out). No victim if enough
+ * blocks are available already. OOM (nothing changed) if every listed
+ * sequence together does not release enough, or the host pool is too small;
+ * on any error the outputs are unspecified and the state unchanged. */
+int pkv_bm_preempt_tail(pkv_bm* bm, const int64_t* running, int n_running, int blocks_needed, int mode,
+                        int64_t* victims_out, int* n_victims, int32_t* pairs_out, int cap, int* n_pairs);
+
+/* A swapped-out sequence's host block table and token count. NO_SEQ if the
+ * sequence is not swapped out. */
+int pkv_bm_swapped_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* n);
+int pkv_bm_swapped_tokens(const pkv_bm* bm, int64_t seq, int* n);
+/* The host pool's free queue (front first) and a host block's refcount. */
+int pkv_bm_host_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n);
+int pkv_bm_host_refcount(const pkv_bm* bm, int32_t host_block, int* rc);
 
 /* Queries. Arrays are host buffers of `cap` entries; *n gets the count. */
 int pkv_bm_slots(const pkv_bm* bm, int64_t seq, int start, int n, int64_t* out);

@@ -66,7 +66,41 @@ Readings taken where the pages are silent or garbled (each is tested):
       evictable list always holds a block's cached descendants before it and
       eviction removes children before parents (no key can name a parent
       block that was reused for other content).
+  * "Where Did the VRAM Go (KV cache tutorial)", §7.1-7.2, and "From OOM to
+    Smooth Inference", §5: when no new KV block can be had, running requests
+    are preempted from the tail of the running set (the newest first) and
+    their blocks released; a preempted request either drops its cache and is
+    prefilled again later (recompute) or has its blocks copied to CPU memory
+    and back (swap). "vLLM Architecture and Memory Use, ch. 3", §3.4: swap
+    space in CPU memory for inactive blocks.
+  R13 Host pool. set_host_blocks(n) gives host block ids 0..n-1 in a FIFO
+      queue (ascending), allowed while nothing is swapped out.
+  R14 swap_out(seqs) moves a group of resident sequences to host blocks. Every
+      distinct device block of the group, in order of first appearance (the
+      sequences in the order given, each table in order), gets one host block
+      from the front of the host queue and one (device, host) pair to copy;
+      a block the group's sequences share is copied once and its host block
+      counts one reference per sharer. Then each sequence, in order, releases
+      its device blocks exactly as free() does and keeps its token count and
+      a table of host blocks. A device block still held by a sequence outside
+      the group stays resident. Prefix-cache keys do not travel with the data.
+  R15 swap_in(seqs) is the reverse: every distinct host block, in order of
+      first appearance, gets a fresh device block (free queue, then the oldest
+      evictable block) and one (host, device) pair; each sequence in order
+      takes its device table and releases its host blocks (a host block whose
+      count reaches zero goes to the back of the host queue).
+  R16 A swapped-out sequence is not resident: calls that need its blocks on
+      the device fail with NO_SEQ, its id stays taken (EXISTS), and free()
+      releases its host blocks.
+  R17 preempt_tail(running, need, mode) walks the running list from its tail
+      (newest first) and picks victims until the blocks a new allocation can
+      take (free + evictable) would reach `need`, counting only the device
+      blocks each victim would actually release. mode "recompute" frees the
+      victims (their requests are prefilled again later); mode "swap" swaps
+      them out as one group. If even every listed sequence is not enough (or,
+      for swap, the host pool is too small) nothing changes (OOM).
 """
+
 from __future__ import annotations
 
 from collections import deque
@@ -119,6 +153,12 @@ class BlockAllocatorModel:
         self.evictable: deque = deque()
         self.prefix_query_tokens = 0
         self.prefix_hit_tokens = 0
+        # host pool for swapped-out sequences (R13-R16)
+        self.num_host_blocks = 0
+        self.host_free: deque = deque()
+        self.host_ref: list = []
+        self.host_tables: dict[int, list[int]] = {}
+        self.host_counts: dict[int, int] = {}
 
     # ----------------------------------------------------------- helpers
     def _needed(self, tokens: int) -> int:
@@ -143,6 +183,9 @@ class BlockAllocatorModel:
                 out.append(b)
         return out
 
+    def _taken(self, seq: int) -> bool:
+        return seq in self.tables or seq in self.host_tables
+
     def _require(self, seq: int):
         if seq not in self.tables:
             raise AllocError(ERR_NO_SEQ, f"sequence {seq} does not exist")
@@ -155,7 +198,7 @@ class BlockAllocatorModel:
         """New sequence holding num_tokens tokens; returns their slots."""
         if num_tokens < 0:
             raise AllocError(ERR_INVALID, "negative token count")
-        if seq in self.tables:
+        if self._taken(seq):
             raise AllocError(ERR_EXISTS, f"sequence {seq} exists")
         blocks = self._pop(self._needed(num_tokens))
         for b in blocks:
@@ -194,7 +237,7 @@ class BlockAllocatorModel:
     def fork(self, parent: int, child: int) -> None:
         """child shares every block of parent (R7)."""
         self._require(parent)
-        if child in self.tables:
+        if self._taken(child):
             raise AllocError(ERR_EXISTS, f"sequence {child} exists")
         table = list(self.tables[parent])
         for b in table:
@@ -205,7 +248,7 @@ class BlockAllocatorModel:
     def share_prefix(self, src: int, num_blocks: int, dst: int) -> None:
         """dst's table is src's first num_blocks blocks (R6)."""
         self._require(src)
-        if dst in self.tables:
+        if self._taken(dst):
             raise AllocError(ERR_EXISTS, f"sequence {dst} exists")
         table = self.tables[src]
         if num_blocks < 0 or num_blocks > len(table):
@@ -219,9 +262,16 @@ class BlockAllocatorModel:
     def free_seq(self, seq: int) -> None:
         """Release seq's blocks in table order (R8); cached blocks reaching zero
         join the evictable list deepest first (R12)."""
+        if seq in self.host_tables:  # R16: a swapped-out sequence releases its host blocks
+            self._release_host(self.host_tables.pop(seq))
+            del self.host_counts[seq]
+            return
         self._require(seq)
-        table = self.tables.pop(seq)
+        self._release(self.tables.pop(seq))
         del self.counts[seq]
+
+    def _release(self, table: list) -> None:
+        """Drop one reference to every block of a table, in order (R8, R12)."""
         cached = []
         for b in table:
             self.ref[b] -= 1
@@ -239,7 +289,7 @@ class BlockAllocatorModel:
         writes K/V only for those."""
         tokens = [int(t) for t in tokens]
         n = len(tokens)
-        if seq in self.tables:
+        if self._taken(seq):
             raise AllocError(ERR_EXISTS, f"sequence {seq} exists")
         bs = self.bs
         matched, parent = [], -1
@@ -274,6 +324,117 @@ class BlockAllocatorModel:
         self.prefix_query_tokens += n
         self.prefix_hit_tokens += n_cached
         return n_cached, [self._slot(table, p) for p in range(n_cached, n)]
+
+    # ----------------------------------------------------------- swapping (R13-R17)
+    def set_host_blocks(self, n: int) -> None:
+        if n < 0:
+            raise AllocError(ERR_INVALID, "negative host pool")
+        if self.host_tables:
+            raise AllocError(ERR_INVALID, "sequences are swapped out")
+        self.num_host_blocks = n
+        self.host_free = deque(range(n))
+        self.host_ref = [0] * n
+
+    def _release_host(self, table: list) -> None:
+        for h in table:
+            self.host_ref[h] -= 1
+            if self.host_ref[h] == 0:
+                self.host_free.append(h)
+
+    @staticmethod
+    def _distinct(tables) -> list:
+        seen, out = set(), []
+        for t in tables:
+            for b in t:
+                if b not in seen:
+                    seen.add(b)
+                    out.append(b)
+        return out
+
+    def _group(self, seqs, resident: bool) -> list:
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise AllocError(ERR_INVALID, "a sequence is listed twice")
+        where = self.tables if resident else self.host_tables
+        for s_ in seqs:
+            if s_ not in where:
+                raise AllocError(ERR_NO_SEQ, f"sequence {s_} is not {'resident' if resident else 'swapped out'}")
+        return seqs
+
+    def swap_out(self, seqs) -> list:
+        """Move a group of resident sequences to host blocks (R14); returns the
+        (device block, host block) pairs to copy, before the released device
+        blocks are written again."""
+        seqs = self._group(seqs, True)
+        blocks = self._distinct(self.tables[s_] for s_ in seqs)
+        if len(self.host_free) < len(blocks):
+            raise AllocError(ERR_OOM, f"need {len(blocks)} host blocks, {len(self.host_free)} free")
+        to_host = {b: self.host_free.popleft() for b in blocks}
+        for s_ in seqs:
+            table = self.tables.pop(s_)
+            host = [to_host[b] for b in table]
+            for h in host:
+                self.host_ref[h] += 1
+            self.host_tables[s_] = host
+            self.host_counts[s_] = self.counts.pop(s_)
+            self._release(table)
+        return [(b, to_host[b]) for b in blocks]
+
+    def swap_in(self, seqs) -> list:
+        """Bring a group of swapped-out sequences back (R15); returns the
+        (host block, device block) pairs to copy before the group is used."""
+        seqs = self._group(seqs, False)
+        hosts = self._distinct(self.host_tables[s_] for s_ in seqs)
+        if self._capacity() < len(hosts):
+            raise AllocError(ERR_OOM, f"need {len(hosts)} blocks, {self._capacity()} available")
+        fresh = self._pop(len(hosts))
+        to_dev = dict(zip(hosts, fresh))
+        for s_ in seqs:
+            host = self.host_tables.pop(s_)
+            table = [to_dev[h] for h in host]
+            for b in table:
+                self.ref[b] += 1
+            self.tables[s_] = table
+            self.counts[s_] = self.host_counts.pop(s_)
+            self._release_host(host)
+        return [(h, to_dev[h]) for h in hosts]
+
+    def preempt_tail(self, running, need: int, mode: str = "recompute"):
+        """Preempt from the tail of the running list until `need` blocks are
+        available (R17); returns (victims in preemption order, swap pairs)."""
+        running = [int(s_) for s_ in running]
+        if mode not in ("recompute", "swap") or need < 0:
+            raise AllocError(ERR_INVALID, "bad preemption request")
+        if len(set(running)) != len(running):
+            raise AllocError(ERR_INVALID, "a sequence is listed twice")
+        for s_ in running:
+            self._require(s_)
+        ref = list(self.ref)
+        avail = self._capacity()
+        victims = []
+        for s_ in reversed(running):
+            if avail >= need:
+                break
+            victims.append(s_)
+            for b in self.tables[s_]:
+                ref[b] -= 1
+                if ref[b] == 0:
+                    avail += 1
+        if avail < need:
+            raise AllocError(ERR_OOM, f"need {need} blocks, {avail} even after preempting every listed sequence")
+        if mode == "swap":
+            return victims, self.swap_out(victims)
+        for s_ in victims:
+            self.free_seq(s_)
+        return victims, []
+
+    def swapped_table(self, seq: int) -> list:
+        if seq not in self.host_tables:
+            raise AllocError(ERR_NO_SEQ, f"sequence {seq} is not swapped out")
+        return list(self.host_tables[seq])
+
+    def host_free_list(self) -> list:
+        return list(self.host_free)
 
     # ----------------------------------------------------------- queries
     def slots(self, seq: int, start: int, n: int) -> list[int]:
@@ -345,6 +506,9 @@ class BlockAllocatorModel:
             "cached_blocks": len(self.key_of),
             "prefix_query_tokens": self.prefix_query_tokens,
             "prefix_hit_tokens": self.prefix_hit_tokens,
+            "host_blocks": self.num_host_blocks,
+            "host_free_blocks": len(self.host_free),
+            "swapped_seqs": len(self.host_tables),
         }
 
     def state(self) -> dict:
@@ -356,4 +520,8 @@ class BlockAllocatorModel:
             "ref": list(self.ref),
             "evictable": list(self.evictable),
             "cache": {b: (k[0], list(k[1])) for b, k in sorted(self.key_of.items())},
+            "host_free": list(self.host_free),
+            "host_ref": list(self.host_ref),
+            "host_tables": {s_: list(t) for s_, t in sorted(self.host_tables.items())},
+            "host_counts": dict(sorted(self.host_counts.items())),
         }

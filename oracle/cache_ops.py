@@ -47,3 +47,16 @@ def block_copy(k_cache, v_cache, pairs):
     for src, dst in pairs:
         k_cache[int(dst)] = k_cache[int(src)]
         v_cache[int(dst)] = v_cache[int(src)]
+
+
+def block_swap(src_k, src_v, dst_k, dst_v, pairs):
+    """dst[d] = src[s] for K and V, whole block, for every (s, d) pair.
+
+    Swapping a preempted request copies its blocks to CPU memory and back
+    ("Where Did the VRAM Go (KV cache tutorial)", §7.1-7.2; "From OOM to Smooth
+    Inference", §5): out, src = device caches and dst = host caches; in, the
+    other way round.
+    """
+    for s, d in pairs:
+        dst_k[int(d)] = src_k[int(s)]
+        dst_v[int(d)] = src_v[int(s)]

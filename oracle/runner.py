@@ -20,7 +20,7 @@ import numpy as np
 
 from .allocator import BlockAllocatorModel
 from .attention import decode_attention
-from .cache_ops import block_copy, scatter
+from .cache_ops import block_copy, block_swap, scatter
 from .prefill import prefill_attention
 
 F16_NAN_BITS = 0x7E00
@@ -39,6 +39,7 @@ class RoundResult:
     slots: list
     cow_pairs: list
     prompts: list = field(default_factory=list)  # (op, cached tokens, slots of the other tokens)
+    swaps: list = field(default_factory=list)    # ("out" | "in", pairs), in op order
 
 
 @dataclass
@@ -53,7 +54,7 @@ class OracleRun:
 
 
 def apply_ops(alloc: BlockAllocatorModel, ops) -> RoundResult:
-    slots, pairs, prompts = [], [], []
+    slots, pairs, prompts, swaps = [], [], [], []
     for op in ops:
         if op.kind == "allocate":
             slots += alloc.allocate(op.seq, op.n)
@@ -73,13 +74,30 @@ def apply_ops(alloc: BlockAllocatorModel, ops) -> RoundResult:
             # the tokens after the cached blocks are written
             c, sl = alloc.allocate_prompt(op.seq, op.tokens)
             prompts.append((op, c, list(sl)))
+        elif op.kind == "swap_out":
+            swaps.append(("out", alloc.swap_out(op.group)))
+        elif op.kind == "swap_in":
+            swaps.append(("in", alloc.swap_in(op.group)))
+        elif op.kind == "preempt":
+            # "Where Did the VRAM Go (KV cache tutorial)", §7.1: newest first
+            _, sp = alloc.preempt_tail(op.group, op.n, op.mode)
+            if sp:
+                swaps.append(("out", sp))
         else:
             raise ValueError(op.kind)
-    return RoundResult(slots, pairs, prompts)
+    return RoundResult(slots, pairs, prompts, swaps)
 
 
-def run_round(wl, alloc, k_cache, v_cache, ops) -> RoundResult:
+def run_round(wl, alloc, k_cache, v_cache, ops, host=None) -> RoundResult:
+    """One round: the ops, then their swap copies (in op order, before any
+    write can reuse a released block), copy-on-write copies, then writes.
+    host = (k_host, v_host) caches of the host pool, if the script swaps."""
     res = apply_ops(alloc, ops)
+    for direction, sp in res.swaps:
+        if direction == "out":
+            block_swap(k_cache, v_cache, host[0], host[1], sp)
+        else:
+            block_swap(host[0], host[1], k_cache, v_cache, sp)
     block_copy(k_cache, v_cache, res.cow_pairs)
     K, V = wl.round_kv(ops)
     scatter(k_cache, v_cache, K, V, res.slots, wl.block_size, wl.kv_dtype,
@@ -88,6 +106,16 @@ def run_round(wl, alloc, k_cache, v_cache, ops) -> RoundResult:
         K, V = wl.prompt_kv(op, c)
         scatter(k_cache, v_cache, K, V, sl, wl.block_size, wl.kv_dtype, wl.k_inv_scale, wl.v_inv_scale)
     return res
+
+
+def _host_pool(wl, alloc):
+    """Host caches for the script's swap space (None when it has none)."""
+    n = getattr(wl, "num_host_blocks", 0)
+    if not n:
+        return None
+    alloc.set_host_blocks(n)
+    return (empty_cache(n, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype),
+            empty_cache(n, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype))
 
 
 def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) -> OracleRun:
@@ -99,13 +127,14 @@ def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) ->
     kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
     vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
     run_ = OracleRun(alloc, kc, vc)
+    host = _host_pool(wl, alloc)
     for ops in wl.setup_rounds:
-        r = run_round(wl, alloc, kc, vc, ops)
+        r = run_round(wl, alloc, kc, vc, ops, host)
         if keep_rounds:
             run_.rounds.append(r)
     for step in range(steps):
         ops = wl.step_ops(step)
-        r = run_round(wl, alloc, kc, vc, ops)
+        r = run_round(wl, alloc, kc, vc, ops, host)
         if keep_rounds:
             run_.rounds.append(r)
         tables = [alloc.block_table(s) for s in wl.batch]
@@ -152,8 +181,9 @@ def run_prefill(wl, seqs=None) -> PrefillRun:
     kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
     vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
     cached = {}
+    host = _host_pool(wl, alloc)
     for ops in wl.setup_rounds:
-        r = run_round(wl, alloc, kc, vc, ops)
+        r = run_round(wl, alloc, kc, vc, ops, host)
         for op, c, _ in r.prompts:
             cached[op.seq] = c
     chunks = wl.chunk_lengths(cached)

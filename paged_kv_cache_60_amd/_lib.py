@@ -22,6 +22,11 @@ PKV_ERR_HIP = -5
 KV_F16 = 0
 KV_FP8_E4M3 = 1
 
+SWAP_OUT = 0
+SWAP_IN = 1
+PREEMPT_RECOMPUTE = 0
+PREEMPT_SWAP = 1
+
 _c_int = ctypes.c_int
 _c_i64 = ctypes.c_int64
 _c_f = ctypes.c_float
@@ -45,6 +50,9 @@ class PkvStats(ctypes.Structure):
         ("cached_blocks", ctypes.c_int32),
         ("prefix_query_tokens", ctypes.c_int64),
         ("prefix_hit_tokens", ctypes.c_int64),
+        ("host_blocks", ctypes.c_int32),
+        ("host_free_blocks", ctypes.c_int32),
+        ("swapped_seqs", ctypes.c_int32),
     ]
 
 
@@ -57,6 +65,7 @@ SIGNATURES = {
                                      _c_int, _c_f, _c_f, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
                                      _c_int, _vp]),
     "paged_block_copy": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_sz, _vp]),
+    "paged_block_swap": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_sz, _c_int, _vp]),
     "paged_attn_decode_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _c_int, _vp,
@@ -89,6 +98,14 @@ SIGNATURES = {
     "pkv_bm_num_free": (_c_int, [_vp]),
     "pkv_bm_stats": (_c_int, [_vp, ctypes.POINTER(PkvStats)]),
     "pkv_bm_export": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_i32]),
+    "pkv_bm_set_host_blocks": (_c_int, [_vp, _c_int]),
+    "pkv_bm_swap_out": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_int]),
+    "pkv_bm_swap_in": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_int]),
+    "pkv_bm_preempt_tail": (_c_int, [_vp, _p_i64, _c_int, _c_int, _c_int, _p_i64, _p_int, _p_i32, _c_int, _p_int]),
+    "pkv_bm_swapped_table": (_c_int, [_vp, _c_i64, _p_i32, _c_int, _p_int]),
+    "pkv_bm_swapped_tokens": (_c_int, [_vp, _c_i64, _p_int]),
+    "pkv_bm_host_free_list": (_c_int, [_vp, _p_i32, _c_int, _p_int]),
+    "pkv_bm_host_refcount": (_c_int, [_vp, ctypes.c_int32, _p_int]),
 }
 
 _lib = None

@@ -114,6 +114,69 @@ class BlockManager:
     def free_seq(self, seq: int) -> None:
         check(self._lib.pkv_bm_free(self._h, seq), "pkv_bm_free")
 
+    # ------------------------------------------------------------ preemption and swapping
+    def set_host_blocks(self, n: int) -> None:
+        check(self._lib.pkv_bm_set_host_blocks(self._h, n), "pkv_bm_set_host_blocks")
+        self.num_host_blocks = int(n)
+
+    def _pairs_call(self, fn, where, seqs) -> list:
+        ids = np.ascontiguousarray(np.asarray(list(seqs), dtype=np.int64))
+        cap = max(1, self.num_blocks + getattr(self, "num_host_blocks", 0))
+        out = np.empty(2 * cap, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(fn(self._h, _i64p(ids) if len(ids) else None, len(ids), _i32p(out), cap, ctypes.byref(n)), where)
+        return [(int(out[2 * i]), int(out[2 * i + 1])) for i in range(n.value)]
+
+    def swap_out(self, seqs) -> list:
+        """Swap a group out; returns (device block, host block) pairs to copy."""
+        return self._pairs_call(self._lib.pkv_bm_swap_out, "pkv_bm_swap_out", seqs)
+
+    def swap_in(self, seqs) -> list:
+        """Swap a group back in; returns (host block, device block) pairs to copy."""
+        return self._pairs_call(self._lib.pkv_bm_swap_in, "pkv_bm_swap_in", seqs)
+
+    def preempt_tail(self, running, need: int, mode: str = "recompute"):
+        """Preempt from the tail of `running` until `need` blocks are available;
+        returns (victims, swap pairs)."""
+        ids = np.ascontiguousarray(np.asarray(list(running), dtype=np.int64))
+        victims = np.empty(max(1, len(ids)), dtype=np.int64)
+        cap = max(1, self.num_blocks)
+        pairs = np.empty(2 * cap, dtype=np.int32)
+        nv, npairs = ctypes.c_int(0), ctypes.c_int(0)
+        m = _lib.PREEMPT_SWAP if mode == "swap" else _lib.PREEMPT_RECOMPUTE
+        if mode not in ("swap", "recompute"):
+            m = -1
+        check(self._lib.pkv_bm_preempt_tail(self._h, _i64p(ids) if len(ids) else None, len(ids), int(need), m,
+                                            _i64p(victims), ctypes.byref(nv), _i32p(pairs), cap,
+                                            ctypes.byref(npairs)), "pkv_bm_preempt_tail")
+        return ([int(v) for v in victims[:nv.value]],
+                [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(npairs.value)])
+
+    def swapped_table(self, seq: int) -> list:
+        n = ctypes.c_int(0)
+        cap = max(1, getattr(self, "num_host_blocks", 0))
+        out = np.empty(cap, dtype=np.int32)
+        check(self._lib.pkv_bm_swapped_table(self._h, seq, _i32p(out), cap, ctypes.byref(n)),
+              "pkv_bm_swapped_table")
+        return out[:n.value].tolist()
+
+    def swapped_tokens(self, seq: int) -> int:
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_swapped_tokens(self._h, seq, ctypes.byref(n)), "pkv_bm_swapped_tokens")
+        return n.value
+
+    def host_free_list(self) -> list:
+        cap = max(1, getattr(self, "num_host_blocks", 0))
+        out = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_host_free_list(self._h, _i32p(out), cap, ctypes.byref(n)), "pkv_bm_host_free_list")
+        return out[:n.value].tolist()
+
+    def host_refcount(self, h: int) -> int:
+        rc = ctypes.c_int(0)
+        check(self._lib.pkv_bm_host_refcount(self._h, h, ctypes.byref(rc)), "pkv_bm_host_refcount")
+        return rc.value
+
     # ------------------------------------------------------------ queries
     def slots(self, seq: int, start: int, n: int) -> list:
         out = np.empty(max(n, 0), dtype=np.int64)
@@ -182,6 +245,9 @@ class BlockManager:
             "cached_blocks": s.cached_blocks,
             "prefix_query_tokens": s.prefix_query_tokens,
             "prefix_hit_tokens": s.prefix_hit_tokens,
+            "host_blocks": s.host_blocks,
+            "host_free_blocks": s.host_free_blocks,
+            "swapped_seqs": s.swapped_seqs,
         }
 
     def export(self, seqs: np.ndarray, tables_out: np.ndarray, ctx_out: np.ndarray) -> None:
@@ -189,10 +255,12 @@ class BlockManager:
         check(self._lib.pkv_bm_export(self._h, _i64p(seqs), len(seqs), _i32p(tables_out),
                                       tables_out.shape[1], _i32p(ctx_out)), "pkv_bm_export")
 
-    def state(self, seqs) -> dict:
-        """Snapshot comparable with the oracle model's state() for the given live ids."""
+    def state(self, seqs, swapped=()) -> dict:
+        """Snapshot comparable with the oracle model's state() for the given
+        resident and swapped-out ids."""
         tables = {int(s): self.block_table(int(s)) for s in sorted(seqs)}
         counts = {int(s): self.num_tokens(int(s)) for s in sorted(seqs)}
+        nh = getattr(self, "num_host_blocks", 0)
         cache = {}
         for b in range(self.num_blocks):
             e = self.cache_entry(b)
@@ -205,4 +273,8 @@ class BlockManager:
             "ref": [self.refcount(b) for b in range(self.num_blocks)],
             "evictable": self.evictable_list(),
             "cache": cache,
+            "host_free": self.host_free_list() if nh else [],
+            "host_ref": [self.host_refcount(h) for h in range(nh)],
+            "host_tables": {int(s): self.swapped_table(int(s)) for s in sorted(swapped)},
+            "host_counts": {int(s): self.swapped_tokens(int(s)) for s in sorted(swapped)},
         }

@@ -13,6 +13,12 @@
 //     before it; hits are mapped into the new request's table; zero-count
 //     cached blocks wait for reuse; eviction is least-recently-used:
 //     "Where Did the VRAM Go (KV cache tutorial)", §4.2-4.4.
+//   - Preemption from the tail of the running set, by recompute (the blocks
+//     are released) or by swapping the blocks to a host pool and back:
+//     "Where Did the VRAM Go (KV cache tutorial)", §7.1-7.2; "From OOM to
+//     Smooth Inference", §5; "vLLM Architecture and Memory Use, ch. 3", §3.4.
+//     A group's shared blocks are copied once; a swapped-out sequence keeps
+//     its token count and a table of host blocks and is not resident.
 // The last block's fill is derived from the sequence's own token count, so two
 // sequences sharing a block never update a common counter. Every call checks
 // before it mutates: a failing call leaves the state as it was.
@@ -100,8 +106,40 @@ struct pkv_bm {
   std::vector<char> in_ev;
   int64_t prefix_query_tokens = 0;
   int64_t prefix_hit_tokens = 0;
+  // host pool of swapped-out sequences
+  int32_t num_host_blocks = 0;
+  std::deque<int32_t> host_free;
+  std::vector<int32_t> host_ref;
+  std::unordered_map<int64_t, Seq> swapped;  // tables hold host block ids
 
   int64_t needed(int64_t tokens) const { return (tokens + bs - 1) / bs; }
+
+  // an id that a new sequence may not take: resident or swapped out
+  bool taken_id(int64_t id) const { return seqs.count(id) || swapped.count(id); }
+
+  // Drop one reference to each block of a table, in order; uncached blocks
+  // reaching 0 go to the back of the free queue, cached ones to the back of
+  // the evictable list, deepest first.
+  void release(const std::vector<int32_t>& table) {
+    std::vector<int32_t> to_cache;
+    for (int32_t b : table) {
+      ref[b] -= 1;
+      if (ref[b] == 0) {
+        if (cached[b])
+          to_cache.push_back(b);
+        else
+          free_q.push_back(b);
+      }
+    }
+    for (auto r = to_cache.rbegin(); r != to_cache.rend(); ++r) ev_push_back(*r);
+  }
+
+  void release_host(const std::vector<int32_t>& table) {
+    for (int32_t h : table) {
+      host_ref[h] -= 1;
+      if (host_ref[h] == 0) host_free.push_back(h);
+    }
+  }
 
   int64_t capacity() const { return static_cast<int64_t>(free_q.size() + evictable.size()); }
 
@@ -283,7 +321,7 @@ void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
 
 int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out) {
   if (!bm || num_tokens < 0) return PKV_ERR_INVALID;
-  if (bm->seqs.count(seq)) return PKV_ERR_EXISTS;
+  if (bm->taken_id(seq)) return PKV_ERR_EXISTS;
   const int64_t nb = bm->needed(num_tokens);
   if (bm->capacity() < nb) return PKV_ERR_OOM;
   Seq s;
@@ -303,7 +341,7 @@ int pkv_bm_allocate(pkv_bm* bm, int64_t seq, int num_tokens, int64_t* slots_out)
 int pkv_bm_allocate_prompt(pkv_bm* bm, int64_t seq, const int32_t* tokens, int n_tokens, int* n_cached,
                            int64_t* slots_out) {
   if (!bm || n_tokens < 0 || !n_cached || (n_tokens > 0 && (!tokens || !slots_out))) return PKV_ERR_INVALID;
-  if (bm->seqs.count(seq)) return PKV_ERR_EXISTS;
+  if (bm->taken_id(seq)) return PKV_ERR_EXISTS;
   const int bs = bm->bs;
   const int full = n_tokens / bs;
   std::vector<int32_t> matched;
@@ -441,7 +479,7 @@ int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return PKV_ERR_INVALID;
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
-  if (bm->seqs.count(child)) return PKV_ERR_EXISTS;
+  if (bm->taken_id(child)) return PKV_ERR_EXISTS;
   Seq c = it->second;
   for (int32_t b : c.table) bm->ref[b] += 1;
   bm->seqs.emplace(child, std::move(c));
@@ -452,7 +490,7 @@ int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst) {
   if (!bm) return PKV_ERR_INVALID;
   auto it = bm->seqs.find(src);
   if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
-  if (bm->seqs.count(dst)) return PKV_ERR_EXISTS;
+  if (bm->taken_id(dst)) return PKV_ERR_EXISTS;
   const Seq& s = it->second;
   if (n_blocks < 0 || n_blocks > static_cast<int>(s.table.size())) return PKV_ERR_INVALID;
   Seq d;
@@ -465,20 +503,188 @@ int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int n_blocks, int64_t dst) {
 
 int pkv_bm_free(pkv_bm* bm, int64_t seq) {
   if (!bm) return PKV_ERR_INVALID;
+  auto sw = bm->swapped.find(seq);
+  if (sw != bm->swapped.end()) {  // a swapped-out sequence gives back its host blocks
+    bm->release_host(sw->second.table);
+    bm->swapped.erase(sw);
+    return PKV_OK;
+  }
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
-  std::vector<int32_t> to_cache;
-  for (int32_t b : it->second.table) {
-    bm->ref[b] -= 1;
-    if (bm->ref[b] == 0) {
-      if (bm->cached[b])
-        to_cache.push_back(b);
-      else
-        bm->free_q.push_back(b);
-    }
-  }
-  for (auto r = to_cache.rbegin(); r != to_cache.rend(); ++r) bm->ev_push_back(*r);
+  bm->release(it->second.table);
   bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The listed ids, checked: no duplicates (INVALID), each present in `where`
+// (NO_SEQ).
+int check_group(const std::unordered_map<int64_t, Seq>& where, const int64_t* seqs, int n) {
+  if (n < 0 || (n > 0 && !seqs)) return PKV_ERR_INVALID;
+  std::unordered_set<int64_t> uniq;
+  for (int i = 0; i < n; ++i)
+    if (!uniq.insert(seqs[i]).second) return PKV_ERR_INVALID;
+  for (int i = 0; i < n; ++i)
+    if (!where.count(seqs[i])) return PKV_ERR_NO_SEQ;
+  return PKV_OK;
+}
+
+// Distinct block ids of the listed tables, in order of first appearance.
+std::vector<int32_t> distinct_blocks(const std::unordered_map<int64_t, Seq>& where, const int64_t* seqs, int n) {
+  std::vector<int32_t> out;
+  std::unordered_set<int32_t> seen;
+  for (int i = 0; i < n; ++i)
+    for (int32_t b : where.at(seqs[i]).table)
+      if (seen.insert(b).second) out.push_back(b);
+  return out;
+}
+
+int swap_out_impl(pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* pairs_out, int cap, int* n_pairs) {
+  const std::vector<int32_t> blocks = distinct_blocks(bm->seqs, seqs, n_seqs);
+  const int nb = static_cast<int>(blocks.size());
+  if (nb > cap || (nb > 0 && !pairs_out)) return PKV_ERR_INVALID;
+  if (static_cast<int>(bm->host_free.size()) < nb) return PKV_ERR_OOM;
+  std::unordered_map<int32_t, int32_t> to_host;
+  for (int i = 0; i < nb; ++i) {
+    const int32_t h = bm->host_free.front();
+    bm->host_free.pop_front();
+    to_host.emplace(blocks[i], h);
+    pairs_out[2 * i] = blocks[i];
+    pairs_out[2 * i + 1] = h;
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    Seq host;
+    host.count = it->second.count;
+    host.table.reserve(it->second.table.size());
+    for (int32_t b : it->second.table) {
+      const int32_t h = to_host.at(b);
+      host.table.push_back(h);
+      bm->host_ref[h] += 1;
+    }
+    bm->release(it->second.table);
+    bm->seqs.erase(it);
+    bm->swapped.emplace(seqs[i], std::move(host));
+  }
+  *n_pairs = nb;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_bm_set_host_blocks(pkv_bm* bm, int num_host_blocks) {
+  if (!bm || num_host_blocks < 0 || !bm->swapped.empty()) return PKV_ERR_INVALID;
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_free.clear();
+  for (int i = 0; i < num_host_blocks; ++i) bm->host_free.push_back(i);
+  bm->host_ref.assign(num_host_blocks, 0);
+  return PKV_OK;
+}
+
+int pkv_bm_swap_out(pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* pairs_out, int cap, int* n_pairs) {
+  if (!bm || !n_pairs || cap < 0) return PKV_ERR_INVALID;
+  const int st = check_group(bm->seqs, seqs, n_seqs);
+  if (st != PKV_OK) return st;
+  return swap_out_impl(bm, seqs, n_seqs, pairs_out, cap, n_pairs);
+}
+
+int pkv_bm_swap_in(pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* pairs_out, int cap, int* n_pairs) {
+  if (!bm || !n_pairs || cap < 0) return PKV_ERR_INVALID;
+  const int st = check_group(bm->swapped, seqs, n_seqs);
+  if (st != PKV_OK) return st;
+  const std::vector<int32_t> hosts = distinct_blocks(bm->swapped, seqs, n_seqs);
+  const int nh = static_cast<int>(hosts.size());
+  if (nh > cap || (nh > 0 && !pairs_out)) return PKV_ERR_INVALID;
+  if (bm->capacity() < nh) return PKV_ERR_OOM;
+  std::unordered_map<int32_t, int32_t> to_dev;
+  for (int i = 0; i < nh; ++i) {
+    const int32_t g = bm->take(nullptr);
+    to_dev.emplace(hosts[i], g);
+    pairs_out[2 * i] = hosts[i];
+    pairs_out[2 * i + 1] = g;
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->swapped.find(seqs[i]);
+    Seq dev;
+    dev.count = it->second.count;
+    dev.table.reserve(it->second.table.size());
+    for (int32_t h : it->second.table) {
+      const int32_t g = to_dev.at(h);
+      dev.table.push_back(g);
+      bm->ref[g] += 1;
+    }
+    bm->release_host(it->second.table);
+    bm->swapped.erase(it);
+    bm->seqs.emplace(seqs[i], std::move(dev));
+  }
+  *n_pairs = nh;
+  return PKV_OK;
+}
+
+int pkv_bm_preempt_tail(pkv_bm* bm, const int64_t* running, int n_running, int blocks_needed, int mode,
+                        int64_t* victims_out, int* n_victims, int32_t* pairs_out, int cap, int* n_pairs) {
+  if (!bm || !n_victims || !n_pairs || blocks_needed < 0 || cap < 0 ||
+      (mode != PKV_PREEMPT_RECOMPUTE && mode != PKV_PREEMPT_SWAP) || (n_running > 0 && !victims_out))
+    return PKV_ERR_INVALID;
+  const int st = check_group(bm->seqs, running, n_running);
+  if (st != PKV_OK) return st;
+  // victims from the tail until enough blocks would be available, counting
+  // only the blocks each victim would actually release
+  std::unordered_map<int32_t, int32_t> drop;
+  int64_t avail = bm->capacity();
+  int nv = 0;
+  for (int i = n_running - 1; i >= 0 && avail < blocks_needed; --i) {
+    victims_out[nv++] = running[i];
+    for (int32_t b : bm->seqs.at(running[i]).table)
+      if (bm->ref[b] - ++drop[b] == 0) ++avail;
+  }
+  if (avail < blocks_needed) return PKV_ERR_OOM;
+  *n_pairs = 0;
+  if (mode == PKV_PREEMPT_SWAP) {
+    const int s2 = swap_out_impl(bm, victims_out, nv, pairs_out, cap, n_pairs);
+    if (s2 != PKV_OK) return s2;
+  } else {
+    for (int i = 0; i < nv; ++i) pkv_bm_free(bm, victims_out[i]);
+  }
+  *n_victims = nv;
+  return PKV_OK;
+}
+
+int pkv_bm_swapped_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* n) {
+  if (!bm || !n || cap < 0) return PKV_ERR_INVALID;
+  auto it = bm->swapped.find(seq);
+  if (it == bm->swapped.end()) return PKV_ERR_NO_SEQ;
+  const auto& t = it->second.table;
+  if (static_cast<int>(t.size()) > cap || (!t.empty() && !out)) return PKV_ERR_INVALID;
+  std::copy(t.begin(), t.end(), out);
+  *n = static_cast<int>(t.size());
+  return PKV_OK;
+}
+
+int pkv_bm_swapped_tokens(const pkv_bm* bm, int64_t seq, int* n) {
+  if (!bm || !n) return PKV_ERR_INVALID;
+  auto it = bm->swapped.find(seq);
+  if (it == bm->swapped.end()) return PKV_ERR_NO_SEQ;
+  *n = static_cast<int>(it->second.count);
+  return PKV_OK;
+}
+
+int pkv_bm_host_free_list(const pkv_bm* bm, int32_t* out, int cap, int* n) {
+  if (!bm || !n || cap < 0) return PKV_ERR_INVALID;
+  if (static_cast<int>(bm->host_free.size()) > cap || (!bm->host_free.empty() && !out)) return PKV_ERR_INVALID;
+  std::copy(bm->host_free.begin(), bm->host_free.end(), out);
+  *n = static_cast<int>(bm->host_free.size());
+  return PKV_OK;
+}
+
+int pkv_bm_host_refcount(const pkv_bm* bm, int32_t host_block, int* rc) {
+  if (!bm || !rc || host_block < 0 || host_block >= bm->num_host_blocks) return PKV_ERR_INVALID;
+  *rc = bm->host_ref[host_block];
   return PKV_OK;
 }
 
@@ -572,6 +778,9 @@ int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out) {
   out->prefix_query_tokens = bm->prefix_query_tokens;
   out->prefix_hit_tokens = bm->prefix_hit_tokens;
   out->live_seqs = static_cast<int32_t>(bm->seqs.size());
+  out->host_blocks = bm->num_host_blocks;
+  out->host_free_blocks = static_cast<int32_t>(bm->host_free.size());
+  out->swapped_seqs = static_cast<int32_t>(bm->swapped.size());
   out->filled_slots = total_filled;
   out->utilization = static_cast<double>(out->used_blocks) / bm->num_blocks;
   out->slot_utilization =

@@ -41,7 +41,7 @@ EVENT_EVERY = 4   # steps covered by one completion event; RING is a multiple of
 class PagedKVEngine:
     def __init__(self, num_blocks, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype="f16",
                  free_order=None, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0,
-                 device="cuda", poison=True):
+                 device="cuda", poison=True, num_host_blocks=0):
         self.num_blocks = int(num_blocks)
         self.hq, self.hkv, self.d, self.bs = int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size)
         self.kv_dtype = kv_dtype
@@ -53,6 +53,15 @@ class PagedKVEngine:
         dt = ops.cache_torch_dtype(kv_dtype)
         self.k_cache = torch.empty(shape, dtype=dt, device=self.device)
         self.v_cache = torch.empty(shape, dtype=dt, device=self.device)
+        # host pool for swapped-out sequences: pinned, same layout, read and
+        # written by paged_block_swap directly
+        self.num_host_blocks = int(num_host_blocks)
+        self.k_host = self.v_host = None
+        if self.num_host_blocks:
+            hshape = (self.num_host_blocks, self.hkv, self.bs, self.d)
+            self.k_host = torch.empty(hshape, dtype=dt, pin_memory=True)
+            self.v_host = torch.empty(hshape, dtype=dt, pin_memory=True)
+            self.bm.set_host_blocks(self.num_host_blocks)
         if poison:
             self.poison()
 
@@ -72,10 +81,11 @@ class PagedKVEngine:
     # ------------------------------------------------------ scripted rounds
     def apply_ops(self, ops_list):
         """Run block-manager ops in order; returns (slots int64 array of the
-        allocate / append ops, cow pairs list, prompts list). A prompt op goes
-        through the prefix cache; its entry is (op, cached tokens, slots of the
-        tokens after them), the ones whose K/V must still be written."""
-        slots, pairs, prompts = [], [], []
+        allocate / append ops, cow pairs list, prompts list, swaps list). A
+        prompt op goes through the prefix cache; its entry is (op, cached
+        tokens, slots of the tokens after them), the ones whose K/V must still
+        be written. A swap entry is ("out" | "in", pairs), in op order."""
+        slots, pairs, prompts, swaps = [], [], [], []
         bm = self.bm
         for op in ops_list:
             if op.kind == "allocate":
@@ -94,10 +104,24 @@ class PagedKVEngine:
             elif op.kind == "prompt":
                 c, sl = bm.allocate_prompt(op.seq, op.tokens)
                 prompts.append((op, c, sl))
+            elif op.kind == "swap_out":
+                swaps.append(("out", bm.swap_out(op.group)))
+            elif op.kind == "swap_in":
+                swaps.append(("in", bm.swap_in(op.group)))
+            elif op.kind == "preempt":
+                _, sp = bm.preempt_tail(op.group, op.n, op.mode)
+                if sp:
+                    swaps.append(("out", sp))
             else:
                 raise ValueError(op.kind)
         s = np.concatenate(slots) if slots else np.zeros(0, dtype=np.int64)
-        return s, pairs, prompts
+        return s, pairs, prompts, swaps
+
+    def swap(self, direction, pairs):
+        """Copy swapped blocks: "out" (device, host) pairs, "in" (host, device)."""
+        if pairs:
+            p = torch.tensor(pairs, dtype=torch.int32).to(self.device, non_blocking=False)
+            ops.paged_block_swap(self.k_cache, self.v_cache, self.k_host, self.v_host, p, direction)
 
     def copy_blocks(self, pairs):
         if pairs:

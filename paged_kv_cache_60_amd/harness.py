@@ -2,8 +2,8 @@
 
 A script (see the ``workloads`` package) is a list of setup rounds of block
 manager operations followed by decode steps. Each round runs all of its
-operations on the host block manager first, then the round's copy-on-write
-block copies, then writes the round's new tokens (in chunks of at most
+operations on the host block manager first, then the round's swap copies (in
+op order), copy-on-write block copies, then writes the round's new tokens (in chunks of at most
 ``chunk_tokens`` tokens, so host staging stays bounded); this is the same
 order in which a serving loop would issue them.
 
@@ -24,11 +24,14 @@ from .engine import PagedKVEngine
 def make_engine(wl, device="cuda", poison=True) -> PagedKVEngine:
     return PagedKVEngine(wl.num_blocks, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                          wl.kv_dtype, wl.free_order, wl.k_scale, wl.v_scale, wl.k_inv_scale,
-                         wl.v_inv_scale, device=device, poison=poison)
+                         wl.v_inv_scale, device=device, poison=poison,
+                         num_host_blocks=getattr(wl, "num_host_blocks", 0))
 
 
 def replay_round(eng: PagedKVEngine, wl, ops, chunk_tokens: int = 1 << 18):
-    slots, pairs, prompts = eng.apply_ops(ops)
+    slots, pairs, prompts, swaps = eng.apply_ops(ops)
+    for direction, sp in swaps:  # in op order, before any write reuses a released block
+        eng.swap(direction, sp)
     eng.copy_blocks(pairs)
     # rows after the cached blocks only; the draws run in threads (the
     # generator releases the GIL), a bounded number of prompts at a time

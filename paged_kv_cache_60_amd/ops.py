@@ -87,6 +87,26 @@ def paged_block_copy(k_cache, v_cache, pairs, stream=None):
                                _stream_ptr(stream)), w)
 
 
+def paged_block_swap(k_cache, v_cache, k_host, v_host, pairs, direction, stream=None):
+    """Whole-block copies between the device caches and pinned host caches of the same
+    layout. direction "out": pairs (device, host), host <- device; "in": pairs (host,
+    device), device <- host. pairs: int32 [n, 2], device or pinned."""
+    w = "paged_block_swap"
+    _require(k_cache.is_cuda and v_cache.is_cuda and k_cache.is_contiguous() and v_cache.is_contiguous()
+             and k_cache.shape == v_cache.shape and k_cache.dim() == 4, w, "caches")
+    _require(k_host.is_pinned() and v_host.is_pinned() and k_host.is_contiguous() and v_host.is_contiguous()
+             and k_host.shape == v_host.shape and k_host.shape[1:] == k_cache.shape[1:]
+             and k_host.dtype == k_cache.dtype and v_host.dtype == v_cache.dtype, w, "host caches")
+    _require(_device_readable(pairs) and pairs.dtype == torch.int32 and pairs.dim() == 2
+             and pairs.shape[1] == 2 and pairs.is_contiguous(), w, "pairs")
+    _require(direction in ("out", "in"), w, "direction")
+    block_bytes = k_cache[0].numel() * k_cache.element_size()
+    lib = _lib.load()
+    check(lib.paged_block_swap(_p(k_cache), _p(v_cache), _p(k_host), _p(v_host), _p(pairs), pairs.shape[0],
+                               k_cache.shape[0], k_host.shape[0], block_bytes,
+                               _lib.SWAP_OUT if direction == "out" else _lib.SWAP_IN, _stream_ptr(stream)), w)
+
+
 def paged_kv_write_step(k_new, v_new, k_cache, v_cache, slot_mapping, ctx_src, ctx_dst, updates,
                         n_updates, block_tables, kv_dtype=F16, k_inv_scale=1.0, v_inv_scale=1.0,
                         stream=None):

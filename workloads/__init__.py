@@ -59,6 +59,10 @@ class Op:
     key:  index of the op's K/V draw in stream 3 (allocate / append).
     tokens: a prompt's token ids.
     parts:  a prompt's K/V rows, in order, as (key in stream 3, rows) draws.
+    Preemption ops ("Where Did the VRAM Go (KV cache tutorial)", §7.1-7.2):
+          "swap_out" / "swap_in" (group = the sequences, in order),
+          "preempt" (group = the running list, n = blocks needed,
+          mode = "recompute" or "swap"), "free" (seq).
     """
     kind: str
     seq: int
@@ -67,6 +71,8 @@ class Op:
     key: int = -1
     tokens: tuple = ()
     parts: tuple = ()
+    group: tuple = ()
+    mode: str = ""
 
     @property
     def creates_tokens(self) -> bool:
@@ -94,6 +100,7 @@ class Workload:
     k_inv_scale: float = 1.0  # fp8 quantisation multipliers (float32 values)
     v_inv_scale: float = 1.0
     meta: dict = field(default_factory=dict)
+    num_host_blocks: int = 0  # host pool for swapped-out sequences
 
     # ------------------------------------------------------------ derived
     @property
@@ -401,6 +408,42 @@ def llama2_7b_chunked(batch: int = 64, chunk: int = 512) -> Workload:
     base.max_steps = 0
     base.max_blocks_per_seq = _ceil_div(max(L), 16)
     base.meta = dict(base.meta, chunk=[min(l, chunk) for l in L])
+    return base
+
+
+def llama2_7b_preempt(mode: str = "swap", max_steps: int = 2, batch: int = 64, victims: int = 16) -> Workload:
+    """The Llama-2-7B batch-64 decode workload with preemption ("Where Did the
+    VRAM Go (KV cache tutorial)", §7.1-7.2; "From OOM to Smooth Inference", §5).
+    After the batch is prefilled, a burst of `victims` new requests needs the
+    blocks of the newest `victims` running sequences: they are preempted from
+    the tail of the running set (mode "swap": copied to a host pool; mode
+    "recompute": dropped). The burst's requests are written, run and finish;
+    the preempted sequences then come back (swapped in, or allocated and
+    prefilled again from the same K/V draws), and the whole batch decodes.
+    Its K/V are then exactly those of the plain workload, so the decode
+    outputs must be too."""
+    base = llama2_7b(max_steps=max_steps, batch=batch)
+    L = base.meta["lengths"]
+    bs = base.block_size
+    nb = base.num_blocks
+    held = [_ceil_div(l - 1, bs) for l in L]
+    tail = list(range(batch - victims, batch))
+    need = nb - sum(held) + sum(held[s] for s in tail)  # every block the tail holds, plus the free ones
+    burst = [batch + i for i in range(victims)]
+    r0 = [Op("allocate", s, L[s] - 1, key=s) for s in range(batch)]
+    r1 = [Op("preempt", -1, need, group=tuple(range(batch)), mode=mode)]
+    r2 = [Op("allocate", b, held[t] * bs, key=10_000 + b) for b, t in zip(burst, tail)]
+    r3 = [Op("free", b) for b in burst]
+    if mode == "swap":
+        r4 = [Op("swap_in", -1, group=tuple(tail))]
+    else:
+        r4 = [Op("allocate", s, L[s] - 1, key=s) for s in tail]
+    base.name = f"llama2_7b_decode_b{batch}_preempt_{mode}"
+    base.description = (f"Llama-2-7B-shaped decode, batch {batch}: the newest {victims} sequences preempted "
+                        f"({mode}) for a burst of {victims} requests, then resumed")
+    base.setup_rounds = [r0, r1, r2, r3, r4]
+    base.num_host_blocks = sum(held[s] for s in tail) if mode == "swap" else 0
+    base.meta = dict(base.meta, preempted=tail, mode=mode)
     return base
 
 
