@@ -134,16 +134,16 @@ def cpu_baseline(wl, target_s=15.0):
     lens = [alloc.num_tokens(s) for s in order]
     done, tokens, elapsed = [], 0, 0.0
     with threadpool_limits(limits=1):
-        for i in range(len(order)):
+        # whole sequences, the batch over and over, until ~target_s of work
+        while elapsed < target_s and len(done) < 64 * len(order):
+            i = len(done) % len(order)
             t0 = time.perf_counter()
             oattn.decode_attention(q, kc, vc, tables, lens, wl.block_size, wl.sm_scale, wl.kv_dtype,
                                    wl.k_scale, wl.v_scale, seqs=[i])
             elapsed += time.perf_counter() - t0
             done.append(i)
             tokens += lens[i]
-            if elapsed >= target_s:
-                break
-    elem = 1 if wl.kv_dtype == "fp8" else 2
+    elem = 1 if wl.kv_dtype != "f16" else 2
     _, nbytes = attention_bytes([lens[i] for i in done], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                 wl.block_size, elem)
     return {
@@ -151,8 +151,8 @@ def cpu_baseline(wl, target_s=15.0):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"gather + fp64 attention of {len(done)} of {len(order)} sequences "
-                  f"({tokens} KV tokens, all {wl.num_q_heads} query heads) of one decode step, "
+        "sample": f"gather + fp64 attention of {len(done)} sequences (the {len(order)} of one decode step, "
+                  f"in order, repeated; {tokens} KV tokens, all {wl.num_q_heads} query heads), "
                   f"{elapsed:.1f} s on one host core",
         "kv_tokens_per_s": round(tokens / elapsed, 1),
     }
@@ -199,7 +199,9 @@ def prefill_cpu_baseline(wl, target_s=15.0):
     done, flops, elapsed = [], 0, 0.0
     from oracle.prefill import prefill_attention
     with threadpool_limits(limits=1):
-        for i in range(len(wl.batch)):
+        # whole sequences' chunks, the batch over and over, until ~target_s of work
+        while elapsed < target_s and len(done) < 16 * len(wl.batch):
+            i = len(done) % len(wl.batch)
             n = o.chunks[i]
             q = wl.prefill_queries(wl.batch[i], n)
             t0 = time.perf_counter()
@@ -208,16 +210,15 @@ def prefill_cpu_baseline(wl, target_s=15.0):
             elapsed += time.perf_counter() - t0
             done.append(i)
             flops += prefill_flops([o.ctx_lens[i]], [n], wl.num_q_heads, wl.head_dim)
-            if elapsed >= target_s:
-                break
+    rows = sum(o.chunks[i] for i in done)
     return {
         "value": round(flops / elapsed / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"gather + fp64 causal attention of {len(done)} of {len(wl.batch)} sequences' chunks "
-                  f"({sum(o.chunks[i] for i in done)} query rows) of one prefill pass, {elapsed:.1f} s on one host core",
-        "query_tokens_per_s": round(sum(o.chunks[i] for i in done) / elapsed, 1),
+        "sample": f"gather + fp64 causal attention of {len(done)} sequences' chunks (the {len(wl.batch)} of one "
+                  f"prefill pass, in order, repeated as needed; {rows} query rows), {elapsed:.1f} s on one host core",
+        "query_tokens_per_s": round(rows / elapsed, 1),
     }
 
 
@@ -295,7 +296,7 @@ def bench_prefill(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if wl.kv_dtype == "f16" else "fp8e4m3-kv/f16",
+        "dtype": "f16" if wl.kv_dtype == "f16" else ("fp8e4m3" if wl.kv_dtype == "fp8" else "fp8e5m2") + "-kv/f16",
         "data": "synthetic",
         "config": {**wl.summary(), "query_rows": rows, "prefix_cache_hit_tokens": int(sum(cached.values())),
                    "timing": "wall clock per step (write + prefill); roofline from events around the prefill"},
@@ -410,6 +411,10 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict L2/MALL between steps (time by events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kv", choices=["fp8", "fp8_e5m2"], default=None,
+                    help="fp8 format of the beam workload (--config 5): e4m3 (default) or e5m2")
+    ap.add_argument("--per-head", action="store_true",
+                    help="one fp8 scale per KV head for the beam workload (--config 5)")
     ap.add_argument("--prefill", choices=sorted(PREFILL_WORKLOADS),
                     help="time chunked prefill instead of decode (qwen3: prefix-cache prefill, batch 256; "
                          "llama2: last-512-token chunks, batch 64)")
@@ -448,7 +453,13 @@ def main():
         return
 
     total_steps = args.warmup + args.steps
-    wl = workloads.make(args.config, max_steps=total_steps + 1)
+    fp8_kw = {}
+    if args.kv or args.per_head:
+        if args.config != 5:
+            print("--kv / --per-head apply to the fp8 beam workload (--config 5)", file=sys.stderr)
+            sys.exit(2)
+        fp8_kw = {"kv_dtype": args.kv or "fp8", "per_head": args.per_head}
+    wl = workloads.make(args.config, max_steps=total_steps + 1, **fp8_kw)
     log(f"bench: {wl.name}: setup")
     dev = torch.device("cuda")
     eng = harness.make_engine(wl, poison=False)
@@ -464,7 +475,7 @@ def main():
     inputs = [harness.step_inputs(wl, s) for s in range(total_steps)]
     out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float16, device=dev)
     flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev) if args.flush else None
-    elem = 1 if wl.kv_dtype == "fp8" else 2
+    elem = 1 if wl.kv_dtype != "f16" else 2
     torch.cuda.synchronize()
 
     def one_step(s, ev=None):
@@ -548,7 +559,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if wl.kv_dtype == "f16" else "fp8e4m3-kv/f16",
+        "dtype": "f16" if wl.kv_dtype == "f16" else ("fp8e4m3" if wl.kv_dtype == "fp8" else "fp8e5m2") + "-kv/f16",
         "data": "synthetic",
         "config": {
             **wl.summary(),
@@ -577,7 +588,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(workloads.make(args.config, max_steps=1), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(workloads.make(args.config, max_steps=1, **fp8_kw), args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

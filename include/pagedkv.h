@@ -10,8 +10,10 @@
  *
  * Conventions shared by every call
  *   - KV cache layout, for K and for V alike: [num_blocks][num_kv_heads]
- *     [block_size][head_dim], contiguous, element type fp16 or OCP fp8 e4m3fn
- *     (one byte). Physical block b, KV head h, offset o starts at element
+ *     [block_size][head_dim], contiguous, element type fp16, OCP fp8 e4m3fn or
+ *     OCP fp8 e5m2 (one byte; [VRAM] §6.2). An fp8 cache has its scales one
+ *     per tensor (the float arguments) or one per KV head (the *_scaled
+ *     calls, [VRAM] §6.3: the granularity can go down to one per head). Physical block b, KV head h, offset o starts at element
  *     ((b * num_kv_heads + h) * block_size + o) * head_dim.
  *   - A slot is block * block_size + offset ([OOM] §2.1: logical block i of
  *     a sequence lives in physical block table[i]).
@@ -47,7 +49,7 @@ typedef enum {
   PKV_ERR_HIP = -5      /* the HIP runtime refused a launch              */
 } pkv_status;
 
-typedef enum { PKV_KV_F16 = 0, PKV_KV_FP8_E4M3 = 1 } pkv_kv_dtype;
+typedef enum { PKV_KV_F16 = 0, PKV_KV_FP8_E4M3 = 1, PKV_KV_FP8_E5M2 = 2 } pkv_kv_dtype;
 
 typedef enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 } pkv_swap_dir;
 
@@ -72,6 +74,8 @@ const char* pkv_status_str(int status);
  *   kv_dtype       PKV_KV_F16: the fp16 bits are copied unchanged.
  *                  PKV_KV_FP8_E4M3: byte = e4m3(float32(x) * inv_scale),
  *                  rounded to nearest even, saturated to +-448.
+ *                  PKV_KV_FP8_E5M2: byte = e5m2(float32(x) * inv_scale),
+ *                  rounded to nearest even, saturated to +-57344.
  *   k/v_inv_scale  fp8 only: multiplier applied before encoding (1/scale).
  * Two valid tokens must not share a slot (the later write would race).
  */
@@ -79,6 +83,15 @@ int paged_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_
                    const int64_t* slot_mapping, int num_tokens, int num_blocks,
                    int num_kv_heads, int head_dim, int block_size, int kv_dtype,
                    float k_inv_scale, float v_inv_scale, void* stream);
+
+/* paged_kv_write with one multiplier per KV head: k_inv_scales and
+ * v_inv_scales are device float arrays of num_kv_heads entries (head h's rows
+ * are encoded as fp8(float32(x) * inv_scales[h])); they may be NULL for an
+ * fp16 cache, INVALID otherwise. [VRAM] §6.3. */
+int paged_kv_write_scaled(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                          int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                          const float* k_inv_scales, const float* v_inv_scales, void* stream);
 
 /*
  * paged_kv_write_step -- paged_kv_write and paged_step_metadata in one
@@ -96,6 +109,15 @@ int paged_kv_write_step(const void* k_new, const void* v_new, void* k_cache, voi
                         float k_inv_scale, float v_inv_scale, const int32_t* ctx_src,
                         int32_t* ctx_dst, int n_ctx, const int32_t* updates, int n_updates,
                         int32_t* block_tables, int num_rows, int max_blocks, void* stream);
+
+/* paged_kv_write_step with per-KV-head multipliers (device arrays, as in
+ * paged_kv_write_scaled). */
+int paged_kv_write_step_scaled(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                               int num_kv_heads, int head_dim, int block_size, int kv_dtype,
+                               const float* k_inv_scales, const float* v_inv_scales, const int32_t* ctx_src,
+                               int32_t* ctx_dst, int n_ctx, const int32_t* updates, int n_updates,
+                               int32_t* block_tables, int num_rows, int max_blocks, void* stream);
 
 /*
  * paged_block_copy -- whole-block copy for copy-on-write.
@@ -159,7 +181,9 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  *                  token written this step). Clamped to
  *                  [0, max_blocks_per_seq*block_size]; 0 gives a zero output.
  *   sm_scale       softmax scale (1/sqrt(head_dim) usually).
- *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale).
+ *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale);
+ *                  kv_dtype PKV_KV_FP8_E4M3 or PKV_KV_FP8_E5M2 (both widened
+ *                  to fp16 exactly before the arithmetic).
  *   partition_tokens 0 = one worker per SIMD of the device (fp16 KV with one
  *                  query head per KV head) or two (other shapes), within
  *                  what the device can hold at once; else a multiple of 16:
@@ -197,6 +221,18 @@ int paged_attn_decode_passes(void* out, const void* q, const void* k_cache, cons
                              const int32_t* ctx_lens, int num_seqs, int num_q_heads,
                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
                              float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                             int partition_tokens, void* workspace, size_t workspace_bytes,
+                             int passes, void* stream);
+
+/* paged_attn_decode_passes with one dequantisation scale per KV head:
+ * k_scales and v_scales are device float arrays of num_kv_heads entries (K of
+ * head h = byte * k_scales[h]); they may be NULL for an fp16 cache, INVALID
+ * otherwise. [VRAM] §6.3 (scales per attention head). */
+int paged_attn_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             float sm_scale, int kv_dtype, const float* k_scales, const float* v_scales,
                              int partition_tokens, void* workspace, size_t workspace_bytes,
                              int passes, void* stream);
 
@@ -241,6 +277,15 @@ int paged_attn_prefill(void* out, const void* q, const void* k_cache, const void
                        const int32_t* q_start, int num_seqs, int total_q, int num_q_heads,
                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
                        float sm_scale, int kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* paged_attn_prefill with one dequantisation scale per KV head (device
+ * arrays, as in paged_attn_decode_scaled). */
+int paged_attn_prefill_scaled(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* ctx_lens,
+                              const int32_t* q_start, int num_seqs, int total_q, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              float sm_scale, int kv_dtype, const float* k_scales, const float* v_scales,
+                              void* stream);
 
 /*
  * paged_step_metadata -- bring a decode step's metadata to the device.

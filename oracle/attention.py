@@ -5,8 +5,9 @@ What is computed (one new query token per sequence):
      block table[i], and copy tokens 0..L-1 into a contiguous buffer
      ("From OOM to Smooth Inference (RAG memory management)", §2.1;
      "Inference Engine Memory Optimisation", §2.2). fp16 values convert to
-     float64 exactly; fp8 bytes become decode(byte) * scale
-     ("Where Did the VRAM Go (KV cache tutorial)", §6.1).
+     float64 exactly; fp8 bytes (e4m3 or e5m2) become decode(byte) * scale
+     with one scale per tensor or per KV head ("Where Did the VRAM Go (KV
+     cache tutorial)", §6.1-6.3).
   2. For query head h, the KV head is h // (Hq / Hkv) (contiguous groups; the
      pages do not say, this is the reading taken).
   3. z_t = sm_scale * <q_h, K_t>;  p_t = exp(z_t - max z);  out = sum p_t V_t / sum p_t.
@@ -29,8 +30,8 @@ def gather_sequence(cache, table, length, block_size, kv_dtype="f16", scale=1.0)
         phys = int(table[t // block_size])
         n = min(block_size, length - t)
         rows = cache[phys, :, :n, :]  # [Hkv, n, D]
-        if kv_dtype == "fp8":
-            vals = fp8.dequantize(rows, scale)
+        if kv_dtype in fp8.KV_FORMATS:
+            vals = fp8.dequantize(rows, scale, fp8.KV_FORMATS[kv_dtype])  # per tensor or per KV head
         else:
             vals = rows.astype(np.float64)
         out[t:t + n] = np.transpose(vals, (1, 0, 2))

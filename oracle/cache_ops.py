@@ -6,9 +6,10 @@ A slot is block * block_size + offset: the page-table mapping of
 of a sequence is stored in physical block table[i]; token t sits at offset
 t mod block_size of logical block t // block_size).
 
-fp16 caches store the value unchanged. fp8 caches store
+fp16 caches store the value unchanged. fp8 caches (e4m3, or e5m2) store
 encode(float32(x) * float32(inv_scale)) per "Where Did the VRAM Go (KV cache
-tutorial)", §6.1-6.2 (see oracle.fp8).
+tutorial)", §6.1-6.3 (see oracle.fp8); inv_scale is one value per tensor or
+one per KV head.
 """
 from __future__ import annotations
 
@@ -25,9 +26,10 @@ def scatter(k_cache, v_cache, k_new, v_new, slot_mapping, block_size,
     """
     k_new = np.asarray(k_new)
     v_new = np.asarray(v_new)
-    if kv_dtype == "fp8":
-        k_src = fp8.quantize(k_new, k_inv_scale)
-        v_src = fp8.quantize(v_new, v_inv_scale)
+    if kv_dtype in fp8.KV_FORMATS:
+        fmt = fp8.KV_FORMATS[kv_dtype]
+        k_src = fp8.quantize(k_new, k_inv_scale, fmt)
+        v_src = fp8.quantize(v_new, v_inv_scale, fmt)
     else:
         k_src, v_src = k_new, v_new
     for i, slot in enumerate(np.asarray(slot_mapping).tolist()):

@@ -29,7 +29,7 @@ FP8_NAN_BITS = 0x7F
 
 def empty_cache(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype):
     shape = (num_blocks, num_kv_heads, block_size, head_dim)
-    if kv_dtype == "fp8":
+    if kv_dtype != "f16":  # 0x7F is a NaN in both e4m3fn and e5m2
         return np.full(shape, FP8_NAN_BITS, dtype=np.uint8)
     return np.full(shape, F16_NAN_BITS, dtype=np.uint16).view(np.float16)
 

@@ -21,6 +21,7 @@ PKV_ERR_HIP = -5
 
 KV_F16 = 0
 KV_FP8_E4M3 = 1
+KV_FP8_E5M2 = 2
 
 SWAP_OUT = 0
 SWAP_IN = 1
@@ -64,6 +65,17 @@ SIGNATURES = {
     "paged_kv_write_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _c_f, _c_f, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
                                      _c_int, _vp]),
+    "paged_kv_write_scaled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _vp, _vp, _vp]),
+    "paged_kv_write_step_scaled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
+                                            _c_int, _vp]),
+    "paged_attn_decode_scaled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_f, _c_int, _vp, _vp, _c_int, _vp, _c_sz,
+                                          _c_int, _vp]),
+    "paged_attn_prefill_scaled": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _c_int,
+                                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp, _vp,
+                                           _vp]),
     "paged_block_copy": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_sz, _vp]),
     "paged_block_swap": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_sz, _c_int, _vp]),
     "paged_attn_decode_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),

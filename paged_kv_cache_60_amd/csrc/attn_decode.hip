@@ -4,8 +4,9 @@
 // a sequence lives in physical block table[i] ("From OOM to Smooth Inference
 // (RAG memory management)", §2.1; "Inference Engine Memory Optimisation",
 // §2.2). The output is plain softmax attention over the sequence's tokens.
-// With an fp8 e4m3 cache K and V are dequantised with one scale per tensor
-// ("Where Did the VRAM Go (KV cache tutorial)", §6.1-6.3).
+// With an fp8 cache (e4m3 or e5m2) K and V are dequantised with one scale per
+// tensor or one per KV head ("Where Did the VRAM Go (KV cache tutorial)",
+// §6.1-6.3).
 //
 // Work decomposition (split-sequence, stream-K style). A segment is one
 // (sequence, KV head); its tokens are cut into units of 16 tokens (32 on the
@@ -78,7 +79,21 @@ struct AttnArgs {
   int workers;        // W, a multiple of kWaves
   float qk_scale;     // sm_scale * log2(e), times k_scale for fp8
   float v_out_scale;  // v_scale for fp8, else 1
+  // one scale per KV head (device memory), or null: then qk_scale and
+  // v_out_scale hold for every head; else head h uses qk_base * k_scale_h[h]
+  // and v_scale_h[h]
+  const float* k_scale_h;
+  const float* v_scale_h;
+  float qk_base;      // sm_scale * log2(e)
 };
+
+// The logit and output scales of KV head h.
+__device__ __forceinline__ float head_qk_scale(const AttnArgs& a, int h) {
+  return a.k_scale_h ? a.qk_base * a.k_scale_h[h] : a.qk_scale;
+}
+__device__ __forceinline__ float head_v_scale(const AttnArgs& a, int h) {
+  return a.v_scale_h ? a.v_scale_h[h] : a.v_out_scale;
+}
 
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
 
@@ -178,8 +193,9 @@ __device__ __forceinline__ int64_t worker_index(int wave, int NW) {
   return (int64_t)wg * NW + wave;
 }
 
-template <int D, int G, bool FP8, int NW>
+template <int D, int G, int FMT, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
+  constexpr bool FP8 = FMT != kF16;
   constexpr int ELEM = FP8 ? 1 : 2;
   constexpr int RB = D * ELEM;       // bytes of one token row of one head
   constexpr int LPR = RB / 16;       // lanes per row
@@ -215,6 +231,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
+    const float qk_scale = head_qk_scale(a, pc.head);
+    const float v_scale = head_v_scale(a, pc.head);
 
     // Query fragments: head hq0+g, elements c*E .. c*E+E-1, as fp16 pairs.
     uint32_t qf[G][W];
@@ -285,7 +303,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 #pragma unroll
           for (int x = 0; x < W; ++x) {
             if constexpr (FP8)
-              kw[x] = (x & 1) ? fp8x2_hi_to_f16x2(kr[i][x / 2]) : fp8x2_lo_to_f16x2(kr[i][x / 2]);
+              kw[x] = fp8x2_to_f16x2<FMT>(kr[i][x / 2], x & 1);
             else
               kw[x] = kr[i][x];
           }
@@ -295,7 +313,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 #pragma unroll
             for (int x = 0; x < W; ++x) s = dot2(qf[g][x], kw[x], s);
             s = group_sum<LPR>(s);
-            z[i][g] = valid[i] ? s * a.qk_scale : -INFINITY;
+            z[i][g] = valid[i] ? s * qk_scale : -INFINITY;
           }
         }
 
@@ -327,7 +345,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
           for (int x = 0; x < W; ++x) {
             uint32_t pw;
             if constexpr (FP8)
-              pw = (x & 1) ? fp8x2_hi_to_f16x2(vr[i][x / 2]) : fp8x2_lo_to_f16x2(vr[i][x / 2]);
+              pw = fp8x2_to_f16x2<FMT>(vr[i][x / 2], x & 1);
             else
               pw = vr[i][x];
             vf[2 * x] = h_lo(pw);
@@ -366,7 +384,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         if (whole) {
-          const float sc = l[g] > 0.0f ? a.v_out_scale / l[g] : 0.0f;
+          const float sc = l[g] > 0.0f ? v_scale / l[g] : 0.0f;
           f16* o = a.out + ((size_t)seq * a.Hq + hq0 + g) * D + c * E;
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = (f16)(acc[g][e] * sc);
@@ -374,7 +392,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
           const size_t pi = ((size_t)w * 2 + slot) * G + g;
           float* o = a.ws_o + pi * D + c * E;
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = acc[g][e] * a.v_out_scale;
+          for (int e = 0; e < E; ++e) o[e] = acc[g][e] * v_scale;
           if (lane == 0) {
             a.ws_ml[2 * pi] = m[g];
             a.ws_ml[2 * pi + 1] = l[g];
@@ -488,20 +506,30 @@ namespace {
 
 typedef void (*KernFn)(AttnArgs);
 
-template <int D, bool FP8>
+template <int D, int FMT>
 KernFn pick_partition_kernel(int G) {
   switch (G) {
-    case 1: return attn_partition_kernel<D, 1, FP8, kWaves>;
-    case 2: return attn_partition_kernel<D, 2, FP8, kWaves>;
-    case 4: return attn_partition_mfma_kernel<D, 4, FP8, kWaves>;
-    case 8: return attn_partition_mfma_kernel<D, 8, FP8, kWaves>;
+    case 1: return attn_partition_kernel<D, 1, FMT, kWaves>;
+    case 2: return attn_partition_kernel<D, 2, FMT, kWaves>;
+    case 4: return attn_partition_mfma_kernel<D, 4, FMT, kWaves>;
+    case 8: return attn_partition_mfma_kernel<D, 8, FMT, kWaves>;
     default: return nullptr;
   }
 }
 
-KernFn pick(int D, int G, bool fp8) {
-  if (D == 64) return fp8 ? pick_partition_kernel<64, true>(G) : pick_partition_kernel<64, false>(G);
-  if (D == 128) return fp8 ? pick_partition_kernel<128, true>(G) : pick_partition_kernel<128, false>(G);
+template <int D>
+KernFn pick_fmt(int G, int fmt) {
+  switch (fmt) {
+    case kF16: return pick_partition_kernel<D, kF16>(G);
+    case kE4M3: return pick_partition_kernel<D, kE4M3>(G);
+    case kE5M2: return pick_partition_kernel<D, kE5M2>(G);
+    default: return nullptr;
+  }
+}
+
+KernFn pick(int D, int G, int fmt) {
+  if (D == 64) return pick_fmt<64>(G, fmt);
+  if (D == 128) return pick_fmt<128>(G, fmt);
   return nullptr;
 }
 
@@ -599,10 +627,11 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_INVALID;
   if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
-  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3 && kv_dtype != PKV_KV_FP8_E5M2)
+    return PKV_ERR_INVALID;
   if (partition_tokens < 0 || partition_tokens % kTile != 0) return PKV_ERR_INVALID;
   const int G = num_q_heads / num_kv_heads;
-  p->fn = pick(head_dim, G, kv_dtype == PKV_KV_FP8_E4M3);
+  p->fn = pick(head_dim, G, kv_dtype);
   p->reduce = pick_reduce(head_dim, G);
   if (!p->fn || !p->reduce) return PKV_ERR_INVALID;
   p->unit = unit_tokens_for(G);
@@ -621,7 +650,7 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
     int wgs = 0, cus = 0;
     if (!device_capacity(p->fn, dyn_lds_bytes(B), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
-    const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype == PKV_KV_FP8_E4M3) * 4 * cus;
+    const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype != PKV_KV_F16) * 4 * cus;
     if (W > by_simd) W = by_simd;
   }
   if (W > ub_all) W = ub_all;
@@ -660,15 +689,14 @@ extern "C" size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_head
   return (bytes + 255) / 256 * 256;
 }
 
-extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_cache,
-                                        const void* v_cache, const int32_t* block_tables,
-                                        int max_blocks_per_seq, const int32_t* ctx_lens,
-                                        int num_seqs, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int block_size, int num_blocks,
-                                        float sm_scale, int kv_dtype, float k_scale,
-                                        float v_scale, int partition_tokens, void* workspace,
-                                        size_t workspace_bytes, int passes, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                int max_blocks_per_seq, const int32_t* ctx_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_dim, int block_size, int num_blocks, float sm_scale, int kv_dtype, float k_scale,
+                float v_scale, const float* k_scales, const float* v_scales, int partition_tokens,
+                void* workspace, size_t workspace_bytes, int passes, void* stream) {
   if (passes < 1 || passes > 3 || num_blocks <= 0) return PKV_ERR_INVALID;
   Plan pl;
   int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
@@ -684,7 +712,7 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
   if (rc != PKV_OK) return rc;
 
   const int G = num_q_heads / num_kv_heads;
-  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
+  const bool fp8 = kv_dtype != PKV_KV_F16;
   const float kLog2e = 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // more than kMaxSeqs sequences: consecutive launches, in order on the stream
@@ -710,6 +738,9 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
     a.workers = pl.workers;
     a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
     a.v_out_scale = fp8 ? v_scale : 1.0f;
+    a.k_scale_h = fp8 ? k_scales : nullptr;
+    a.v_scale_h = fp8 ? v_scales : nullptr;
+    a.qk_base = sm_scale * kLog2e;
     if (passes & 1) {
       hipLaunchKernelGGL(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64), dyn_lds_bytes(B), s, a);
       if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
@@ -721,6 +752,37 @@ extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_
     }
   }
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attn_decode_passes(void* out, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* ctx_lens,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int num_blocks,
+                                        float sm_scale, int kv_dtype, float k_scale,
+                                        float v_scale, int partition_tokens, void* workspace,
+                                        size_t workspace_bytes, int passes, void* stream) {
+  return pkv::decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale, kv_dtype,
+                          k_scale, v_scale, nullptr, nullptr, partition_tokens, workspace, workspace_bytes,
+                          passes, stream);
+}
+
+extern "C" int paged_attn_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                        float sm_scale, int kv_dtype, const float* k_scales,
+                                        const float* v_scales, int partition_tokens, void* workspace,
+                                        size_t workspace_bytes, int passes, void* stream) {
+  if (kv_dtype != PKV_KV_F16 && num_seqs > 0 && (!k_scales || !v_scales)) return PKV_ERR_INVALID;
+  return pkv::decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale, kv_dtype,
+                          1.0f, 1.0f, k_scales, v_scales, partition_tokens, workspace, workspace_bytes, passes,
+                          stream);
 }
 
 extern "C" int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -36,19 +36,21 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ f16x8 f16x8_from_u32x4(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // 8 fp8 bytes (two dwords) -> 8 fp16 values, exactly
+template <int FMT>
 __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = fp8x2_lo_to_f16x2(w0);
-  r[1] = fp8x2_hi_to_f16x2(w0);
-  r[2] = fp8x2_lo_to_f16x2(w1);
-  r[3] = fp8x2_hi_to_f16x2(w1);
+  r[0] = fp8x2_to_f16x2<FMT>(w0, false);
+  r[1] = fp8x2_to_f16x2<FMT>(w0, true);
+  r[2] = fp8x2_to_f16x2<FMT>(w1, false);
+  r[3] = fp8x2_to_f16x2<FMT>(w1, true);
   return __builtin_bit_cast(f16x8, r);
 }
 
-template <int D, int G, bool FP8, int NW>
+template <int D, int G, int FMT, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a) {
   static_assert(G == 4 || G == 8, "group size");
   static_assert(D == 64 || D == 128, "head_dim");
+  constexpr bool FP8 = FMT != kF16;
   constexpr int ELEM = FP8 ? 1 : 2;
   constexpr int RB = D * ELEM;          // bytes of one token row of one head
   constexpr int KM = D / 32;            // q.k MFMAs per tile
@@ -95,6 +97,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
+    const float qk_scale = head_qk_scale(a, pc.head);
+    const float v_scale = head_v_scale(a, pc.head);
 
     // Q^T as the B operand: head = col (zero past G), d = grp * DQ + 8m + slot
     f16x8 qb[KM];
@@ -161,8 +165,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         for (int m = 0; m < KM; ++m) {
           f16x8 aa, ab;
           if constexpr (FP8) {
-            aa = fp8x8_to_f16x8(ka[m / 2][(m % 2) * 2], ka[m / 2][(m % 2) * 2 + 1]);
-            ab = fp8x8_to_f16x8(kb[m / 2][(m % 2) * 2], kb[m / 2][(m % 2) * 2 + 1]);
+            aa = fp8x8_to_f16x8<FMT>(ka[m / 2][(m % 2) * 2], ka[m / 2][(m % 2) * 2 + 1]);
+            ab = fp8x8_to_f16x8<FMT>(kb[m / 2][(m % 2) * 2], kb[m / 2][(m % 2) * 2 + 1]);
           } else {
             aa = f16x8_from_u32x4(ka[m]);
             ab = f16x8_from_u32x4(kb[m]);
@@ -177,8 +181,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         for (int v = 0; v < 4; ++v) {
           const int tka = ta + 4 * grp + v;
           const int tkb = ta + 16 + 4 * grp + v;
-          z[v] = (ok_a && tka < L) ? sa[v] * a.qk_scale : -INFINITY;
-          z[4 + v] = (ok_b && tkb < L) ? sb[v] * a.qk_scale : -INFINITY;
+          z[v] = (ok_a && tka < L) ? sa[v] * qk_scale : -INFINITY;
+          z[4 + v] = (ok_b && tkb < L) ? sb[v] * qk_scale : -INFINITY;
         }
         float mt = z[0];
 #pragma unroll
@@ -208,8 +212,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           const bool ok = (r < 16 ? ok_a : ok_b) && (ta + r < L);
           _Float16* dst = vbuf + r * VS + v_cb / ELEM;
           if constexpr (FP8) {
-            const f16x8 lo = ok ? fp8x8_to_f16x8(vv[i][0], vv[i][1]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            const f16x8 hi = ok ? fp8x8_to_f16x8(vv[i][2], vv[i][3]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            const f16x8 lo = ok ? fp8x8_to_f16x8<FMT>(vv[i][0], vv[i][1]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            const f16x8 hi = ok ? fp8x8_to_f16x8<FMT>(vv[i][2], vv[i][3]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
             *reinterpret_cast<f16x8*>(dst) = lo;
             *reinterpret_cast<f16x8*>(dst + 8) = hi;
           } else {
@@ -241,7 +245,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const int slot = t == start ? 0 : 1;
     if (col < G) {
       if (whole) {
-        const float sc = l_part > 0.0f ? a.v_out_scale / l_part : 0.0f;
+        const float sc = l_part > 0.0f ? v_scale / l_part : 0.0f;
         f16* orow = a.out + ((size_t)seq * a.Hq + hq0 + col) * D + 4 * grp;
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
@@ -254,7 +258,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         const size_t pi = ((size_t)w * 2 + slot) * G + col;
         float* orow = a.ws_o + pi * D + 4 * grp;
 #pragma unroll
-        for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * a.v_out_scale;
+        for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * v_scale;
         if (grp == 0) {
           a.ws_ml[2 * pi] = m_run;
           a.ws_ml[2 * pi + 1] = l_part;

@@ -16,7 +16,7 @@
 // Each wave holds 32 columns (two 16-column MFMA operands). The workgroup walks
 // the tokens the tile can see, 32 at a time (two 16-token tiles, each inside
 // one block): all 256 threads load the chunk's K and V rows from the cache
-// into LDS as fp16 (fp8 rows widened exactly), double-buffered so that the
+// into LDS as fp16 (fp8 rows, e4m3 or e5m2, widened exactly), double-buffered so that the
 // next chunk's loads are in flight while this one is computed, and every wave
 // then runs, per chunk:
 //   S = K . Q^T       v_mfma_f32_16x16x32_f16, M = 16 tokens, N = 16 columns,
@@ -78,11 +78,19 @@ struct PrefillArgs {
   int tiles_bound;    // tiles per KV head the grid provides (>= the real count)
   float qk_scale;     // sm_scale * log2(e), times k_scale for fp8
   float v_out_scale;  // v_scale for fp8, else 1
+  const float* k_scale_h;  // one scale per KV head (device), or null: qk_scale / v_out_scale hold
+  const float* v_scale_h;
+  float qk_base;           // sm_scale * log2(e)
 };
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
+
+// A float the caller knows is equal on all lanes, moved to a scalar register.
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
 
 // Query rows of sequence s: [first, first + count), or none if q_start puts
 // them outside [0, total_q).
@@ -148,12 +156,13 @@ __device__ __forceinline__ int logical_index() {
 }
 
 // 8 fp8 bytes (two dwords) -> 8 fp16 values, exactly
+template <int FMT>
 __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = fp8x2_lo_to_f16x2(w0);
-  r[1] = fp8x2_hi_to_f16x2(w0);
-  r[2] = fp8x2_lo_to_f16x2(w1);
-  r[3] = fp8x2_hi_to_f16x2(w1);
+  r[0] = fp8x2_to_f16x2<FMT>(w0, false);
+  r[1] = fp8x2_to_f16x2<FMT>(w0, true);
+  r[2] = fp8x2_to_f16x2<FMT>(w1, false);
+  r[3] = fp8x2_to_f16x2<FMT>(w1, true);
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -171,8 +180,9 @@ struct ChunkShape {
 };
 
 // The chunk's K and V pieces that this thread moves: global -> registers.
-template <int D, bool FP8>
+template <int D, int FMT>
 struct Stage {
+  static constexpr bool FP8 = FMT != kF16;
   using S = ChunkShape<D, FP8>;
   u32x4 k[S::PPT];
   u32x4 v[S::PPT];
@@ -218,10 +228,10 @@ struct Stage {
       const u32x4 kk = live[i] ? k[i] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live[i] ? v[i] : u32x4{0u, 0u, 0u, 0u};
       if constexpr (FP8) {
-        *reinterpret_cast<f16x8*>(kd) = fp8x8_to_f16x8(kk[0], kk[1]);
-        *reinterpret_cast<f16x8*>(kd + 8) = fp8x8_to_f16x8(kk[2], kk[3]);
-        *reinterpret_cast<f16x8*>(vd) = fp8x8_to_f16x8(vv[0], vv[1]);
-        *reinterpret_cast<f16x8*>(vd + 8) = fp8x8_to_f16x8(vv[2], vv[3]);
+        *reinterpret_cast<f16x8*>(kd) = fp8x8_to_f16x8<FMT>(kk[0], kk[1]);
+        *reinterpret_cast<f16x8*>(kd + 8) = fp8x8_to_f16x8<FMT>(kk[2], kk[3]);
+        *reinterpret_cast<f16x8*>(vd) = fp8x8_to_f16x8<FMT>(vv[0], vv[1]);
+        *reinterpret_cast<f16x8*>(vd + 8) = fp8x8_to_f16x8<FMT>(vv[2], vv[3]);
       } else {
         *reinterpret_cast<u32x4*>(kd) = kk;
         *reinterpret_cast<u32x4*>(vd) = vv;
@@ -233,10 +243,11 @@ struct Stage {
 // three workgroups per compute unit (3 waves per SIMD) hide the LDS and
 // matrix-core latencies of the token loop far better than two (measured on
 // MI355X: 10.7 -> 8.4 ms on the Qwen3-shaped prefix-cache prefill)
-template <int D, int G, bool FP8>
+template <int D, int G, int FMT>
 __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArgs a) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(D == 64 || D == 128, "head_dim");
+  constexpr bool FP8 = FMT != kF16;
   using S = ChunkShape<D, FP8>;
   constexpr int KM = D / 32;   // q.k MFMAs per 16-token tile and column group
   constexpr int NT = D / 16;   // output head-dim tiles
@@ -272,6 +283,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
+  const float qk_scale = uniform_f32(a.k_scale_h ? a.qk_base * a.k_scale_h[head] : a.qk_scale);
 
   // Q^T operands (B of S = K Q^T): column c = 32 wave + 16 cg + col holds query
   // token c / G, head c % G of the group; d = grp * DQ + 8 m + slot
@@ -327,7 +339,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
     *bb = t0 + 16 < kend ? __builtin_amdgcn_readlane(lane_blk, tl + 1 - tile0) : -1;
   };
 
-  Stage<D, FP8> st;
+  Stage<D, FMT> st;
   int ba = -1, bb = -1;
   if (nchunks > 0) {
     chunk_blocks(0, &ba, &bb);
@@ -392,7 +404,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
       float m = z[cg][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) m = fmaxf(m, z[cg][i]);
-      mt[cg] = m * a.qk_scale;
+      mt[cg] = m * qk_scale;
     }
     const bool need = mt[0] > m_run[0] + kLazy || mt[1] > m_run[1] + kLazy;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -416,7 +428,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
       float ps = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(z[cg][i], a.qk_scale, neg_m));
+        const float p = fast_exp2(__builtin_fmaf(z[cg][i], qk_scale, neg_m));
         ps += p;
         pb[cg][i] = (_Float16)p;
       }
@@ -442,6 +454,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
     bb = nbb;
   }
 
+  const float v_scale = uniform_f32(a.v_scale_h ? a.v_scale_h[head] : a.v_out_scale);
   // per-column sums over the four lane groups (the max is already common);
   // lane (col, grp) holds d = 16c + 4grp + v of its column
 #pragma unroll
@@ -452,7 +465,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
     const int c = wave * kCols + cg * 16 + col;
     const int tl = c / G;
     if (tl < nt) {
-      const float sc = l > 0.0f ? a.v_out_scale / l : 0.0f;
+      const float sc = l > 0.0f ? v_scale / l : 0.0f;
       f16* orow = a.out + ((size_t)(qfirst + row0 + tl) * a.Hq + head * G + c % G) * D + 4 * grp;
 #pragma unroll
       for (int cc = 0; cc < NT; ++cc) {
@@ -467,20 +480,30 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
 
 typedef void (*PrefillFn)(PrefillArgs);
 
-template <int D, bool FP8>
+template <int D, int FMT>
 PrefillFn pick_d(int G) {
   switch (G) {
-    case 1: return attn_prefill_kernel<D, 1, FP8>;
-    case 2: return attn_prefill_kernel<D, 2, FP8>;
-    case 4: return attn_prefill_kernel<D, 4, FP8>;
-    case 8: return attn_prefill_kernel<D, 8, FP8>;
+    case 1: return attn_prefill_kernel<D, 1, FMT>;
+    case 2: return attn_prefill_kernel<D, 2, FMT>;
+    case 4: return attn_prefill_kernel<D, 4, FMT>;
+    case 8: return attn_prefill_kernel<D, 8, FMT>;
     default: return nullptr;
   }
 }
 
-PrefillFn pick(int D, int G, bool fp8) {
-  if (D == 64) return fp8 ? pick_d<64, true>(G) : pick_d<64, false>(G);
-  if (D == 128) return fp8 ? pick_d<128, true>(G) : pick_d<128, false>(G);
+template <int D>
+PrefillFn pick_fmt(int G, int fmt) {
+  switch (fmt) {
+    case kF16: return pick_d<D, kF16>(G);
+    case kE4M3: return pick_d<D, kE4M3>(G);
+    case kE5M2: return pick_d<D, kE5M2>(G);
+    default: return nullptr;
+  }
+}
+
+PrefillFn pick(int D, int G, int fmt) {
+  if (D == 64) return pick_fmt<64>(G, fmt);
+  if (D == 128) return pick_fmt<128>(G, fmt);
   return nullptr;
 }
 
@@ -493,27 +516,29 @@ int log2_exact(int v) {
 }  // namespace
 }  // namespace pkv
 
-extern "C" int paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_tables, int max_blocks_per_seq,
-                                  const int32_t* ctx_lens, const int32_t* q_start, int num_seqs,
-                                  int total_q, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int num_blocks, float sm_scale, int kv_dtype,
-                                  float k_scale, float v_scale, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                 int max_blocks_per_seq, const int32_t* ctx_lens, const int32_t* q_start, int num_seqs, int total_q,
+                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks, float sm_scale,
+                 int kv_dtype, float k_scale, float v_scale, const float* k_scales, const float* v_scales,
+                 void* stream) {
   if (num_seqs < 0 || total_q < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
   if (block_size != 16 && block_size != 32 && block_size != 64) return PKV_ERR_INVALID;
-  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3) return PKV_ERR_INVALID;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_FP8_E4M3 && kv_dtype != PKV_KV_FP8_E5M2)
+    return PKV_ERR_INVALID;
   const int G = num_q_heads / num_kv_heads;
-  PrefillFn fn = pick(head_dim, G, kv_dtype == PKV_KV_FP8_E4M3);
+  PrefillFn fn = pick(head_dim, G, kv_dtype);
   if (!fn) return PKV_ERR_INVALID;
   if ((int64_t)max_blocks_per_seq * block_size > 0x7FFFFFFF) return PKV_ERR_INVALID;
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !q_start) return PKV_ERR_INVALID;
 
-  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3;
+  const bool fp8 = kv_dtype != PKV_KV_F16;
   const float kLog2e = 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int b0 = 0; b0 < num_seqs; b0 += kMaxSeqs) {
@@ -540,8 +565,37 @@ extern "C" int paged_attn_prefill(void* out, const void* q, const void* k_cache,
     a.tiles_bound = (int)tiles;
     a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
     a.v_out_scale = fp8 ? v_scale : 1.0f;
+    a.k_scale_h = fp8 ? k_scales : nullptr;
+    a.v_scale_h = fp8 ? v_scales : nullptr;
+    a.qk_base = sm_scale * kLog2e;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* ctx_lens, const int32_t* q_start, int num_seqs,
+                                  int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float sm_scale, int kv_dtype,
+                                  float k_scale, float v_scale, void* stream) {
+  return pkv::prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, q_start,
+                           num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           sm_scale, kv_dtype, k_scale, v_scale, nullptr, nullptr, stream);
+}
+
+extern "C" int paged_attn_prefill_scaled(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* ctx_lens, const int32_t* q_start, int num_seqs,
+                                         int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int num_blocks, float sm_scale, int kv_dtype,
+                                         const float* k_scales, const float* v_scales, void* stream) {
+  if (kv_dtype != PKV_KV_F16 && num_seqs > 0 && total_q > 0 && (!k_scales || !v_scales)) return PKV_ERR_INVALID;
+  return pkv::prefill_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, q_start,
+                           num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           sm_scale, kv_dtype, 1.0f, 1.0f, k_scales, v_scales, stream);
 }

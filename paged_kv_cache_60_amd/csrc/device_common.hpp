@@ -60,4 +60,28 @@ __device__ __forceinline__ uint32_t fp8x2_hi_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
+// Cache element formats: fp16, OCP fp8 e4m3fn, OCP fp8 e5m2 (the values of
+// pkv_kv_dtype).
+enum KvFmt { kF16 = 0, kE4M3 = 1, kE5M2 = 2 };
+
+// e5m2 bytes to fp16 pairs: e5m2 is the top byte of an fp16 with the same
+// exponent layout, so each byte moves to the high byte of its half (exact).
+// v_perm_b32 with the word in both sources: selector 0x0C writes 0x00.
+__device__ __forceinline__ uint32_t e5m2x2_lo_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x010C000Cu);  // bytes [0, b0, 0, b1]
+}
+__device__ __forceinline__ uint32_t e5m2x2_hi_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x030C020Cu);  // bytes [0, b2, 0, b3]
+}
+
+// Bytes 0, 1 (lo) or 2, 3 (hi) of a word of fp8 codes as an fp16 pair.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool hi) {
+  static_assert(FMT == kE4M3 || FMT == kE5M2, "fp8 format");
+  if constexpr (FMT == kE4M3)
+    return hi ? fp8x2_hi_to_f16x2(w) : fp8x2_lo_to_f16x2(w);
+  else
+    return hi ? e5m2x2_hi_to_f16x2(w) : e5m2x2_lo_to_f16x2(w);
+}
+
 }  // namespace pkv

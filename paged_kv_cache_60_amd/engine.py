@@ -45,9 +45,10 @@ class PagedKVEngine:
         self.num_blocks = int(num_blocks)
         self.hq, self.hkv, self.d, self.bs = int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size)
         self.kv_dtype = kv_dtype
-        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
-        self.k_inv_scale, self.v_inv_scale = float(k_inv_scale), float(v_inv_scale)
         self.device = torch.device(device)
+        # fp8 scales: one per tensor (numbers) or one per KV head (float32 device tensors)
+        self.k_scale, self.v_scale, self.k_inv_scale, self.v_inv_scale = (
+            self._scale(x) for x in (k_scale, v_scale, k_inv_scale, v_inv_scale))
         self.bm = BlockManager(self.num_blocks, self.bs, free_order)
         shape = (self.num_blocks, self.hkv, self.bs, self.d)
         dt = ops.cache_torch_dtype(kv_dtype)
@@ -64,6 +65,12 @@ class PagedKVEngine:
             self.bm.set_host_blocks(self.num_host_blocks)
         if poison:
             self.poison()
+
+    def _scale(self, x):
+        a = np.asarray(x)
+        if a.ndim == 0:
+            return float(a)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.device)
 
     @property
     def block_bytes(self) -> int:

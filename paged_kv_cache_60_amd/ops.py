@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import PkvError, check
 
 F16 = "f16"
-FP8 = "fp8"
+FP8 = "fp8"            # OCP e4m3fn
+FP8_E5M2 = "fp8_e5m2"  # OCP e5m2
 
 
 def kv_dtype_code(kv_dtype: str) -> int:
@@ -22,11 +23,23 @@ def kv_dtype_code(kv_dtype: str) -> int:
         return _lib.KV_F16
     if kv_dtype == FP8:
         return _lib.KV_FP8_E4M3
+    if kv_dtype == FP8_E5M2:
+        return _lib.KV_FP8_E5M2
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
 def cache_torch_dtype(kv_dtype: str) -> torch.dtype:
     return torch.float16 if kv_dtype == F16 else torch.uint8
+
+
+def _per_head(scale) -> bool:
+    """A scale given as a device tensor holds one value per KV head (the *_scaled
+    entry points); a Python number is one value for the whole tensor."""
+    return isinstance(scale, torch.Tensor)
+
+
+def _scales_ok(k, v, hkv) -> bool:
+    return all(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.shape == (hkv,) for t in (k, v))
 
 
 def _stream_ptr(stream=None) -> ctypes.c_void_p:
@@ -51,7 +64,8 @@ def _cache_ok(c: torch.Tensor, kv_dtype: str) -> bool:
 
 def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, kv_dtype=F16,
                    k_inv_scale=1.0, v_inv_scale=1.0, stream=None):
-    """Scatter k_new/v_new [T, Hkv, D] (fp16) into the caches at slot_mapping [T] (int64)."""
+    """Scatter k_new/v_new [T, Hkv, D] (fp16) into the caches at slot_mapping [T] (int64).
+    fp8 multipliers: Python numbers (one per tensor) or float32 device tensors [Hkv] (one per KV head)."""
     w = "paged_kv_write"
     _require(k_new.is_cuda and k_new.dtype == torch.float16 and k_new.is_contiguous(), w, "k_new")
     _require(v_new.shape == k_new.shape and v_new.dtype == torch.float16 and v_new.is_contiguous(), w, "v_new")
@@ -63,6 +77,12 @@ def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, kv_dtype=F16,
     _require(slot_mapping.is_cuda and slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
              and slot_mapping.is_contiguous(), w, "slot_mapping")
     lib = _lib.load()
+    if _per_head(k_inv_scale):
+        _require(_scales_ok(k_inv_scale, v_inv_scale, hkv), w, "per-head inverse scales")
+        check(lib.paged_kv_write_scaled(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T, nb,
+                                        hkv, d, bs, kv_dtype_code(kv_dtype), _p(k_inv_scale), _p(v_inv_scale),
+                                        _stream_ptr(stream)), w)
+        return
     check(lib.paged_kv_write(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T, nb,
                              hkv, d, bs, kv_dtype_code(kv_dtype), float(k_inv_scale), float(v_inv_scale),
                              _stream_ptr(stream)), w)
@@ -131,6 +151,14 @@ def paged_kv_write_step(k_new, v_new, k_cache, v_cache, slot_mapping, ctx_src, c
     _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2, w, "tables")
     rows, maxb = block_tables.shape
     lib = _lib.load()
+    if _per_head(k_inv_scale):
+        _require(_scales_ok(k_inv_scale, v_inv_scale, hkv), w, "per-head inverse scales")
+        check(lib.paged_kv_write_step_scaled(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T,
+                                             nb, hkv, d, bs, kv_dtype_code(kv_dtype), _p(k_inv_scale),
+                                             _p(v_inv_scale), _p(ctx_src), _p(ctx_dst), ctx_dst.numel(),
+                                             _p(updates), int(n_updates), _p(block_tables), rows, maxb,
+                                             _stream_ptr(stream)), w)
+        return
     check(lib.paged_kv_write_step(_p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(slot_mapping), T, nb,
                                   hkv, d, bs, kv_dtype_code(kv_dtype), float(k_inv_scale), float(v_inv_scale),
                                   _p(ctx_src), _p(ctx_dst), ctx_dst.numel(), _p(updates), int(n_updates),
@@ -181,6 +209,14 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
                  "workspace too small")
         ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
     lib = _lib.load()
+    if _per_head(k_scale):
+        _require(_scales_ok(k_scale, v_scale, hkv), w, "per-head scales")
+        check(lib.paged_attn_decode_scaled(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), maxb,
+                                           _p(ctx_lens), B, hq, hkv, d, bs, nb, float(sm_scale),
+                                           kv_dtype_code(kv_dtype), _p(k_scale), _p(v_scale),
+                                           int(partition_tokens), ws_ptr, ws_bytes, int(passes),
+                                           _stream_ptr(stream)), w)
+        return
     check(lib.paged_attn_decode_passes(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), maxb,
                                        _p(ctx_lens), B, hq, hkv, d, bs, nb, float(sm_scale),
                                        kv_dtype_code(kv_dtype), float(k_scale), float(v_scale),
@@ -208,6 +244,13 @@ def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start
     _require(q_start.is_cuda and q_start.dtype == torch.int32 and q_start.shape == (B + 1,)
              and q_start.is_contiguous(), w, "q_start")
     lib = _lib.load()
+    if _per_head(k_scale):
+        _require(_scales_ok(k_scale, v_scale, hkv), w, "per-head scales")
+        check(lib.paged_attn_prefill_scaled(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                            block_tables.shape[1], _p(ctx_lens), _p(q_start), B, total, hq, hkv,
+                                            d, bs, nb, float(sm_scale), kv_dtype_code(kv_dtype), _p(k_scale),
+                                            _p(v_scale), _stream_ptr(stream)), w)
+        return
     check(lib.paged_attn_prefill(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
                                  block_tables.shape[1], _p(ctx_lens), _p(q_start), B, total, hq, hkv, d, bs,
                                  nb, float(sm_scale), kv_dtype_code(kv_dtype), float(k_scale), float(v_scale),

@@ -6,7 +6,7 @@ import sys
 import numpy as np
 import torch
 
-TOL = {"f16": (2e-3, 1e-2), "fp8": (3e-2, 1e-2)}  # (atol, rtol) per KV dtype
+TOL = {"f16": (2e-3, 1e-2), "fp8": (3e-2, 1e-2), "fp8_e5m2": (3e-2, 1e-2)}  # (atol, rtol) per KV dtype
 
 
 def log(*a):

@@ -78,6 +78,27 @@ def test_config5_beam_fp8_full_size():
     _check(wl, steps=2, seqs=sample_seqs(wl.meta["lengths"], 10))
 
 
+@pytest.mark.parametrize("kv_dtype,per_head", [("fp8_e5m2", False), ("fp8", True), ("fp8_e5m2", True)])
+def test_config5_beam_fp8_variants_full_size(kv_dtype, per_head):
+    """The beam workload with e5m2 storage and/or one scale per KV head."""
+    wl = workloads.beam_fp8(max_steps=2, kv_dtype=kv_dtype, per_head=per_head)
+    _check(wl, steps=2, seqs=sample_seqs(wl.meta["lengths"], 8))
+
+
+def test_per_head_scales_all_equal_match_per_tensor_bits():
+    """Per-head scales that are all equal give the per-tensor results bit for bit
+    (the same fp32 products in the same order)."""
+    wl = workloads.beam_fp8(prompts=6, max_steps=1)
+    eng, outs, _ = _gpu_run(wl, 1)
+    hkv = wl.num_kv_heads
+    wl2 = workloads.beam_fp8(prompts=6, max_steps=1)
+    for name in ("k_scale", "v_scale", "k_inv_scale", "v_inv_scale"):
+        setattr(wl2, name, np.full(hkv, getattr(wl, name), dtype=np.float32))
+    eng2, outs2, _ = _gpu_run(wl2, 1)
+    assert np.array_equal(cache_bits(eng.k_cache), cache_bits(eng2.k_cache))
+    assert np.array_equal(outs[0].view(np.uint16), outs2[0].view(np.uint16))
+
+
 def test_copy_on_write_inside_decode_steps():
     """Every beam's first tail token is written by a decode step: the step's
     copy-on-write pairs go through paged_step_metadata and paged_block_copy."""
@@ -87,7 +108,8 @@ def test_copy_on_write_inside_decode_steps():
 
 @pytest.mark.parametrize("hq,hkv,d,bs,kv", [(8, 8, 64, 16, "f16"), (16, 8, 128, 16, "f16"),
                                            (32, 8, 128, 32, "f16"), (64, 8, 128, 64, "fp8"),
-                                           (8, 2, 64, 64, "fp8"), (16, 16, 128, 64, "fp8")])
+                                           (8, 2, 64, 64, "fp8"), (16, 16, 128, 64, "fp8"),
+                                           (32, 8, 128, 16, "fp8_e5m2"), (16, 16, 64, 32, "fp8_e5m2")])
 def test_small_shapes_all_outputs(hq, hkv, d, bs, kv):
     # ragged lengths: 1, block boundaries +-1, many splits, one long
     L = [1, 2, bs - 1, bs, bs + 1, 63, 64, 65, 511, 512, 513, 1500]

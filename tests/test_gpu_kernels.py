@@ -30,7 +30,7 @@ def _caches(nb, hkv, bs, d, kv_dtype):
     return o_k, o_v, g_k, g_v
 
 
-@pytest.mark.parametrize("kv_dtype", ["f16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8", "fp8_e5m2"])
 @pytest.mark.parametrize("hkv,d,bs", [(8, 64, 16), (32, 128, 16), (40, 128, 32), (8, 128, 64)])
 def test_kv_write_bit_exact(kv_dtype, hkv, d, bs):
     log(f"kv_write {kv_dtype} hkv={hkv} d={d} bs={bs}")
@@ -54,10 +54,13 @@ def test_kv_write_bit_exact(kv_dtype, hkv, d, bs):
     assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
 
 
-@pytest.mark.parametrize("inv_scale", [1.0, 448.0 / 5.25, 0.731, 81.37])
-def test_kv_write_fp8_every_fp16_value(inv_scale):
+@pytest.mark.parametrize("kv_dtype,inv_scale", [("fp8", 1.0), ("fp8", 448.0 / 5.25), ("fp8", 0.731), ("fp8", 81.37),
+                                               ("fp8_e5m2", 1.0), ("fp8_e5m2", 57344.0 / 5.25),
+                                               ("fp8_e5m2", 0.731), ("fp8_e5m2", 4096.0)])
+def test_kv_write_fp8_every_fp16_value(kv_dtype, inv_scale):
     """Every finite fp16 input through the device encoder, against the oracle codec."""
-    log(f"fp8 exhaustive inv_scale={inv_scale}")
+    log(f"{kv_dtype} exhaustive inv_scale={inv_scale}")
+    fmt = fp8.KV_FORMATS[kv_dtype]
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x = bits.view(np.float16)
     x = x[np.isfinite(x)]
@@ -70,15 +73,37 @@ def test_kv_write_fp8_every_fp16_value(inv_scale):
     nb = -(-T // bs)
     slots = np.arange(T, dtype=np.int64)
     kinv = float(np.float32(inv_scale))
-    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, "fp8")
+    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, kv_dtype)
     ops.paged_kv_write(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v,
-                       torch.from_numpy(slots).to(DEV), "fp8", kinv, kinv)
+                       torch.from_numpy(slots).to(DEV), kv_dtype, kinv, kinv)
     torch.cuda.synchronize()
     got = cache_bits(g_k).reshape(-1)[:T * d][:n]
-    want = fp8.quantize(x, kinv)
+    want = fp8.quantize(x, kinv, fmt)
     assert np.array_equal(got, want)
     gotv = cache_bits(g_v).reshape(-1)[:T * d][:n]
-    assert np.array_equal(gotv, fp8.quantize(-x, kinv))
+    assert np.array_equal(gotv, fp8.quantize(-x, kinv, fmt))
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "fp8_e5m2"])
+def test_kv_write_per_head_scales_bit_exact(kv_dtype):
+    """One multiplier per KV head (paged_kv_write_scaled), against the oracle."""
+    g = np.random.default_rng(21)
+    nb, hkv, bs, d, T = 20, 8, 16, 128, 200
+    slots = g.permutation(nb * bs)[:T].astype(np.int64)
+    K = (g.standard_normal((T, hkv, d), dtype=np.float32) * np.arange(1, hkv + 1)[None, :, None]).astype(np.float16)
+    V = g.standard_normal((T, hkv, d), dtype=np.float32).astype(np.float16)
+    fmax = np.float32(448 if kv_dtype == "fp8" else 57344)
+    kinv = fmax / np.abs(K.astype(np.float32)).max(axis=(0, 2))
+    vinv = (fmax / np.abs(V.astype(np.float32)).max(axis=(0, 2))).astype(np.float32)
+    kinv = kinv.astype(np.float32)
+    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, kv_dtype)
+    cache_ops.scatter(o_k, o_v, K, V, slots, bs, kv_dtype, kinv, vinv)
+    ops.paged_kv_write(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v,
+                       torch.from_numpy(slots).to(DEV), kv_dtype, torch.from_numpy(kinv).to(DEV),
+                       torch.from_numpy(vinv).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
+    assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
 
 
 @pytest.mark.parametrize("kv_dtype", ["f16", "fp8"])

@@ -64,9 +64,13 @@ CHUNKS = [1, 15, 3, 17, 30, 64, 1, 129, 513, 0, 9, 0]
 @pytest.mark.parametrize("hq,hkv,d,bs,dt", [
     (8, 8, 64, 16, "f16"), (16, 8, 128, 16, "f16"), (32, 8, 128, 32, "f16"),
     (64, 8, 128, 64, "fp8"), (8, 2, 64, 64, "fp8"), (16, 16, 128, 64, "fp8"), (4, 2, 128, 32, "f16"),
+    (16, 8, 128, 16, "fp8_e5m2"), (32, 8, 64, 32, "fp8_e5m2"), (16, 8, 128, 16, "fp8+ph"),
+    (8, 8, 128, 32, "fp8_e5m2+ph"),
 ])
 def test_small_shapes_all_rows(hq, hkv, d, bs, dt):
-    wl = workloads.small_prefill(100 + hq + d + bs, LENGTHS, CHUNKS, hq, hkv, d, bs, dt)
+    per_head = dt.endswith("+ph")
+    dt = dt.replace("+ph", "")
+    wl = workloads.small_prefill(100 + hq + d + bs, LENGTHS, CHUNKS, hq, hkv, d, bs, dt, per_head=per_head)
     out, o = _check(wl)
     # rows with nothing to attend (the chunk longer than its context) are exact zeros
     r0 = int(o.q_start[10])

@@ -119,28 +119,43 @@ def test_scatter_skips_minus_one_and_block_copy():
     assert np.array_equal(vc[0].view(np.uint16), vc[3].view(np.uint16))
 
 
-def test_fp8_cache_matches_sdpa_on_dequantized_values():
+@pytest.mark.parametrize("kv_dtype,per_head", [("fp8", False), ("fp8_e5m2", False), ("fp8", True),
+                                               ("fp8_e5m2", True)])
+def test_fp8_cache_matches_sdpa_on_dequantized_values(kv_dtype, per_head):
+    """fp8 caches (e4m3 or e5m2, one scale per tensor or per KV head) attend like
+    SDPA on the values torch's own fp8 conversion gives for the same scaled data."""
     g = np.random.default_rng(9)
     L, hkv, hq, d, bs = 23, 2, 8, 16, 8
     K = g.standard_normal((L, hkv, d)).astype(np.float16)
     V = g.standard_normal((L, hkv, d)).astype(np.float16)
-    ks, vs = np.float32(np.abs(K).max()) / np.float32(448), np.float32(np.abs(V).max()) / np.float32(448)
+    V[:, 1] *= 40  # the heads' ranges differ, so per-head scales differ
+    fmax = np.float32(448 if kv_dtype == "fp8" else 57344)
+    tdt = torch.float8_e4m3fn if kv_dtype == "fp8" else torch.float8_e5m2
+    if per_head:
+        ks = np.abs(K).max(axis=(0, 2)).astype(np.float32) / fmax
+        vs = np.abs(V).max(axis=(0, 2)).astype(np.float32) / fmax
+    else:
+        ks, vs = np.float32(np.abs(K).max()) / fmax, np.float32(np.abs(V).max()) / fmax
     kinv, vinv = np.float32(1) / ks, np.float32(1) / vs
-    kc = runner.empty_cache(4, hkv, bs, d, "fp8")
-    vc = runner.empty_cache(4, hkv, bs, d, "fp8")
+    kc = runner.empty_cache(4, hkv, bs, d, kv_dtype)
+    vc = runner.empty_cache(4, hkv, bs, d, kv_dtype)
     table = [2, 0, 3]
     slots = [table[p // bs] * bs + p % bs for p in range(L)]
-    cache_ops.scatter(kc, vc, K, V, slots, bs, "fp8", float(kinv), float(vinv))
+    cache_ops.scatter(kc, vc, K, V, slots, bs, kv_dtype, kinv, vinv)
     q = g.standard_normal((1, hq, d)).astype(np.float16)
-    out = attention.decode_attention(q, kc, vc, [table], [L], bs, 0.25, "fp8", float(ks), float(vs))
-    # library route for the same quantised values: torch's e4m3fn conversion
-    kq = torch.from_numpy(K.astype(np.float32) * kinv).to(torch.float8_e4m3fn).to(torch.float64).numpy() * float(ks)
-    vq = torch.from_numpy(V.astype(np.float32) * vinv).to(torch.float8_e4m3fn).to(torch.float64).numpy() * float(vs)
+    out = attention.decode_attention(q, kc, vc, [table], [L], bs, 0.25, kv_dtype, ks, vs)
+    # library route for the same quantised values: torch's fp8 conversion, per head
+    bk = np.broadcast_to(kinv, (hkv,)).astype(np.float32)[None, :, None]
+    bv = np.broadcast_to(vinv, (hkv,)).astype(np.float32)[None, :, None]
+    sk = np.broadcast_to(ks, (hkv,)).astype(np.float64)[None, :, None]
+    sv = np.broadcast_to(vs, (hkv,)).astype(np.float64)[None, :, None]
+    kq = torch.from_numpy(K.astype(np.float32) * bk).to(tdt).to(torch.float64).numpy() * sk
+    vq = torch.from_numpy(V.astype(np.float32) * bv).to(tdt).to(torch.float64).numpy() * sv
     ref = sdpa64(q[0].astype(np.float64), kq, vq, 0.25)
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
-    # and close to the unquantised result (relative precision of e4m3 ~ 1/16)
+    # and close to the unquantised result (relative precision ~1/16 for e4m3, ~1/8 for e5m2)
     ref16 = sdpa64(q[0].astype(np.float64), K.astype(np.float64), V.astype(np.float64), 0.25)
-    assert np.abs(out[0] - ref16).max() < 0.1
+    assert np.abs(out[0] - ref16).max() < (0.1 if kv_dtype == "fp8" else 0.2) * np.abs(V).max() / 4
 
 
 # ---------------------------------------------------- whole-pipeline pins
@@ -184,11 +199,14 @@ def _check_pipeline(wl, steps, sample=None):
     for s in seqs:
         K, V = lk[s]
         assert K.shape[0] == run.ctx_lens[-1][s]
-        if wl.kv_dtype == "fp8":
-            K = torch.from_numpy(K.astype(np.float32) * np.float32(wl.k_inv_scale)).to(
-                torch.float8_e4m3fn).to(torch.float64).numpy() * wl.k_scale
-            V = torch.from_numpy(V.astype(np.float32) * np.float32(wl.v_inv_scale)).to(
-                torch.float8_e4m3fn).to(torch.float64).numpy() * wl.v_scale
+        if wl.kv_dtype != "f16":
+            # torch's own fp8 conversion of the scaled values; scales per tensor or per KV head
+            tdt = torch.float8_e4m3fn if wl.kv_dtype == "fp8" else torch.float8_e5m2
+            hs = lambda x, dt: np.broadcast_to(np.asarray(x, dtype=dt), (wl.num_kv_heads,))[None, :, None]  # noqa: E731
+            K = torch.from_numpy(K.astype(np.float32) * hs(wl.k_inv_scale, np.float32)).to(
+                tdt).to(torch.float64).numpy() * hs(wl.k_scale, np.float64)
+            V = torch.from_numpy(V.astype(np.float32) * hs(wl.v_inv_scale, np.float32)).to(
+                tdt).to(torch.float64).numpy() * hs(wl.v_scale, np.float64)
         ref = sdpa64(q[s].astype(np.float64), K.astype(np.float64), V.astype(np.float64), wl.sm_scale)
         np.testing.assert_allclose(out[s], ref, rtol=1e-11, atol=1e-12)
     return run
@@ -209,8 +227,9 @@ def test_pipeline_shared_prefix_small():
     assert run.alloc.refcount(run.tables[-1][0][0]) == 5
 
 
-def test_pipeline_beam_fp8_small():
-    wl = workloads.beam_fp8(prompts=3, max_steps=2)
+@pytest.mark.parametrize("kv_dtype,per_head", [("fp8", False), ("fp8_e5m2", True)])
+def test_pipeline_beam_fp8_small(kv_dtype, per_head):
+    wl = workloads.beam_fp8(prompts=3, max_steps=2, kv_dtype=kv_dtype, per_head=per_head)
     run = _check_pipeline(wl, 1)
     # every beam shares its prompt's full blocks
     for i in range(3):

@@ -88,7 +88,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    kv_dtype: str  # "f16" or "fp8"
+    kv_dtype: str  # "f16", "fp8" (e4m3fn) or "fp8_e5m2"
     num_blocks: int
     free_order: np.ndarray  # int32 permutation of the pool
     batch: list  # sequence ids, in batch order
@@ -229,25 +229,37 @@ def _perm(seed, n):
     return rng(seed, STREAM_PERM).permutation(n).astype(np.int32)
 
 
-def _fp8_scales(wl: Workload, steps: int):
-    """Per-tensor scale max|x| / 448 over every K (resp. V) value the
-    workload generates for its setup and first `steps` decode steps, in
-    float32; the multiplier is float32(1) / scale."""
-    kmax = np.float32(0)
-    vmax = np.float32(0)
+FP8_MAX = {"fp8": 448.0, "fp8_e5m2": 57344.0}  # largest finite e4m3 / e5m2 value
+
+
+def _fp8_scales(wl: Workload, steps: int, per_head: bool = False):
+    """Scale = max|x| / (the format's largest value) over every K (resp. V)
+    value the workload generates for its setup and first `steps` decode steps,
+    in float32, for the whole tensor or for each KV head; the multiplier is
+    float32(1) / scale."""
+    hkv = wl.num_kv_heads
+    kmax = np.zeros(hkv, dtype=np.float32)
+    vmax = np.zeros(hkv, dtype=np.float32)
     ops = [o for r in wl.setup_rounds for o in r]
     for s in range(steps):
         ops += wl.step_ops(s)
     for o in ops:
-        if o.creates_tokens:
+        if o.creates_tokens or o.kind == "prompt":
             k, v = wl.op_kv(o)
-            kmax = max(kmax, np.abs(k.astype(np.float32)).max())
-            vmax = max(vmax, np.abs(v.astype(np.float32)).max())
-    ks = np.float32(kmax) / np.float32(448.0)
-    vs = np.float32(vmax) / np.float32(448.0)
-    wl.k_scale, wl.v_scale = float(ks), float(vs)
-    wl.k_inv_scale = float(np.float32(1.0) / ks)
-    wl.v_inv_scale = float(np.float32(1.0) / vs)
+            if len(k):
+                kmax = np.maximum(kmax, np.abs(k.astype(np.float32)).max(axis=(0, 2)))
+                vmax = np.maximum(vmax, np.abs(v.astype(np.float32)).max(axis=(0, 2)))
+    fmax = np.float32(FP8_MAX[wl.kv_dtype])
+    if per_head:
+        ks, vs = kmax / fmax, vmax / fmax
+        wl.k_scale, wl.v_scale = ks, vs
+        wl.k_inv_scale, wl.v_inv_scale = np.float32(1.0) / ks, np.float32(1.0) / vs
+    else:
+        ks = np.float32(kmax.max()) / fmax
+        vs = np.float32(vmax.max()) / fmax
+        wl.k_scale, wl.v_scale = float(ks), float(vs)
+        wl.k_inv_scale = float(np.float32(1.0) / ks)
+        wl.v_inv_scale = float(np.float32(1.0) / vs)
 
 
 def tiny(max_steps: int = 2) -> Workload:
@@ -470,7 +482,8 @@ def opt13b_rag(max_steps: int = 32, batch: int = 128) -> Workload:
     )
 
 
-def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4, tail_max: int = 128) -> Workload:
+def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4, tail_max: int = 128,
+             kv_dtype: str = "fp8", per_head: bool = False) -> Workload:
     """Beam / parallel-sampling decode with an fp8 e4m3 KV cache: 64 query
     heads over 8 KV heads, head_dim 128, block size 64. 32 prompts of uniform
     length in [512, 2048] are allocated (beam 0 of each prompt holds it) and
@@ -481,7 +494,9 @@ def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4, tail_max: in
     writes in place; the last tail token is written by the first decode step.
     K and V each use one float32 scale max|x|/448 over the data generated.
     tail_max = 1 makes every tail a single token, so all copy-on-write happens
-    inside the first decode step."""
+    inside the first decode step. kv_dtype "fp8_e5m2" stores e5m2 instead
+    (scale max|x|/57344); per_head gives every KV head its own scale ("Where
+    Did the VRAM Go (KV cache tutorial)", §6.2-6.3)."""
     seed = 5
     bs = 64
     g = rng(seed, STREAM_LENGTHS)
@@ -508,17 +523,20 @@ def beam_fp8(max_steps: int = 8, prompts: int = 32, beams: int = 4, tail_max: in
         need += full + sum(_ceil_div(P[i] + T[i][b] + max_steps, bs) - full for b in range(beams))
     nb = math.ceil(1.1 * need)
     lengths = [P[i] + T[i][b] for i in range(prompts) for b in range(beams)]
+    fmt = "e4m3" if kv_dtype == "fp8" else "e5m2"
+    gran = "per-head" if per_head else "per-tensor"
+    suffix = ("" if kv_dtype == "fp8" else "_e5m2") + ("_perhead" if per_head else "")
     wl = Workload(
-        name="beam4_fp8_gqa64x8", seed=seed,
-        description="32 prompts x beam 4, fp8 e4m3 KV (per-tensor scale), 64/8 heads, D=128, bs=64, "
+        name="beam4_fp8_gqa64x8" + suffix, seed=seed,
+        description=f"32 prompts x beam 4, fp8 {fmt} KV ({gran} scale), 64/8 heads, D=128, bs=64, "
                     "prompt~U[512,2048], tails~U[1,128] with copy-on-write",
-        num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=bs, kv_dtype="fp8",
+        num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=bs, kv_dtype=kv_dtype,
         num_blocks=nb, free_order=_perm(seed, nb), batch=list(range(prompts * beams)),
         setup_rounds=rounds, max_steps=max_steps,
         max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, bs),
         meta={"lengths": lengths, "prompts": P, "tails": T},
     )
-    _fp8_scales(wl, max_steps)
+    _fp8_scales(wl, max_steps, per_head)
     return wl
 
 
@@ -536,7 +554,7 @@ def make(config: int, **kw) -> Workload:
 
 
 def small_prefill(seed: int, lengths, chunks, num_q_heads, num_kv_heads, head_dim, block_size,
-                  kv_dtype="f16", slack=1.25) -> Workload:
+                  kv_dtype="f16", slack=1.25, per_head=False) -> Workload:
     """Independent sequences of the given context lengths, each holding all
     its tokens, whose last chunks[s] positions are prefilled (edge cases:
     chunks of one row, whole-sequence chunks, chunk edges inside blocks)."""
@@ -552,13 +570,13 @@ def small_prefill(seed: int, lengths, chunks, num_q_heads, num_kv_heads, head_di
         max_blocks_per_seq=max(1, _ceil_div(max(L + [1]), block_size)),
         meta={"lengths": L, "chunk": list(chunks)},
     )
-    if kv_dtype == "fp8":
-        _fp8_scales(wl, 0)
+    if kv_dtype != "f16":
+        _fp8_scales(wl, 0, per_head)
     return wl
 
 
 def small_custom(seed: int, lengths, num_q_heads, num_kv_heads, head_dim, block_size,
-                 kv_dtype="f16", num_blocks=None, max_steps=1, slack=1.25) -> Workload:
+                 kv_dtype="f16", num_blocks=None, max_steps=1, slack=1.25, per_head=False) -> Workload:
     """A plain workload of independent sequences for edge-case tests."""
     L = list(lengths)
     need = sum(_ceil_div(max(l, 0) + max_steps, block_size) for l in L)
@@ -572,6 +590,6 @@ def small_custom(seed: int, lengths, num_q_heads, num_kv_heads, head_dim, block_
         max_blocks_per_seq=max(1, _ceil_div(max(L + [1]) - 1 + max_steps, block_size)),
         meta={"lengths": L},
     )
-    if kv_dtype == "fp8":
-        _fp8_scales(wl, max_steps)
+    if kv_dtype != "f16":
+        _fp8_scales(wl, max_steps, per_head)
     return wl
