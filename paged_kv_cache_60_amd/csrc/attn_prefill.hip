@@ -55,7 +55,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kCols = 32;                 // query columns per wave
+constexpr int kNcg = kCols / 16;          // 16-column MFMA operands per wave
 constexpr int kTileCols = kWaves * kCols; // query columns per workgroup
+constexpr int kMinBlocks = 3;             // workgroups per compute unit the launch bound asks for
 constexpr int kChunk = 32;                // tokens per step of the token loop
 constexpr int kMaxSeqs = 4096;            // sequences per launch (tile prefix in LDS)
 constexpr float kLazy = 8.0f;             // log2 headroom before the running max moves
@@ -244,7 +246,7 @@ struct Stage {
 // matrix-core latencies of the token loop far better than two (measured on
 // MI355X: 10.7 -> 8.4 ms on the Qwen3-shaped prefix-cache prefill)
 template <int D, int G, int FMT>
-__global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(PrefillArgs a) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr bool FP8 = FMT != kF16;
@@ -253,10 +255,11 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
   constexpr int NT = D / 16;   // output head-dim tiles
   constexpr int DQ = D / 4;    // head-dim elements per lane group in the q.k operands
   constexpr int QT = kTileCols / G;  // query tokens per workgroup tile
-  static_assert(2 * S::BUF * 2 >= (kMaxSeqs + 1 + kWaves * 64) * 4, "the tile prefix fits in the K/V buffers");
+  constexpr int LDS_HALVES = 2 * S::BUF > (kMaxSeqs + 1 + kWaves * 64) * 2 ? 2 * S::BUF
+                                                                          : (kMaxSeqs + 1 + kWaves * 64) * 2;
 
   // two K/V chunk buffers; before the token loop the same memory holds the tile prefix
-  __shared__ __align__(16) _Float16 lds[2 * S::BUF];
+  __shared__ __align__(16) _Float16 lds[LDS_HALVES];
   int* pt = reinterpret_cast<int*>(lds);
   build_tile_prefix(a, G, pt, pt + a.B + 1);
 
@@ -287,10 +290,10 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
 
   // Q^T operands (B of S = K Q^T): column c = 32 wave + 16 cg + col holds query
   // token c / G, head c % G of the group; d = grp * DQ + 8 m + slot
-  f16x8 qb[2][KM];
-  int qpos[2];
+  f16x8 qb[kNcg][KM];
+  int qpos[kNcg];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
+  for (int cg = 0; cg < kNcg; ++cg) {
     const int c = wave * kCols + cg * 16 + col;
     const int tl = c / G;
     const bool live = tl < nt;
@@ -302,10 +305,10 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
   }
   const bool all_live = nt == QT;
 
-  f32x4 o[2][NT];
-  float m_run[2], l_part[2];
+  f32x4 o[kNcg][NT];
+  float m_run[kNcg], l_part[kNcg];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
+  for (int cg = 0; cg < kNcg; ++cg) {
 #pragma unroll
     for (int c = 0; c < NT; ++c) o[cg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[cg] = -INFINITY;
@@ -361,19 +364,20 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
     const bool ok_b = (unsigned)bb < (unsigned)a.num_blocks;
 
     // S = K . Q^T for both tiles and both column groups
-    f32x4 s[2][2];
+    f32x4 s[2][kNcg];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) s[tt][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cg = 0; cg < kNcg; ++cg) s[tt][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const _Float16* krow = buf + (16 * tt + col) * S::KS + grp * DQ;
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
         const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 8 * m);
-        s[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[0][m], s[tt][0], 0, 0, 0);
-        s[tt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[1][m], s[tt][1], 0, 0, 0);
+#pragma unroll
+        for (int cg = 0; cg < kNcg; ++cg)
+          s[tt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[cg][m], s[tt][cg], 0, 0, 0);
       }
     }
 
@@ -383,10 +387,10 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
     // exceed it by more than kLazy, so between moves no lane shuffles and the
     // accumulators are not rescaled (p <= 2^kLazy then, well inside fp16).
     const bool plain = all_live && ok_a && ok_b && t0 + kChunk - 1 <= pos0;
-    float z[2][8];
-    float mt[2];
+    float z[kNcg][8];
+    float mt[kNcg];
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
+    for (int cg = 0; cg < kNcg; ++cg) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         z[cg][v] = s[0][cg][v];
@@ -406,10 +410,12 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
       for (int i = 1; i < 8; ++i) m = fmaxf(m, z[cg][i]);
       mt[cg] = m * qk_scale;
     }
-    const bool need = mt[0] > m_run[0] + kLazy || mt[1] > m_run[1] + kLazy;
+    bool need = false;
+#pragma unroll
+    for (int cg = 0; cg < kNcg; ++cg) need = need || mt[cg] > m_run[cg] + kLazy;
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
+      for (int cg = 0; cg < kNcg; ++cg) {
         float m = mt[cg];
         m = fmaxf(m, shfl_xor_f32(m, 16));
         m = fmaxf(m, shfl_xor_f32(m, 32));
@@ -421,9 +427,9 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
         m_run[cg] = mn;
       }
     }
-    f16x8 pb[2];
+    f16x8 pb[kNcg];
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
+    for (int cg = 0; cg < kNcg; ++cg) {
       const float neg_m = -safe_max(m_run[cg]);
       float ps = 0.0f;
 #pragma unroll
@@ -444,8 +450,9 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
       const f16x4 r1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
       const f16x4 r2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2)));
       const f16x8 va = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[0][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[0], o[0][c], 0, 0, 0);
-      o[1][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[1], o[1][c], 0, 0, 0);
+#pragma unroll
+      for (int cg = 0; cg < kNcg; ++cg)
+        o[cg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[cg], o[cg][c], 0, 0, 0);
     }
 
     if (j + 1 < nchunks) st.store(lds + ((j + 1) & 1) * S::BUF);
@@ -458,7 +465,7 @@ __global__ void __launch_bounds__(kWaves * 64, 3) attn_prefill_kernel(PrefillArg
   // per-column sums over the four lane groups (the max is already common);
   // lane (col, grp) holds d = 16c + 4grp + v of its column
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
+  for (int cg = 0; cg < kNcg; ++cg) {
     float l = l_part[cg];
     l += shfl_xor_f32(l, 16);
     l += shfl_xor_f32(l, 32);
