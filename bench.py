@@ -46,7 +46,7 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 EVENT_EVERY = 5  # timed steps per pass-1 event pair
 
 
-KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "device_common.hpp")
+KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "attn_shared_mfma.hpp", "device_common.hpp")
 PREFILL_SOURCES = ("attn_prefill.hip", "device_common.hpp")
 
 
@@ -420,6 +420,9 @@ def main():
                          "llama2: last-512-token chunks, batch 64)")
     ap.add_argument("--swap", action="store_true",
                     help="time paged_block_swap (preemption by swapping, 16 sequences of the Llama-2-7B batch)")
+    ap.add_argument("--shared", action="store_true",
+                    help="attend with paged_attn_decode_shared: runs of the batch that share leading blocks "
+                         "(beams of one prompt, a common prefix) read them once")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one plain 256 MiB device copy (known bytes, for counter scaling)")
     args = ap.parse_args()
@@ -464,11 +467,15 @@ def main():
     dev = torch.device("cuda")
     eng = harness.make_engine(wl, poison=False)
     harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
-    eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, args.partition)
+    eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, args.partition, shared_prefix=args.shared)
     workers = ops.decode_workers(len(wl.batch), wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
                                  wl.max_blocks_per_seq, wl.kv_dtype, args.partition)
     group = wl.num_q_heads // wl.num_kv_heads
     kernel = "attn_partition_mfma_kernel" if group >= 4 else "attn_partition_kernel"
+    if args.shared:
+        # the pass-1 events bracket both launches: the shared-prefix pass and pass 1 over the rest
+        kernel = "attn_shared_mfma_kernel + " + kernel
+        log(f"bench: {eng.groups.shape[1]} shared-prefix groups")
 
     # stage every step's inputs in HBM before timing
     B = len(wl.batch)
@@ -546,7 +553,7 @@ def main():
     p1_avg_s = sum(p1_ms) / len(p1_ms) / 1e3
     achieved = (sum(p1_bytes) / len(p1_bytes)) / p1_avg_s / 1e9
     achieved_logical = (sum(p1_bytes_logical) / len(p1_bytes_logical)) / p1_avg_s / 1e9
-    traffic = load_counters(wl.name)
+    traffic = load_counters(wl.name + ("_shared" if args.shared else ""))
 
     result = {
         "metric": METRIC,
@@ -566,6 +573,7 @@ def main():
             "mean_ctx_len": round(float(np.mean([c.mean() for c in ctx_steps])), 1),
             "partition_tokens": args.partition,
             "attention_workers": workers,
+            "shared_prefix_groups": int(eng.groups.shape[1]) if args.shared else 0,
             "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
         },
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),

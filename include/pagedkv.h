@@ -244,6 +244,53 @@ int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, i
                               int partition_tokens);
 
 /*
+ * paged_attn_decode_shared -- paged_attn_decode for a batch in which runs of
+ * consecutive sequences share their leading blocks: beams or parallel samples
+ * forked from one prompt ([VLLM] §3.2) or requests mapped onto the same
+ * prefix-cache blocks ([VRAM] §4.2-4.4). The output is the same attention as
+ * paged_attn_decode's; only the order of the sums differs.
+ * Group g is the sequences first[g] .. first[g] + size[g] - 1 of the batch;
+ * its first prefix[g] tokens (rounded down to a multiple of 16) are read once
+ * for all its members, through the table of sequence first[g], as the
+ * contraction of every member's query heads with the shared K/V on the
+ * matrix cores (up to 32 query columns per pass over the shared blocks; a
+ * larger group is covered by several passes). Each member's remaining tokens
+ * go through paged_attn_decode's pass 1, and a last pass merges the two
+ * partial softmax states of each (sequence, query head), which is exact up to
+ * rounding: the softmax of a concatenation is the weighted merge of the
+ * softmaxes of its parts.
+ *   group_first, group_size, group_prefix  device, int32 [num_groups]
+ *                  (pkv_bm_prefix_groups computes them). Precondition: groups
+ *                  ascending and disjoint, and every member maps its first
+ *                  prefix tokens to the same physical blocks as the group's
+ *                  first sequence. A member with fewer tokens than the prefix
+ *                  attends only to its own ctx_len of them. Entries that break
+ *                  the precondition give wrong results but never an access
+ *                  outside the buffers (members past the batch are dropped).
+ *   k_scale, v_scale, k_scales, v_scales  fp8 only: per-tensor multipliers, or
+ *                  one per KV head when k_scales and v_scales (device float
+ *                  [num_kv_heads]) are both non-NULL.
+ *   passes         bit 0: pass over the shared blocks; bit 1: pass 1 over the
+ *                  members' own tokens and every other sequence; bit 2: merge.
+ *                  7 = the whole call (each bit exists so a pass can be timed).
+ *   workspace      device, >= paged_attn_decode_shared_workspace_bytes(...).
+ * Other arguments, shapes and errors as paged_attn_decode; num_seqs at most
+ * 4096, num_groups in [0, num_seqs].
+ */
+size_t paged_attn_decode_shared_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                                int head_dim);
+
+int paged_attn_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                             const float* k_scales, const float* v_scales, const int32_t* group_first,
+                             const int32_t* group_size, const int32_t* group_prefix, int num_groups,
+                             int partition_tokens, void* workspace, size_t workspace_bytes,
+                             int passes, void* stream);
+
+/*
  * paged_attn_prefill -- chunked (multi-token, causal) attention over the paged
  * K/V. A request that found its leading blocks in the prefix cache prefills
  * only the positions that missed ([VRAM] §4.2, §5); a prompt split into chunks
@@ -481,6 +528,21 @@ int pkv_bm_stats(const pkv_bm* bm, pkv_bm_stats_t* out);
  * wider than max_blocks. */
 int pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* tables_out,
                   int max_blocks, int32_t* ctx_lens_out);
+
+/* The groups paged_attn_decode_shared reads once: walking seqs in order, a
+ * group is a maximal run of consecutive entries (at most max_members) whose
+ * first table entry is one block every member holds in full (token count >=
+ * block_size); its prefix is block_size times the number of leading table
+ * positions at which every member holds the same block, in full. Runs of one
+ * entry are not groups. Writes (first batch index, members, prefix tokens) of
+ * each group in batch order and their number to *num_groups. Shared blocks
+ * are never written (copy-on-write, [VLLM] §3.3), and an append only adds or
+ * replaces blocks past the full ones, so the groups stay valid through decode
+ * steps until a sequence of the batch is freed, forked or swapped.
+ * NO_SEQ for a sequence that is not resident; INVALID if cap is too small. */
+int pkv_bm_prefix_groups(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int max_members,
+                         int32_t* group_first, int32_t* group_size, int32_t* group_prefix, int cap,
+                         int* num_groups);
 
 #ifdef __cplusplus
 }

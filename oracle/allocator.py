@@ -99,6 +99,18 @@ Readings taken where the pages are silent or garbled (each is tested):
       victims (their requests are prefilled again later); mode "swap" swaps
       them out as one group. If even every listed sequence is not enough (or,
       for swap, the host pool is too small) nothing changes (OOM).
+  * "vLLM Architecture and Memory Use, ch. 3", §3.2, and "Where Did the VRAM
+    Go", §4.2-4.4: forked sequences and prefix-cache hits hold the same
+    physical blocks at the same table positions, so their K/V there is one
+    copy in memory.
+  R18 prefix_groups(seqs, max_members) finds the runs of a decode batch that
+      share leading blocks. Walking the batch in order, a group is a maximal
+      run of consecutive entries, at most max_members long, whose first
+      table entry is one block that every member holds in full (token count
+      >= bs). Its prefix is bs times the number of leading table positions at
+      which every member holds the same block, in full. A run of one entry is
+      not a group. The result is (first batch index, members, prefix tokens)
+      per group, in batch order.
 """
 
 from __future__ import annotations
@@ -437,6 +449,35 @@ class BlockAllocatorModel:
         return list(self.host_free)
 
     # ----------------------------------------------------------- queries
+    def prefix_groups(self, seqs, max_members: int) -> list:
+        """Runs of the batch that share leading full blocks (R18)."""
+        seqs = [int(s_) for s_ in seqs]
+        if max_members < 1:
+            raise AllocError(ERR_INVALID, "max_members must be positive")
+        for s_ in seqs:
+            self._require(s_)
+
+        def full_first(s_):
+            return self.tables[s_][0] if self.counts[s_] >= self.bs else None
+
+        groups = []
+        i = 0
+        while i < len(seqs):
+            head = full_first(seqs[i])
+            j = i + 1
+            if head is not None:
+                while j < len(seqs) and j - i < max_members and full_first(seqs[j]) == head:
+                    j += 1
+            if j - i >= 2:
+                members = seqs[i:j]
+                n = 0
+                while all((n + 1) * self.bs <= self.counts[m] and self.tables[m][n] == self.tables[members[0]][n]
+                          for m in members):
+                    n += 1
+                groups.append((i, j - i, n * self.bs))
+            i = j
+        return groups
+
     def slots(self, seq: int, start: int, n: int) -> list[int]:
         self._require(seq)
         if start < 0 or n < 0 or start + n > self.counts[seq]:

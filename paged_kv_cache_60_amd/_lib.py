@@ -86,6 +86,10 @@ SIGNATURES = {
                                           _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f,
                                           _c_int, _vp, _c_sz, _c_int, _vp]),
     "paged_attn_decode_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "paged_attn_decode_shared_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int]),
+    "paged_attn_decode_shared": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _vp,
+                                          _vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _c_sz, _c_int, _vp]),
     "paged_attn_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _vp]),
     "paged_step_metadata": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp,
@@ -110,6 +114,7 @@ SIGNATURES = {
     "pkv_bm_num_free": (_c_int, [_vp]),
     "pkv_bm_stats": (_c_int, [_vp, ctypes.POINTER(PkvStats)]),
     "pkv_bm_export": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_i32]),
+    "pkv_bm_prefix_groups": (_c_int, [_vp, _p_i64, _c_int, _c_int, _p_i32, _p_i32, _p_i32, _c_int, _p_int]),
     "pkv_bm_set_host_blocks": (_c_int, [_vp, _c_int]),
     "pkv_bm_swap_out": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_int]),
     "pkv_bm_swap_in": (_c_int, [_vp, _p_i64, _c_int, _p_i32, _c_int, _p_int]),

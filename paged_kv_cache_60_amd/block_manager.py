@@ -255,6 +255,21 @@ class BlockManager:
         check(self._lib.pkv_bm_export(self._h, _i64p(seqs), len(seqs), _i32p(tables_out),
                                       tables_out.shape[1], _i32p(ctx_out)), "pkv_bm_export")
 
+    def prefix_groups(self, seqs, max_members: int) -> np.ndarray:
+        """Runs of the batch that share leading full blocks, as int32 [3, n]:
+        first batch index, members, shared tokens of each group (the groups
+        paged_attn_decode_shared reads once)."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        cap = max(1, len(seqs) // 2)
+        first = np.empty(cap, dtype=np.int32)
+        size = np.empty(cap, dtype=np.int32)
+        prefix = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(self._lib.pkv_bm_prefix_groups(self._h, _i64p(seqs) if len(seqs) else None, len(seqs),
+                                             int(max_members), _i32p(first), _i32p(size), _i32p(prefix), cap,
+                                             ctypes.byref(n)), "pkv_bm_prefix_groups")
+        return np.stack([first[:n.value], size[:n.value], prefix[:n.value]]).astype(np.int32)
+
     def state(self, seqs, swapped=()) -> dict:
         """Snapshot comparable with the oracle model's state() for the given
         resident and swapped-out ids."""

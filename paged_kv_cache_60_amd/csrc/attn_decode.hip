@@ -58,6 +58,8 @@ constexpr int kTile = 16;
 constexpr int kWaves = 4;          // waves (workers) per workgroup
 constexpr int kMaxWorkers = 8192;  // the workspace holds partials for this many workers
 constexpr int kMaxSeqs = 4096;     // sequences per launch (their unit prefix lives in LDS)
+constexpr int kSharedCols = 32;    // query columns (member, head) of one shared pass over a prefix
+constexpr int kMaxSharedWorkers = 2048;
 
 struct AttnArgs {
   const f16* q;
@@ -85,6 +87,24 @@ struct AttnArgs {
   const float* k_scale_h;
   const float* v_scale_h;
   float qk_base;      // sm_scale * log2(e)
+  // Shared-prefix groups (paged_attn_decode_shared; NG = 0 otherwise). Group
+  // g is the batch sequences grp_first[g] .. + grp_size[g] - 1; their first
+  // group_tokens(g) tokens are attended in a pass of their own, through the
+  // table of sequence grp_first[g], and pass 1 covers only the rest.
+  const int32_t* grp_first = nullptr;
+  const int32_t* grp_size = nullptr;
+  const int32_t* grp_prefix = nullptr;
+  int NG = 0;
+  int g_log2 = 0;           // log2(query heads per KV head)
+  int s_workers = 0;        // workers of the shared pass
+  float* ws_wo = nullptr;   // [B * Hq][D]  whole pass-1 pieces of grouped sequences
+  float* ws_wml = nullptr;  // [B * Hq][2]
+  float* ws_swo = nullptr;  // [B * Hq][D]  whole shared pieces, by (member, query head)
+  float* ws_swml = nullptr; // [B * Hq][2]
+  float* ws_so = nullptr;   // [kMaxSharedWorkers][2][kSharedCols][D]  split shared pieces
+  float* ws_sml = nullptr;  // [kMaxSharedWorkers][2][kSharedCols][2]
+  int32_t* ws_spt = nullptr;  // [NG + 1]  unit prefix over the groups (shared pass -> merge)
+  int32_t* ws_gid = nullptr;  // [B]       group of each sequence or -1 (pass 1 -> merge)
 };
 
 // The logit and output scales of KV head h.
@@ -105,18 +125,73 @@ __device__ __forceinline__ int64_t share_start(int64_t w, int64_t total, int64_t
 // register so that the arithmetic that depends on it stays scalar.
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Dynamic LDS of a pass-1 workgroup: pt[B + 1] then scan[blockDim]. pt[0] = 0
-// and pt[s + 1] = pt[s] + ceil(len(s) / unit), len(s) = the clamped context
-// length of sequence s. Ends with a barrier.
+// The clamped context length of sequence s.
 __device__ __forceinline__ int seq_len(const AttnArgs& a, int s) {
   return clamp_len(a.ctx_lens[s], a.max_blocks << a.bs_log2);
 }
 
-__device__ void build_prefix(const AttnArgs& a, int* pt, int* scan) {
-  const int n = a.B;
+// Members of group g inside the batch (0 for an entry outside it).
+__device__ __forceinline__ int group_members(const AttnArgs& a, int g) {
+  const int f = a.grp_first[g];
+  if (f < 0 || f >= a.B) return 0;
+  const int n = a.grp_size[g];
+  return n < 0 ? 0 : min(n, a.B - f);
+}
+
+// Shared tokens of group g: a multiple of 16 (tiles never straddle the edge),
+// within the table width.
+__device__ __forceinline__ int group_tokens(const AttnArgs& a, int g) {
+  return clamp_len(a.grp_prefix[g], a.max_blocks << a.bs_log2) & ~15;
+}
+
+// Shared tokens of every batch sequence's group, or -1 for a sequence in no
+// group, into the LDS array pre[B] (pass 1 with shared-prefix groups); the
+// first workgroup also writes each sequence's group to ws_gid for the merge.
+// One scatter over the groups: a group's members are consecutive. Ends with a
+// barrier.
+__device__ void build_group_map(const AttnArgs& a, int* pre) {
   const int T = blockDim.x;
   const int tid = threadIdx.x;
-  for (int i = tid; i < n; i += T) pt[i + 1] = (seq_len(a, i) + a.unit_tokens - 1) / a.unit_tokens;
+  const bool first_wg = blockIdx.x == 0;
+  for (int i = tid; i < a.B; i += T) {
+    pre[i] = -1;
+    if (first_wg) a.ws_gid[i] = -1;
+  }
+  __syncthreads();
+  for (int g = tid; g < a.NG; g += T) {
+    const int n = group_members(a, g);
+    if (n == 0) continue;
+    const int f = a.grp_first[g];
+    const int tok = group_tokens(a, g);
+    for (int m = 0; m < n; ++m) {
+      pre[f + m] = tok;
+      if (first_wg) a.ws_gid[f + m] = g;
+    }
+  }
+  __syncthreads();
+}
+
+// First token pass 1 covers for a sequence of L tokens whose group shares
+// `pre` tokens (-1: no group): 0, or the shared tokens (all L tokens if the
+// prefix is longer).
+__device__ __forceinline__ int private_start(int pre, int L) { return pre < 0 ? 0 : min(pre, L); }
+
+// Units of the shared pass for group g: one run of the prefix's 32-token
+// units per kSharedCols query columns of its members.
+__device__ __forceinline__ int group_units(const AttnArgs& a, int g) {
+  return (group_tokens(a, g) + 31) / 32;
+}
+__device__ __forceinline__ int group_parts(const AttnArgs& a, int g) {
+  return ((group_members(a, g) << a.g_log2) + kSharedCols - 1) / kSharedCols;
+}
+
+// pt[0] = 0, pt[i + 1] = pt[i] + units(i) for i < n, by all threads of the
+// workgroup; scan holds blockDim ints. Ends with a barrier.
+template <class Units>
+__device__ void build_scan(int n, int* pt, int* scan, Units units) {
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n; i += T) pt[i + 1] = units(i);
   __syncthreads();
   // each thread sums a run of consecutive sequences; the runs are scanned
   const int per = (n + T - 1) / T;
@@ -139,6 +214,16 @@ __device__ void build_prefix(const AttnArgs& a, int* pt, int* scan) {
   }
   if (tid == 0) pt[0] = 0;
   __syncthreads();
+}
+
+// Dynamic LDS of a pass-1 workgroup: pt[B + 1], scan[blockDim], then with
+// shared-prefix groups pre[B] (build_group_map).
+__device__ void build_prefix(const AttnArgs& a, int* pt, int* scan, int* pre) {
+  if (a.NG) build_group_map(a, pre);
+  build_scan(a.B, pt, scan, [&](int i) {
+    const int L = seq_len(a, i);
+    return (L - (a.NG ? private_start(pre[i], L) : 0) + a.unit_tokens - 1) / a.unit_tokens;
+  });
 }
 
 // The last sequence s in [0, B) with pt[s] <= q; pt is non-decreasing, so
@@ -207,7 +292,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 
   extern __shared__ int dyn_smem[];
   int* pt = dyn_smem;
-  build_prefix(a, pt, pt + a.B + 1);
+  int* pre = pt + a.B + 1 + NW * 64;
+  build_prefix(a, pt, pt + a.B + 1, pre);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -231,6 +317,10 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
+    // a member of a shared-prefix group starts after the shared tokens
+    const int pre_s = a.NG ? wave_uniform(pre[seq]) : -1;
+    const int grp = pre_s;  // >= 0 for a group member
+    const int base = private_start(pre_s, L);
     const float qk_scale = head_qk_scale(a, pc.head);
     const float v_scale = head_v_scale(a, pc.head);
 
@@ -266,12 +356,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
       // block ids of up to 64 tiles, one per lane, fetched together so that
       // no tile waits on its own table read
       int my_blk = -1;
-      if (j0 + lane < pc.u1) my_blk = tab[((j0 + lane) * kTile) >> a.bs_log2];
+      if (j0 + lane < pc.u1) my_blk = tab[(base + (j0 + lane) * kTile) >> a.bs_log2];
       const int nj = min(64, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
         const int blk = __builtin_amdgcn_readlane(my_blk, j);
         if ((unsigned)blk >= (unsigned)a.num_blocks) continue;  // never followed
-        const int t0 = (j0 + j) * kTile;
+        const int t0 = base + (j0 + j) * kTile;
         // A tile lies inside one block, so all 16 rows are in bounds even past
         // the sequence end; rows at or past L are masked below.
         const bool full = t0 + kTile <= L;
@@ -377,25 +467,27 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
       }
     }
 
-    // the whole segment -> output; part of one -> this worker's slot
+    // the whole segment -> output (or, for a group member, the buffer the
+    // merge reads); part of one -> this worker's slot
     const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
     const int slot = t == start ? 0 : 1;
     if (lane < LPR) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (whole) {
+        if (whole && grp < 0) {
           const float sc = l[g] > 0.0f ? v_scale / l[g] : 0.0f;
           f16* o = a.out + ((size_t)seq * a.Hq + hq0 + g) * D + c * E;
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = (f16)(acc[g][e] * sc);
         } else {
-          const size_t pi = ((size_t)w * 2 + slot) * G + g;
-          float* o = a.ws_o + pi * D + c * E;
+          const size_t pi = whole ? (size_t)seq * a.Hq + hq0 + g : ((size_t)w * 2 + slot) * G + g;
+          float* o = (whole ? a.ws_wo : a.ws_o) + pi * D + c * E;
+          float* ml = whole ? a.ws_wml : a.ws_ml;
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = acc[g][e] * v_scale;
           if (lane == 0) {
-            a.ws_ml[2 * pi] = m[g];
-            a.ws_ml[2 * pi + 1] = l[g];
+            ml[2 * pi] = m[g];
+            ml[2 * pi + 1] = l[g];
           }
         }
       }
@@ -420,44 +512,52 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
-// Pass 2. One wave per (sequence, query head). Lane k holds the weight of
-// piece k (64 pieces at a time); each lane owns D/64 output elements.
-template <int D, int G>
-__global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
-  constexpr int DL = D / 64;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= a.B * a.Hq) return;
-  const int lane = threadIdx.x & 63;
-  const int seq = wid / a.Hq;
-  const int hq = wid - seq * a.Hq;
-  const int kvh = hq / G;
-  const int g = hq - kvh * G;
-  const int p0 = a.ws_pt[seq];
-  const int n_u = a.ws_pt[seq + 1] - p0;
-  f16* out = a.out + (size_t)wid * D + lane * DL;
-  if (n_u == 0) {
+// Online-softmax state of one output row in a wave: max M (log2 units), sum
+// l, and the lane's DL output elements, unnormalised, relative to M.
+template <int DL>
+struct Row {
+  float M = -INFINITY;
+  float l = 0.0f;
+  float acc[DL] = {};
+};
+
+// Folds one partial state (max m, sum l, the lane's DL output elements o,
+// relative to m) into r.
+template <int DL>
+__device__ __forceinline__ void fold(Row<DL>& r, float m, float l, const float* o) {
+  const float Mn = fmaxf(r.M, m);
+  const float Ms = safe_max(Mn);
+  const float a1 = fast_exp2(r.M - Ms);
+  const float a2 = fast_exp2(m - Ms);
+  r.l = r.l * a1 + l * a2;
 #pragma unroll
-    for (int e = 0; e < DL; ++e) out[e] = (f16)0.0f;
-    return;
-  }
-  const int P = a.ws_pt[a.B];
-  const int64_t total = (int64_t)a.Hkv * P;
-  const int64_t W = a.workers;
-  const int64_t s0 = (int64_t)kvh * P + p0;  // the segment's units: [s0, s1)
-  const int64_t s1 = s0 + n_u;
+  for (int e = 0; e < DL; ++e) r.acc[e] = r.acc[e] * a1 + o[e] * a2;
+  r.M = Mn;
+}
+
+// Folds into r the pieces of the segment holding units [s0, s1) of a unit
+// space of `total` units cut into W shares. The piece of worker w sits in
+// slot 0 if it starts the worker's share, else in slot 1; a slot holds `cols`
+// columns of D + 2 floats (o in ws_o, (max, sum) in ws_ml) and the row is
+// column `col`. Lane k holds the weight of piece k (64 pieces at a time); each
+// lane owns D/64 output elements.
+template <int D>
+__device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_ml, int cols, int col,
+                            int64_t s0, int64_t s1, int64_t total, int64_t W) {
+  constexpr int DL = D / 64;
+  const int lane = threadIdx.x & 63;
+  if (s0 < 0 || s0 >= s1 || s1 > total) return;  // only inconsistent group entries get here
   // worker holding unit u: the largest w with share_start(w) <= u
   const int64_t wa = ((s0 + 1) * W - 1) / total;
   const int64_t wb = (s1 * W - 1) / total;
-  if (wa == wb) return;  // held whole by one worker: written by pass 1
   const int np = (int)(wb - wa + 1);
-  // a piece sits in slot 0 if it starts its worker's share, else in slot 1
   float M = -INFINITY;
   for (int k = lane; k < np; k += 64) {
     const int64_t wk = wa + k;
     const int64_t st = share_start(wk, total, W);
     if (share_start(wk + 1, total, W) == st) continue;  // empty share
     const int slot = st >= s0 ? 0 : 1;
-    M = fmaxf(M, a.ws_ml[2 * ((wk * 2 + slot) * G + g)]);
+    M = fmaxf(M, ws_ml[2 * ((wk * 2 + slot) * cols + col)]);
   }
   M = wave_max(M);
   const float Ms = safe_max(M);
@@ -474,9 +574,9 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
       const int64_t st = share_start(wk, total, W);
       if (share_start(wk + 1, total, W) != st) {
         slot_k = st >= s0 ? 0 : 1;
-        const int64_t pi = (wk * 2 + slot_k) * G + g;
-        wgt = fast_exp2(a.ws_ml[2 * pi] - Ms);
-        lsum += a.ws_ml[2 * pi + 1] * wgt;
+        const int64_t pi = (wk * 2 + slot_k) * cols + col;
+        wgt = fast_exp2(ws_ml[2 * pi] - Ms);
+        lsum += ws_ml[2 * pi + 1] * wgt;
       }
     }
     const int nk = min(64, np - k0);
@@ -484,22 +584,205 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
       const float wj = readlane_f32(wgt, j);
       if (wj == 0.0f) continue;  // empty share, or a weight that underflowed
       const int slot = __builtin_amdgcn_readlane(slot_k, j);
-      const int64_t pi = ((wa + k0 + j) * 2 + slot) * G + g;
-      const float* o = a.ws_o + pi * D + lane * DL;
+      const int64_t pi = ((wa + k0 + j) * 2 + slot) * cols + col;
+      const float* o = ws_o + pi * D + lane * DL;
 #pragma unroll
       for (int e = 0; e < DL; ++e) acc[e] = fmaf(wj, o[e], acc[e]);
     }
   }
-  lsum = wave_sum(lsum);
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  fold(r, M, wave_sum(lsum), acc);
+}
+
+// Writes r, normalised, to the lane's DL elements of an output row.
+template <int DL>
+__device__ __forceinline__ void write_row(const Row<DL>& r, f16* out) {
+  const float inv = r.l > 0.0f ? 1.0f / r.l : 0.0f;
 #pragma unroll
-  for (int e = 0; e < DL; ++e) out[e] = (f16)(acc[e] * inv);
+  for (int e = 0; e < DL; ++e) out[e] = (f16)(r.acc[e] * inv);
+}
+
+// Workers holding the first and last unit of the segment [s0, s1).
+__device__ __forceinline__ bool held_whole(int64_t s0, int64_t s1, int64_t total, int64_t W) {
+  return ((s0 + 1) * W - 1) / total == (s1 * W - 1) / total;
+}
+
+// Pass 2. One wave per (sequence, query head): combines the pieces of a
+// segment that pass 1 split between workers; writes zeros for empty
+// sequences.
+template <int D, int G>
+__global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
+  constexpr int DL = D / 64;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= a.B * a.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int seq = wid / a.Hq;
+  const int hq = wid - seq * a.Hq;
+  const int kvh = hq / G;
+  const int g = hq - kvh * G;
+  const int p0 = a.ws_pt[seq];
+  const int n_u = a.ws_pt[seq + 1] - p0;
+  f16* out = a.out + (size_t)wid * D + lane * DL;
+  Row<DL> r;
+  if (n_u > 0) {
+    const int P = a.ws_pt[a.B];
+    const int64_t total = (int64_t)a.Hkv * P;
+    const int64_t s0 = (int64_t)kvh * P + p0;  // the segment's units: [s0, s1)
+    if (held_whole(s0, s0 + n_u, total, a.workers)) return;  // written by pass 1
+    fold_pieces<D>(r, a.ws_o, a.ws_ml, G, g, s0, s0 + n_u, total, a.workers);
+  }
+  write_row(r, out);
+}
+
+// Where the merge finds the pieces of one segment of one output row: split
+// between the workers [wa, wb] of a unit space (slots of `cols` columns, this
+// row's column `col`), or held whole by one worker (one piece at row `wid` of
+// the whole-piece buffers).
+struct SegPieces {
+  int n = 0;  // pieces (0: no segment)
+  bool whole = false;
+  int64_t wa = 0, s0 = 0, total = 1, W = 1;
+  const float* o = nullptr;
+  const float* ml = nullptr;
+  int cols = 0, col = 0;
+};
+
+__device__ __forceinline__ SegPieces seg_pieces(int64_t s0, int64_t s1, int64_t total, int64_t W, const float* o,
+                                                const float* ml, int cols, int col, const float* wo,
+                                                const float* wml, int64_t wid, int D) {
+  SegPieces p;
+  if (s0 < 0 || s0 >= s1 || s1 > total) return p;  // empty (or inconsistent group entries)
+  const int64_t wa = ((s0 + 1) * W - 1) / total;
+  const int64_t wb = (s1 * W - 1) / total;
+  if (wa == wb) {
+    p.n = 1;
+    p.whole = true;
+    p.o = wo + wid * D;
+    p.ml = wml + 2 * wid;
+    return p;
+  }
+  p.n = (int)(wb - wa + 1);
+  p.wa = wa;
+  p.s0 = s0;
+  p.total = total;
+  p.W = W;
+  p.o = o;
+  p.ml = ml;
+  p.cols = cols;
+  p.col = col;
+  return p;
+}
+
+// Piece k of a segment: its (max, sum) pair and output row, or false for the
+// empty share of a worker.
+__device__ __forceinline__ bool piece_at(const SegPieces& p, int k, int D, const float** ml, const float** o) {
+  if (p.whole) {
+    *ml = p.ml;
+    *o = p.o;
+    return true;
+  }
+  const int64_t wk = p.wa + k;
+  const int64_t st = share_start(wk, p.total, p.W);
+  if (share_start(wk + 1, p.total, p.W) == st) return false;
+  const int slot = st >= p.s0 ? 0 : 1;  // slot 0: the piece starts the worker's share
+  const int64_t pi = (wk * 2 + slot) * p.cols + p.col;
+  *ml = p.ml + 2 * pi;
+  *o = p.o + pi * D;
+  return true;
+}
+
+// Pass 2 of the shared-prefix decode. One wave per (sequence, query head). A
+// sequence outside every group is handled exactly as in attn_reduce_kernel. A group
+// member merges the pieces of its pass-1 segment and of its columns in the
+// shared pass over its group's prefix: every piece's (max, sum) is loaded at
+// once (lane k holds piece k), then the output rows, weighted.
+template <int D, int G>
+__global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
+  constexpr int DL = D / 64;
+  constexpr int MP = kSharedCols / G;  // members per shared pass
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= a.B * a.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int seq = wid / a.Hq;
+  const int hq = wid - seq * a.Hq;
+  const int kvh = hq / G;
+  const int g = hq - kvh * G;
+  // written by pass 1 only when there are groups
+  const int gid = a.NG ? a.ws_gid[seq] : -1;
+  const int grp = gid >= 0 && gid < a.NG ? gid : -1;
+  const int p0 = a.ws_pt[seq];
+  const int n_u = a.ws_pt[seq + 1] - p0;
+  const int P = a.ws_pt[a.B];
+  f16* out = a.out + (size_t)wid * D + lane * DL;
+
+  const int64_t totalP = (int64_t)a.Hkv * P;
+  const int64_t s0P = (int64_t)kvh * P + p0;
+  if (grp < 0) {  // exactly as attn_reduce_kernel: the same bits as paged_attn_decode
+    Row<DL> r;
+    if (n_u > 0) {
+      if (held_whole(s0P, s0P + n_u, totalP, a.workers)) return;  // written by pass 1
+      fold_pieces<D>(r, a.ws_o, a.ws_ml, G, g, s0P, s0P + n_u, totalP, a.workers);
+    }
+    write_row(r, out);
+    return;
+  }
+  SegPieces sp;
+  if (n_u > 0)
+    sp = seg_pieces(s0P, s0P + n_u, totalP, a.workers, a.ws_o, a.ws_ml, G, g, a.ws_wo, a.ws_wml, wid, D);
+  SegPieces ss;
+  {
+    const int ug = group_units(a, grp);
+    const int m = seq - a.grp_first[grp];
+    if (ug > 0 && m >= 0) {
+      const int part = m / MP;
+      const int c = (m - part * MP) * G + g;
+      const int PS = a.ws_spt[a.NG];
+      const int64_t s0 = (int64_t)kvh * PS + a.ws_spt[grp] + (int64_t)part * ug;
+      ss = seg_pieces(s0, s0 + ug, (int64_t)a.Hkv * PS, a.s_workers, a.ws_so, a.ws_sml, kSharedCols, c, a.ws_swo,
+                      a.ws_swml, wid, D);
+    }
+  }
+
+  Row<DL> r;
+  const int N = sp.n + ss.n;
+  for (int k0 = 0; k0 < N; k0 += 64) {
+    const int k = k0 + lane;
+    const float* ml = nullptr;
+    const float* o = nullptr;
+    bool have = false;
+    if (k < sp.n)
+      have = piece_at(sp, k, D, &ml, &o);
+    else if (k < N)
+      have = piece_at(ss, k - sp.n, D, &ml, &o);
+    const float m = have ? ml[0] : -INFINITY;
+    const float l = have ? ml[1] : 0.0f;
+    const float M = wave_max(m);
+    const float Ms = safe_max(M);
+    const float wgt = have ? fast_exp2(m - Ms) : 0.0f;
+    const float lsum = wave_sum(l * wgt);
+    float acc[DL];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
+    const uint64_t op = reinterpret_cast<uint64_t>(o);
+    const int nk = min(64, N - k0);
+    for (int j = 0; j < nk; ++j) {
+      const float wj = readlane_f32(wgt, j);
+      if (wj == 0.0f) continue;  // empty share, or a weight that underflowed
+      const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(op >> 32), j) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)op, j);
+      const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) acc[e] = fmaf(wj, oj[e], acc[e]);
+    }
+    fold(r, M, lsum, acc);
+  }
+  write_row(r, out);
 }
 
 }  // namespace
 }  // namespace pkv
 
 #include "attn_gqa_mfma.hpp"
+#include "attn_shared_mfma.hpp"
 
 namespace pkv {
 namespace {
@@ -550,6 +833,34 @@ KernFn pick_reduce(int D, int G) {
   return nullptr;
 }
 
+template <int D>
+KernFn pick_reduce_shared_d(int G) {
+  switch (G) {
+    case 1: return attn_reduce_shared_kernel<D, 1>;
+    case 2: return attn_reduce_shared_kernel<D, 2>;
+    case 4: return attn_reduce_shared_kernel<D, 4>;
+    case 8: return attn_reduce_shared_kernel<D, 8>;
+    default: return nullptr;
+  }
+}
+
+template <int D>
+KernFn pick_shared_d(int fmt) {
+  switch (fmt) {
+    case kF16: return attn_shared_mfma_kernel<D, kF16, kWaves>;
+    case kE4M3: return attn_shared_mfma_kernel<D, kE4M3, kWaves>;
+    case kE5M2: return attn_shared_mfma_kernel<D, kE5M2, kWaves>;
+    default: return nullptr;
+  }
+}
+
+// (shared pass, merge) kernels of paged_attn_decode_shared
+bool pick_shared(int D, int G, int fmt, KernFn* shared, KernFn* reduce) {
+  *shared = D == 64 ? pick_shared_d<64>(fmt) : D == 128 ? pick_shared_d<128>(fmt) : nullptr;
+  *reduce = D == 64 ? pick_reduce_shared_d<64>(G) : D == 128 ? pick_reduce_shared_d<128>(G) : nullptr;
+  return *shared && *reduce;
+}
+
 int log2_exact(int v) {
   int k = 0;
   while ((1 << k) < v) ++k;
@@ -558,7 +869,9 @@ int log2_exact(int v) {
 
 int unit_tokens_for(int group) { return group >= 4 ? 32 : kTile; }
 
-size_t dyn_lds_bytes(int B) { return (size_t)(B + 1 + kWaves * 64) * sizeof(int); }
+size_t dyn_lds_bytes(int B, bool groups = false) {
+  return (size_t)(B + 1 + kWaves * 64 + (groups ? B : 0)) * sizeof(int);
+}
 
 // Workgroups of a pass-1 kernel that can be resident at once on the current
 // device (occupancy x compute units) and the compute-unit count, cached per
@@ -621,7 +934,8 @@ struct Plan {
 // Validates the shape and picks the kernels and the worker count; returns a
 // status code.
 int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-         int max_blocks_per_seq, int kv_dtype, int partition_tokens, bool need_workers, Plan* p) {
+         int max_blocks_per_seq, int kv_dtype, int partition_tokens, bool need_workers, Plan* p,
+         bool groups = false) {
   if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
@@ -648,7 +962,7 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
     W = (ub_all + per - 1) / per;
   } else {
     int wgs = 0, cus = 0;
-    if (!device_capacity(p->fn, dyn_lds_bytes(B), &wgs, &cus)) return PKV_ERR_HIP;
+    if (!device_capacity(p->fn, dyn_lds_bytes(B, groups), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
     const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype != PKV_KV_F16) * 4 * cus;
     if (W > by_simd) W = by_simd;
@@ -691,6 +1005,68 @@ extern "C" size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_head
 
 namespace pkv {
 namespace {
+
+// Workspace of paged_attn_decode_shared, byte offsets of its regions (each
+// 256-byte aligned): pass-1 slots and unit prefix as paged_attn_decode's,
+// then the merge buffers of whole pieces, the shared pass's slots and its
+// unit prefix over the groups.
+struct SharedLayout {
+  size_t o, ml, pt, wo, wml, swo, swml, so, sml, spt, gid, total;
+};
+
+SharedLayout shared_layout(int B, int Hq, int Hkv, int D) {
+  const size_t G = (size_t)(Hq / Hkv);
+  const size_t rows = (size_t)B * Hq;
+  SharedLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return at;
+  };
+  L.o = take((size_t)kMaxWorkers * 2 * G * D * sizeof(float));
+  L.ml = take((size_t)kMaxWorkers * 2 * G * 2 * sizeof(float));
+  L.pt = take((size_t)(B + 1) * sizeof(int32_t));
+  L.wo = take(rows * D * sizeof(float));
+  L.wml = take(rows * 2 * sizeof(float));
+  L.swo = take(rows * D * sizeof(float));
+  L.swml = take(rows * 2 * sizeof(float));
+  L.so = take((size_t)kMaxSharedWorkers * 2 * kSharedCols * D * sizeof(float));
+  L.sml = take((size_t)kMaxSharedWorkers * 2 * kSharedCols * 2 * sizeof(float));
+  L.spt = take((size_t)(B + 1) * sizeof(int32_t));
+  L.gid = take((size_t)B * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+// Dynamic LDS of the shared pass: unit prefix, scan space, three per-group arrays.
+size_t shared_lds_bytes(int NG) { return (size_t)(4 * NG + 1 + kWaves * 64) * sizeof(int); }
+
+// Workers of the shared pass: two per SIMD (a kSharedCols-column tile keeps
+// about 200 registers per lane), within what the device holds at once; with
+// partition_tokens, about that many tokens each of the largest shared unit
+// space the groups can describe.
+int shared_workers(KernFn fn, int B, int NG, int Hkv, int G, int max_blocks, int block_size,
+                   int partition_tokens, int* W_out) {
+  const int64_t max_units = ((int64_t)max_blocks * block_size + 31) / 32;
+  const int64_t parts = (int64_t)NG + ((int64_t)B * G + kSharedCols - 1) / kSharedCols;
+  const int64_t ub = (int64_t)Hkv * parts * max_units;
+  int64_t W;
+  if (partition_tokens > 0) {
+    const int64_t per = (partition_tokens + 31) / 32;
+    W = (ub + per - 1) / per;
+  } else {
+    int wgs = 0, cus = 0;
+    if (!device_capacity(fn, shared_lds_bytes(NG), &wgs, &cus)) return PKV_ERR_HIP;
+    W = (int64_t)wgs * kWaves;
+    if (W > (int64_t)2 * 4 * cus) W = (int64_t)2 * 4 * cus;
+  }
+  if (W > ub) W = ub;
+  if (W > kMaxSharedWorkers) W = kMaxSharedWorkers;
+  if (W < kWaves) W = kWaves;
+  *W_out = (int)(W / kWaves * kWaves);
+  return PKV_OK;
+}
 
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                 int max_blocks_per_seq, const int32_t* ctx_lens, int num_seqs, int num_q_heads, int num_kv_heads,
@@ -796,4 +1172,108 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_cache, 
                                   ctx_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   block_size, num_blocks, sm_scale, kv_dtype, k_scale, v_scale,
                                   partition_tokens, workspace, workspace_bytes, 3, stream);
+}
+
+extern "C" size_t paged_attn_decode_shared_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                                           int head_dim) {
+  if (num_seqs <= 0 || num_seqs > pkv::kMaxSeqs || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  return pkv::shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
+}
+
+extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                        float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                                        const float* k_scales, const float* v_scales,
+                                        const int32_t* group_first, const int32_t* group_size,
+                                        const int32_t* group_prefix, int num_groups, int partition_tokens,
+                                        void* workspace, size_t workspace_bytes, int passes, void* stream) {
+  using namespace pkv;
+  if (passes < 1 || passes > 7 || num_blocks <= 0 || num_seqs > kMaxSeqs) return PKV_ERR_INVALID;
+  if (num_groups < 0 || num_groups > (num_seqs > 0 ? num_seqs : 0)) return PKV_ERR_INVALID;
+  if ((k_scales == nullptr) != (v_scales == nullptr)) return PKV_ERR_INVALID;
+  Plan pl;
+  int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
+                partition_tokens, false, &pl);
+  if (rc != PKV_OK) return rc;
+  const int G = num_q_heads / num_kv_heads;
+  KernFn shared_fn, reduce_fn;
+  if (!pick_shared(head_dim, G, kv_dtype, &shared_fn, &reduce_fn)) return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
+  if (num_groups > 0 && (!group_first || !group_size || !group_prefix)) return PKV_ERR_INVALID;
+  const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  if (!workspace || workspace_bytes < lay.total) return PKV_ERR_INVALID;
+  rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
+            partition_tokens, true, &pl, num_groups > 0);
+  if (rc != PKV_OK) return rc;
+  int s_workers = kWaves;
+  if (num_groups > 0) {
+    rc = shared_workers(shared_fn, num_seqs, num_groups, num_kv_heads, G, max_blocks_per_seq, block_size,
+                        partition_tokens, &s_workers);
+    if (rc != PKV_OK) return rc;
+  }
+
+  const bool fp8 = kv_dtype != PKV_KV_F16;
+  const bool per_head = fp8 && k_scales != nullptr;
+  const float kLog2e = 1.4426950408889634f;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  AttnArgs a;
+  a.q = static_cast<const f16*>(q);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.ws_o = reinterpret_cast<float*>(ws + lay.o);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+  a.ws_pt = reinterpret_cast<int32_t*>(ws + lay.pt);
+  a.out = static_cast<f16*>(out);
+  a.max_blocks = max_blocks_per_seq;
+  a.B = num_seqs;
+  a.Hkv = num_kv_heads;
+  a.Hq = num_q_heads;
+  a.bs_log2 = log2_exact(block_size);
+  a.num_blocks = num_blocks;
+  a.unit_tokens = pl.unit;
+  a.workers = pl.workers;
+  a.qk_scale = sm_scale * kLog2e * (fp8 && !per_head ? k_scale : 1.0f);
+  a.v_out_scale = fp8 && !per_head ? v_scale : 1.0f;
+  a.k_scale_h = per_head ? k_scales : nullptr;
+  a.v_scale_h = per_head ? v_scales : nullptr;
+  a.qk_base = sm_scale * kLog2e;
+  a.grp_first = group_first;
+  a.grp_size = group_size;
+  a.grp_prefix = group_prefix;
+  a.NG = num_groups;
+  a.g_log2 = log2_exact(G);
+  a.s_workers = s_workers;
+  a.ws_wo = reinterpret_cast<float*>(ws + lay.wo);
+  a.ws_wml = reinterpret_cast<float*>(ws + lay.wml);
+  a.ws_swo = reinterpret_cast<float*>(ws + lay.swo);
+  a.ws_swml = reinterpret_cast<float*>(ws + lay.swml);
+  a.ws_so = reinterpret_cast<float*>(ws + lay.so);
+  a.ws_sml = reinterpret_cast<float*>(ws + lay.sml);
+  a.ws_spt = reinterpret_cast<int32_t*>(ws + lay.spt);
+  a.ws_gid = reinterpret_cast<int32_t*>(ws + lay.gid);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((passes & 1) && num_groups > 0) {
+    hipLaunchKernelGGL(shared_fn, dim3((unsigned)(s_workers / kWaves)), dim3(kWaves * 64),
+                       shared_lds_bytes(num_groups), s, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  if (passes & 2) {
+    hipLaunchKernelGGL(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64),
+                       dyn_lds_bytes(num_seqs, num_groups > 0), s, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  if (passes & 4) {
+    const int waves = num_seqs * num_q_heads;
+    hipLaunchKernelGGL(reduce_fn, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
 }

@@ -33,6 +33,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+constexpr float kLazy = 8.0f;  // log2 headroom before a running max moves
+
 __device__ __forceinline__ f16x8 f16x8_from_u32x4(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // 8 fp8 bytes (two dwords) -> 8 fp16 values, exactly
@@ -66,7 +68,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   __shared__ __align__(16) _Float16 vlds[NW * 32 * VS];
   extern __shared__ int dyn_smem[];
   int* pt = dyn_smem;
-  build_prefix(a, pt, pt + a.B + 1);
+  int* pre = pt + a.B + 1 + NW * 64;
+  build_prefix(a, pt, pt + a.B + 1, pre);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -97,6 +100,9 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
+    // a member of a shared-prefix group starts after the shared tokens
+    const int sgrp = a.NG ? wave_uniform(pre[seq]) : -1;  // >= 0 for a group member
+    const int base = private_start(sgrp, L);
     const float qk_scale = head_qk_scale(a, pc.head);
     const float v_scale = head_v_scale(a, pc.head);
 
@@ -126,12 +132,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
       int my_blk = -1;
       {
         const int jj = j0 + (lane >> 1);
-        const int tt = 32 * jj + 16 * (lane & 1);
+        const int tt = base + 32 * jj + 16 * (lane & 1);
         if (jj < pc.u1 && tt < L) my_blk = tab[tt >> a.bs_log2];
       }
       const int nj = min(32, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
-        const int ta = 32 * (j0 + j);
+        const int ta = base + 32 * (j0 + j);
         const int blk_a = __builtin_amdgcn_readlane(my_blk, 2 * j);
         const int blk_b = __builtin_amdgcn_readlane(my_blk, 2 * j + 1);
         const bool ok_a = (unsigned)blk_a < (unsigned)a.num_blocks;
@@ -184,14 +190,23 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           z[v] = (ok_a && tka < L) ? sa[v] * qk_scale : -INFINITY;
           z[4 + v] = (ok_b && tkb < L) ? sb[v] * qk_scale : -INFINITY;
         }
+        // the running max (log2 units) moves only when some lane's logits exceed
+        // it by more than kLazy: between moves the accumulators are not
+        // rescaled and no lane shuffles run (p <= 2^kLazy, well inside fp16)
         float mt = z[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
-        mt = fmaxf(mt, shfl_xor_f32(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f32(mt, 32));
-        const float mn = fmaxf(m_run, mt);
-        const float ms = safe_max(mn);
-        const float alpha = fast_exp2(m_run - ms);
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy)) {
+          mt = fmaxf(mt, shfl_xor_f32(mt, 16));
+          mt = fmaxf(mt, shfl_xor_f32(mt, 32));
+          const float mn = fmaxf(m_run, mt);
+          const float alpha = fast_exp2(m_run - safe_max(mn));
+          l_part *= alpha;
+#pragma unroll
+          for (int c = 0; c < NT; ++c) o[c] *= alpha;
+          m_run = mn;
+        }
+        const float ms = safe_max(m_run);
         f16x8 pb;
         float ps = 0.0f;
 #pragma unroll
@@ -200,10 +215,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           ps += p;
           pb[i] = (_Float16)p;
         }
-        l_part = l_part * alpha + ps;
-        m_run = mn;
-#pragma unroll
-        for (int c = 0; c < NT; ++c) o[c] *= alpha;
+        l_part += ps;
 
         // V rows -> LDS as fp16 (rows past the end as zeros)
 #pragma unroll
@@ -244,7 +256,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
     const int slot = t == start ? 0 : 1;
     if (col < G) {
-      if (whole) {
+      if (whole && sgrp < 0) {
         const float sc = l_part > 0.0f ? v_scale / l_part : 0.0f;
         f16* orow = a.out + ((size_t)seq * a.Hq + hq0 + col) * D + 4 * grp;
 #pragma unroll
@@ -255,13 +267,15 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           *reinterpret_cast<f16x4*>(orow + 16 * c) = h;
         }
       } else {
-        const size_t pi = ((size_t)w * 2 + slot) * G + col;
-        float* orow = a.ws_o + pi * D + 4 * grp;
+        // a group member's whole segment goes to the buffer the merge reads
+        const size_t pi = whole ? (size_t)seq * a.Hq + hq0 + col : ((size_t)w * 2 + slot) * G + col;
+        float* orow = (whole ? a.ws_wo : a.ws_o) + pi * D + 4 * grp;
+        float* ml = whole ? a.ws_wml : a.ws_ml;
 #pragma unroll
         for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * v_scale;
         if (grp == 0) {
-          a.ws_ml[2 * pi] = m_run;
-          a.ws_ml[2 * pi + 1] = l_part;
+          ml[2 * pi] = m_run;
+          ml[2 * pi + 1] = l_part;
         }
       }
     }

@@ -808,4 +808,53 @@ int pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int32_t* ta
   return PKV_OK;
 }
 
+// Runs of consecutive batch entries whose tables start with the same full
+// blocks. Forked sequences and prefix-cache hits hold one physical block at
+// the same table position, so one read of it serves the whole run.
+int pkv_bm_prefix_groups(const pkv_bm* bm, const int64_t* seqs, int n_seqs, int max_members,
+                         int32_t* group_first, int32_t* group_size, int32_t* group_prefix, int cap,
+                         int* num_groups) {
+  if (!bm || !num_groups || n_seqs < 0 || max_members < 1 || cap < 0) return PKV_ERR_INVALID;
+  if (n_seqs > 0 && !seqs) return PKV_ERR_INVALID;
+  std::vector<const Seq*> s(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PKV_ERR_NO_SEQ;
+    s[i] = &it->second;
+  }
+  const int64_t bs = bm->bs;
+  // the first block if the sequence holds it in full, else -1
+  auto head = [&](int i) { return s[i]->count >= bs ? s[i]->table[0] : -1; };
+  struct G {
+    int first, size, prefix;
+  };
+  std::vector<G> out;
+  for (int i = 0; i < n_seqs;) {
+    const int32_t h = head(i);
+    int j = i + 1;
+    if (h >= 0)
+      while (j < n_seqs && j - i < max_members && head(j) == h) ++j;
+    if (j - i >= 2) {
+      int64_t n = 0;
+      for (;; ++n) {
+        bool same = true;
+        for (int m = i; m < j && same; ++m)
+          same = (n + 1) * bs <= s[m]->count && s[m]->table[n] == s[i]->table[n];
+        if (!same) break;
+      }
+      out.push_back(G{i, j - i, static_cast<int>(n * bs)});
+    }
+    i = j;
+  }
+  if (static_cast<int>(out.size()) > cap || (!out.empty() && (!group_first || !group_size || !group_prefix)))
+    return PKV_ERR_INVALID;
+  for (size_t g = 0; g < out.size(); ++g) {
+    group_first[g] = out[g].first;
+    group_size[g] = out[g].size;
+    group_prefix[g] = out[g].prefix;
+  }
+  *num_groups = static_cast<int>(out.size());
+  return PKV_OK;
+}
+
 }  // extern "C"

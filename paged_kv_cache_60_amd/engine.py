@@ -146,10 +146,14 @@ class PagedKVEngine:
                            self.k_inv_scale, self.v_inv_scale)
 
     # ------------------------------------------------------ decode steps
-    def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0):
+    def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0, shared_prefix=False):
         """Set up a decode batch: device-resident block tables (uploaded once
         here), the per-step metadata buffers (two pinned halves on the host,
-        one set on the device) and the attention workspace."""
+        one set on the device) and the attention workspace. shared_prefix:
+        find the runs of the batch that share leading full blocks (forked
+        beams, common prefixes) and attend with paged_attn_decode_shared,
+        which reads those blocks once per run; decode steps only append, so
+        the runs stay valid until the batch is set up again."""
         torch.cuda.synchronize(self.device)  # queued kernels may still read the previous buffers
         B = len(batch_seqs)
         self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
@@ -176,7 +180,13 @@ class PagedKVEngine:
         tab, ctx = self.host_tables()
         self.tables_dev = torch.from_numpy(tab).to(self.device)
         self.ctx_dev.copy_(torch.from_numpy(ctx))
-        wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
+        self.groups = None
+        if shared_prefix:
+            g = self.bm.prefix_groups(self.batch, ops.SHARED_COLUMNS // (self.hq // self.hkv))
+            self.groups = torch.from_numpy(np.ascontiguousarray(g)).to(self.device)
+            wsb = ops.shared_workspace_bytes(B, self.hq, self.hkv, self.d)
+        else:
+            wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
         torch.cuda.synchronize(self.device)
 
@@ -243,9 +253,18 @@ class PagedKVEngine:
                                 n_upd, self.tables_dev, self.kv_dtype, self.k_inv_scale, self.v_inv_scale)
 
     def attend(self, q, out, passes=3):
-        ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
-                              1.0 / float(self.d) ** 0.5, self.kv_dtype, self.k_scale, self.v_scale,
-                              self.partition_tokens, self.workspace, passes)
+        """Attention of the step; passes: 1 = pass 1 (with the shared-prefix
+        pass when groups are set), 2 = pass 2 (the merge), 3 = both."""
+        sm_scale = 1.0 / float(self.d) ** 0.5
+        if self.groups is not None:
+            bits = (3 if passes & 1 else 0) | (4 if passes & 2 else 0)
+            ops.paged_attn_decode_shared(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
+                                         self.groups, sm_scale, self.kv_dtype, self.k_scale, self.v_scale,
+                                         self.partition_tokens, self.workspace, bits)
+            return
+        ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev, sm_scale,
+                              self.kv_dtype, self.k_scale, self.v_scale, self.partition_tokens, self.workspace,
+                              passes)
 
     def decode_step(self, k_new, v_new, q, out):
         """Full decode step: append one token per batch sequence, write it, attend."""

@@ -100,9 +100,12 @@ def step_inputs(wl, step, device="cuda"):
             torch.from_numpy(q).to(device))
 
 
-def run_steps(eng: PagedKVEngine, wl, steps: int, partition_tokens: int = 0, device="cuda"):
-    """Decode `steps` steps; returns per-step outputs (host fp16 arrays) and (tables, ctx)."""
-    eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, partition_tokens)
+def run_steps(eng: PagedKVEngine, wl, steps: int, partition_tokens: int = 0, device="cuda",
+              shared_prefix: bool = False):
+    """Decode `steps` steps; returns per-step outputs (host fp16 arrays) and (tables, ctx).
+    shared_prefix: attend with the shared-prefix decode (runs of the batch that
+    share leading blocks read them once)."""
+    eng.prepare_steps(wl.batch, wl.max_blocks_per_seq, partition_tokens, shared_prefix=shared_prefix)
     outs, metas = [], []
     B = len(wl.batch)
     for s in range(steps):

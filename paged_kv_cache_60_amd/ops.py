@@ -224,6 +224,62 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
                                        _stream_ptr(stream)), w)
 
 
+# query columns (sequence, query head) of one pass over a group's shared blocks;
+# a group of more than SHARED_COLUMNS / G members takes several passes
+SHARED_COLUMNS = 32
+
+
+def shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
+    """Bytes of device workspace paged_attn_decode_shared needs (0 for a bad shape)."""
+    return int(_lib.load().paged_attn_decode_shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                                    head_dim))
+
+
+def paged_attn_decode_shared(out, q, k_cache, v_cache, block_tables, ctx_lens, groups, sm_scale, kv_dtype=F16,
+                             k_scale=1.0, v_scale=1.0, partition_tokens=0, workspace=None, passes=7,
+                             stream=None):
+    """paged_attn_decode for a batch whose runs of sequences share leading
+    blocks: groups is a device int32 tensor [3, num_groups] holding, per
+    group, its first batch index, its member count and its shared tokens (as
+    BlockManager.prefix_groups returns them). passes: bit 0 the pass over the
+    shared blocks, bit 1 pass 1 over the rest, bit 2 the merge."""
+    w = "paged_attn_decode_shared"
+    _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
+    _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype) and k_cache.shape == v_cache.shape,
+             w, "caches")
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _require(d == d2, w, "head_dim")
+    _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(), w, "block_tables")
+    _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
+             and ctx_lens.is_contiguous(), w, "ctx_lens")
+    _require(groups.is_cuda and groups.dtype == torch.int32 and groups.dim() == 2 and groups.shape[0] == 3
+             and groups.is_contiguous(), w, "groups")
+    ng = groups.shape[1]
+    maxb = block_tables.shape[1]
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if B > 0:
+        need = shared_workspace_bytes(B, hq, hkv, d)
+        _require(need > 0, w, "shape")
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _require(workspace.is_cuda and workspace.numel() * workspace.element_size() >= need, w,
+                 "workspace too small")
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
+    per_head = _per_head(k_scale)
+    if per_head:
+        _require(_scales_ok(k_scale, v_scale, hkv), w, "per-head scales")
+    gp = [ctypes.c_void_p(groups.data_ptr() + r * ng * 4) if ng else ctypes.c_void_p(0) for r in range(3)]
+    check(_lib.load().paged_attn_decode_shared(
+        _p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), maxb, _p(ctx_lens), B, hq, hkv, d, bs, nb,
+        float(sm_scale), kv_dtype_code(kv_dtype), 1.0 if per_head else float(k_scale),
+        1.0 if per_head else float(v_scale), _p(k_scale) if per_head else ctypes.c_void_p(0),
+        _p(v_scale) if per_head else ctypes.c_void_p(0), gp[0], gp[1], gp[2], ng, int(partition_tokens),
+        ws_ptr, ws_bytes, int(passes), _stream_ptr(stream)), w)
+
+
 def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, ctx_lens, q_start, sm_scale, kv_dtype=F16,
                        k_scale=1.0, v_scale=1.0, stream=None):
     """Chunked causal prefill. out/q [total_q, Hq, D] fp16; block_tables [B, max_blocks] int32;

@@ -56,7 +56,7 @@ def attn(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d=96), dict(bs=8), dict(bs=48), dict(hq=12, hkv=8), dict(hq=24, hkv=8),
-                                 dict(dt=2), dict(part=100), dict(part=8), dict(part=-16), dict(passes=0),
+                                 dict(dt=3), dict(part=100), dict(part=8), dict(part=-16), dict(passes=0),
                                  dict(passes=4),
                                  dict(hkv=0), dict(nb=0), dict(maxb=0), dict(out=N), dict(q=N),
                                  dict(ws=N, maxb=64), dict(wsb=16, maxb=64), dict(B=-1)])
@@ -110,3 +110,37 @@ def test_write_and_copy_validation():
     assert lib.paged_block_copy(FAKE, FAKE, FAKE, 0, 4, 4096, N) == 0
     assert lib.paged_block_copy(FAKE, FAKE, FAKE, 2, 4, 4100, N) == -1
     assert lib.paged_block_copy(FAKE, FAKE, N, 2, 4, 4096, N) == -1
+
+
+def shared(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, maxb=8, ctx=FAKE, B=2, hq=8, hkv=8, d=128, bs=16,
+             nb=16, scale=0.1, dt=0, ks=1.0, vs=1.0, kss=N, vss=N, gf=FAKE, gs=FAKE, gp=FAKE, ng=1, part=0,
+             ws=FAKE, wsb=1 << 30, passes=7, stream=N)
+    a.update(kw)
+    return _lib.load().paged_attn_decode_shared(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(passes=0), dict(passes=8), dict(ng=-1), dict(ng=3), dict(B=4097, ng=0),
+                                 dict(gf=N), dict(gp=N), dict(kss=FAKE), dict(d=96), dict(hq=12),
+                                 dict(ws=N), dict(wsb=1 << 20), dict(out=N), dict(nb=0), dict(part=8)])
+def test_shared_decode_rejects_bad_arguments(bad):
+    assert shared(**bad) == _lib.PKV_ERR_INVALID
+
+
+def test_shared_decode_empty_batch_is_ok():
+    assert shared(B=0, ng=0) == _lib.PKV_OK
+
+
+def test_shared_workspace_bytes():
+    lib = _lib.load()
+
+    def expect(b, hq, hkv, d):
+        g, rows = hq // hkv, b * hq
+        regions = [8192 * 2 * g * d * 4, 8192 * 2 * g * 2 * 4, (b + 1) * 4, rows * d * 4, rows * 2 * 4,
+                   rows * d * 4, rows * 2 * 4, 2048 * 2 * 32 * d * 4, 2048 * 2 * 32 * 2 * 4, (b + 1) * 4, b * 4]
+        return sum(-(-n // 256) * 256 for n in regions)
+    f = lib.paged_attn_decode_shared_workspace_bytes
+    assert f(128, 64, 8, 128) == expect(128, 64, 8, 128)
+    assert f(256, 16, 8, 128) == expect(256, 16, 8, 128)
+    assert f(3, 8, 8, 64) == expect(3, 8, 8, 64)
+    assert f(4097, 8, 8, 64) == 0 and f(0, 8, 8, 64) == 0 and f(4, 12, 8, 64) == 0 and f(4, 8, 8, 96) == 0

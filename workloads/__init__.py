@@ -575,6 +575,57 @@ def small_prefill(seed: int, lengths, chunks, num_q_heads, num_kv_heads, head_di
     return wl
 
 
+def small_forks(seed: int, prompts, members, tails, singles, num_q_heads, num_kv_heads, head_dim,
+                block_size, kv_dtype="f16", max_steps=1, per_head=False) -> Workload:
+    """Prompts forked into several members that then grow private tails
+    (appended one token per member per round, so the first members to write
+    into a shared partial block copy it), with independent sequences between
+    the groups in the batch: prompt i has members[i] sequences, tails[i] their
+    tail lengths, and singles[i] independent sequences follow its group."""
+    bs = block_size
+    ops0, ops1, batch, lengths = [], [], [], []
+    nxt, key = 0, 0
+    groups = []
+    for i, P in enumerate(prompts):
+        ids = list(range(nxt, nxt + members[i]))
+        nxt += members[i]
+        ops0.append(Op("allocate", ids[0], P, key=key))
+        key += 1
+        ops1 += [Op("fork", c, src=ids[0]) for c in ids[1:]]
+        groups.append(ids)
+        batch += ids
+        lengths += [P + t + 1 for t in tails[i]]
+        for _ in range(singles[i]):
+            L = 16 * (i + 1) + 7 * len(batch) + 1
+            ops0.append(Op("allocate", nxt, L, key=key))
+            key += 1
+            batch.append(nxt)
+            lengths.append(L + 1)
+            nxt += 1
+    rounds = [ops0, ops1]
+    for r in range(max(max(t) for t in tails)):
+        ops = []
+        for i, ids in enumerate(groups):
+            for m, s_ in enumerate(ids):
+                if tails[i][m] > r:
+                    ops.append(Op("append", s_, 1, key=key))
+                    key += 1
+        if ops:
+            rounds.append(ops)
+    need = sum(_ceil_div(L + max_steps, bs) for L in lengths)
+    nb = max(1, math.ceil(1.25 * need))
+    wl = Workload(
+        name=f"forks_{seed}", seed=seed, description="forked prompts with private tails",
+        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=bs,
+        kv_dtype=kv_dtype, num_blocks=nb, free_order=_perm(seed, nb), batch=batch, setup_rounds=rounds,
+        max_steps=max_steps, max_blocks_per_seq=_ceil_div(max(lengths) - 1 + max_steps, bs),
+        meta={"lengths": lengths},
+    )
+    if kv_dtype != "f16":
+        _fp8_scales(wl, max_steps, per_head)
+    return wl
+
+
 def small_custom(seed: int, lengths, num_q_heads, num_kv_heads, head_dim, block_size,
                  kv_dtype="f16", num_blocks=None, max_steps=1, slack=1.25, per_head=False) -> Workload:
     """A plain workload of independent sequences for edge-case tests."""
