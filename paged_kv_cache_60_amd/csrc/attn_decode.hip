@@ -176,13 +176,10 @@ __device__ void build_group_map(const AttnArgs& a, int* pre) {
 // prefix is longer).
 __device__ __forceinline__ int private_start(int pre, int L) { return pre < 0 ? 0 : min(pre, L); }
 
-// Units of the shared pass for group g: one run of the prefix's 32-token
-// units per kSharedCols query columns of its members.
+// Units of the shared pass for one part of group g: its prefix's 32-token
+// units (a part is up to kSharedCols query columns of the group's members).
 __device__ __forceinline__ int group_units(const AttnArgs& a, int g) {
   return (group_tokens(a, g) + 31) / 32;
-}
-__device__ __forceinline__ int group_parts(const AttnArgs& a, int g) {
-  return ((group_members(a, g) << a.g_log2) + kSharedCols - 1) / kSharedCols;
 }
 
 // pt[0] = 0, pt[i + 1] = pt[i] + units(i) for i < n, by all threads of the

@@ -242,6 +242,87 @@ struct Stage {
   }
 };
 
+// fp16 chunks staged straight from global memory into LDS (global_load_lds,
+// 16 bytes per lane; lane i of a wave instruction lands in LDS slot i). The
+// LDS layout is pair-major: for each pair p of 16-byte chunks of a row
+// (halves 16p .. 16p + 15), the 32 rows of the chunk follow one another, 32
+// bytes each: byte p * 1024 + r * 32 + 16 (c % 2) holds chunk c of row r. One
+// instruction fills one pair for all 32 rows; the q.k and transposing V reads
+// then differ only by immediate offsets between pairs, and a quarter-wave's K
+// read touches each bank at most twice.
+template <int D>
+struct Direct {
+  static constexpr int RB = D * 2;               // bytes of one fp16 row
+  static constexpr int NP = D / 16;              // chunk pairs per row
+  static constexpr int PAIR_HALVES = kChunk * 16;  // halves of one pair block (1 KiB)
+  static constexpr int HALVES = NP * PAIR_HALVES;  // halves of one tensor's chunk
+  static constexpr int PPW = NP / kWaves;        // pairs per wave, per tensor
+  static_assert(PPW >= 1 && NP % kWaves == 0, "chunk shape");
+
+  // halves offset of 16-byte chunk c of row r, plus e halves within the chunk
+  __device__ static __forceinline__ int at(int r, int c, int e) {
+    return (c >> 1) * PAIR_HALVES + r * 16 + (c & 1) * 8 + e;
+  }
+
+  // This lane's byte offset within its 16-token tile (the same for every pair,
+  // and every chunk of the token loop): row lane / 2 mod 16, chunk lane % 2.
+  __device__ static __forceinline__ uint32_t lane_off(int lane) {
+    return (uint32_t)(((lane >> 1) & 15) * RB + (lane & 1) * 16);
+  }
+
+  // K rows to buf[0, HALVES), V rows to buf[HALVES, 2 HALVES). Lanes 0-31 hold
+  // rows 0-15 (block blk_a), lanes 32-63 rows 16-31 (blk_b); a tile in a block
+  // outside the pool reads the head's first rows (V zeroed later).
+  __device__ static __forceinline__ void issue(const PrefillArgs& a, int blk_a, int blk_b, const uint8_t* kc_head,
+                                               const uint8_t* vc_head, size_t blk_stride, int t0, _Float16* buf,
+                                               int wave, int lane, uint32_t loff) {
+    const int bsm = (1 << a.bs_log2) - 1;
+    const bool oka = (unsigned)blk_a < (unsigned)a.num_blocks;
+    const bool okb = (unsigned)blk_b < (unsigned)a.num_blocks;
+    const size_t base_a = oka ? (size_t)blk_a * blk_stride + (size_t)(t0 & bsm) * RB : 0;
+    const size_t base_b = okb ? (size_t)blk_b * blk_stride + (size_t)((t0 + 16) & bsm) * RB : 0;
+    const size_t off = (lane < 32 ? base_a : base_b) + loff;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int pp = wave * PPW + i;  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kc_head + off + pp * 32),
+                                       (__attribute__((address_space(3))) void*)(buf + pp * PAIR_HALVES), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vc_head + off + pp * 32),
+                                       (__attribute__((address_space(3))) void*)(buf + HALVES + pp * PAIR_HALVES),
+                                       16, 0, 0);
+    }
+  }
+
+  // V rows that must read as zeros: past `end`, or in a tile outside the pool
+  __device__ static __forceinline__ void zero_invalid(_Float16* buf, int t0, int end, bool oka, bool okb) {
+    _Float16* vb = buf + HALVES;
+    for (int idx = threadIdx.x; idx < kChunk * NP; idx += kWaves * 64) {
+      const int r = idx % kChunk;
+      const int pp = idx / kChunk;
+      const bool ok = (r < 16 ? oka : okb) && t0 + r < end;
+      if (!ok) {
+        u32x4* d = reinterpret_cast<u32x4*>(vb + pp * PAIR_HALVES + r * 16);
+        d[0] = u32x4{0u, 0u, 0u, 0u};
+        d[1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+};
+
+// Where a chunk buffer keeps row r's 16-byte piece c (8 halves), plus e
+// halves, for K and for V (offsets in halves from the buffer's start).
+template <int D, bool FP8>
+struct PaddedLayout {  // rows padded to D + 8 halves (Stage)
+  using S = ChunkShape<D, FP8>;
+  __device__ static __forceinline__ int k(int r, int c) { return r * S::KS + c * 8; }
+  __device__ static __forceinline__ int v(int r, int c, int e) { return kChunk * S::KS + r * S::VS + c * 8 + e; }
+};
+template <int D>
+struct PairLayout {  // pair-major rows (Direct)
+  __device__ static __forceinline__ int k(int r, int c) { return Direct<D>::at(r, c, 0); }
+  __device__ static __forceinline__ int v(int r, int c, int e) { return Direct<D>::HALVES + Direct<D>::at(r, c, e); }
+};
+
 // three workgroups per compute unit (3 waves per SIMD) hide the LDS and
 // matrix-core latencies of the token loop far better than two (measured on
 // MI355X: 10.7 -> 8.4 ms on the Qwen3-shaped prefix-cache prefill)
@@ -255,11 +336,18 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
   constexpr int NT = D / 16;   // output head-dim tiles
   constexpr int DQ = D / 4;    // head-dim elements per lane group in the q.k operands
   constexpr int QT = kTileCols / G;  // query tokens per workgroup tile
-  constexpr int LDS_HALVES = 2 * S::BUF > (kMaxSeqs + 1 + kWaves * 64) * 2 ? 2 * S::BUF
-                                                                          : (kMaxSeqs + 1 + kWaves * 64) * 2;
+  // fp16 chunks go straight from global memory to LDS (Direct); fp8 chunks are
+  // widened on the way through registers (Stage)
+  constexpr bool DIRECT = !FP8;
+  constexpr int PREFIX_HALVES = (kMaxSeqs + 1 + kWaves * 64) * 2;
+  constexpr int LDS_HALVES = !DIRECT && 2 * S::BUF > PREFIX_HALVES ? 2 * S::BUF : PREFIX_HALVES;
 
-  // two K/V chunk buffers; before the token loop the same memory holds the tile prefix
+  // the tile prefix; with Stage the same memory then holds the two chunk buffers
   __shared__ __align__(16) _Float16 lds[LDS_HALVES];
+  // the two chunk buffers of Direct: separate arrays, so that the compiler can
+  // tell the buffer being read from the one the loads are landing in
+  __shared__ __align__(16) _Float16 dbuf0[DIRECT ? 2 * Direct<D>::HALVES : 8];
+  __shared__ __align__(16) _Float16 dbuf1[DIRECT ? 2 * Direct<D>::HALVES : 8];
   int* pt = reinterpret_cast<int*>(lds);
   build_tile_prefix(a, G, pt, pt + a.B + 1);
 
@@ -342,23 +430,11 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
     *bb = t0 + 16 < kend ? __builtin_amdgcn_readlane(lane_blk, tl + 1 - tile0) : -1;
   };
 
-  Stage<D, FMT> st;
-  int ba = -1, bb = -1;
-  if (nchunks > 0) {
-    chunk_blocks(0, &ba, &bb);
-    st.load(a, ba, bb, kc_head, vc_head, blk_stride, 0, kend);
-    st.store(lds);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < nchunks; ++j) {
-    const int t0 = j * kChunk;
-    _Float16* buf = lds + (j & 1) * S::BUF;
-    int nba = -1, nbb = -1;
-    if (j + 1 < nchunks) {
-      chunk_blocks(t0 + kChunk, &nba, &nbb);
-      st.load(a, nba, nbb, kc_head, vc_head, blk_stride, t0 + kChunk, kend);
-    }
+  // The arithmetic of the chunk at token t0, whose tiles lie in blocks ba and
+  // bb, from the chunk buffer buf laid out as Lay: S = K Q^T, the online
+  // softmax, O^T += V^T P^T.
+  auto compute_chunk = [&](const _Float16* buf, int t0, int ba, int bb, auto lay) {
+    using Lay = decltype(lay);
     // tokens of a block outside the pool are skipped
     const bool ok_a = (unsigned)ba < (unsigned)a.num_blocks;
     const bool ok_b = (unsigned)bb < (unsigned)a.num_blocks;
@@ -371,10 +447,10 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
       for (int cg = 0; cg < kNcg; ++cg) s[tt][cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const _Float16* krow = buf + (16 * tt + col) * S::KS + grp * DQ;
+      const int kr = 16 * tt + col;
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
-        const f16x8 ka = *reinterpret_cast<const f16x8*>(krow + 8 * m);
+        const f16x8 ka = *reinterpret_cast<const f16x8*>(buf + Lay::k(kr, grp * (DQ / 8) + m));
 #pragma unroll
         for (int cg = 0; cg < kNcg; ++cg)
           s[tt][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[cg][m], s[tt][cg], 0, 0, 0);
@@ -442,11 +518,11 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
     }
 
     // O^T += V^T . P^T, one 16-row head-dim tile at a time
-    const _Float16* vbuf = buf + kChunk * S::KS;
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-      const _Float16* p1 = vbuf + tr_row * S::VS + 16 * c + tr_col;
-      const _Float16* p2 = vbuf + (16 + tr_row) * S::VS + 16 * c + tr_col;
+      const int pc = 2 * c + (tr_col >> 3);  // the 16-byte piece holding elements 16c + tr_col ..
+      const _Float16* p1 = buf + Lay::v(tr_row, pc, tr_col & 7);
+      const _Float16* p2 = buf + Lay::v(16 + tr_row, pc, tr_col & 7);
       const f16x4 r1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1)));
       const f16x4 r2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2)));
       const f16x8 va = __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -454,11 +530,72 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
       for (int cg = 0; cg < kNcg; ++cg)
         o[cg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[cg], o[cg][c], 0, 0, 0);
     }
+  };
 
-    if (j + 1 < nchunks) st.store(lds + ((j + 1) & 1) * S::BUF);
+  if constexpr (DIRECT) {
+    // chunk j + 1 lands in one buffer while chunk j is computed from the other;
+    // each wave waits for its own loads, then the barrier makes all of them
+    // visible (and ends every read of the buffer the next loads overwrite)
+    using DS = Direct<D>;
+    const uint32_t loff = DS::lane_off(lane);
+    auto zero_if_needed = [&](_Float16* buf, int t0, int ba, int bb) {
+      const bool oka = (unsigned)ba < (unsigned)a.num_blocks;
+      const bool okb = (unsigned)bb < (unsigned)a.num_blocks;
+      if (!(oka && okb && t0 + kChunk - 1 < kend)) {  // uniform over the workgroup
+        DS::zero_invalid(buf, t0, kend, oka, okb);
+        __syncthreads();
+      }
+    };
+    int ba = -1, bb = -1;
+    if (nchunks > 0) {
+      chunk_blocks(0, &ba, &bb);
+      DS::issue(a, ba, bb, kc_head, vc_head, blk_stride, 0, dbuf0, wave, lane, loff);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    ba = nba;
-    bb = nbb;
+    if (nchunks > 0) zero_if_needed(dbuf0, 0, ba, bb);
+    auto step = [&](int j, _Float16* cur, _Float16* nxt) {
+      const int t0 = j * kChunk;
+      int nba = -1, nbb = -1;
+      if (j + 1 < nchunks) {
+        chunk_blocks(t0 + kChunk, &nba, &nbb);
+        DS::issue(a, nba, nbb, kc_head, vc_head, blk_stride, t0 + kChunk, nxt, wave, lane, loff);
+      }
+      compute_chunk(cur, t0, ba, bb, PairLayout<D>{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 1 < nchunks) zero_if_needed(nxt, t0 + kChunk, nba, nbb);
+      ba = nba;
+      bb = nbb;
+    };
+    for (int j = 0; j < nchunks; j += 2) {
+      step(j, dbuf0, dbuf1);
+      if (j + 1 < nchunks) step(j + 1, dbuf1, dbuf0);
+    }
+  } else {
+    Stage<D, FMT> st;
+    int ba = -1, bb = -1;
+    if (nchunks > 0) {
+      chunk_blocks(0, &ba, &bb);
+      st.load(a, ba, bb, kc_head, vc_head, blk_stride, 0, kend);
+      st.store(lds);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < nchunks; ++j) {
+      const int t0 = j * kChunk;
+      int nba = -1, nbb = -1;
+      if (j + 1 < nchunks) {
+        chunk_blocks(t0 + kChunk, &nba, &nbb);
+        st.load(a, nba, nbb, kc_head, vc_head, blk_stride, t0 + kChunk, kend);
+      }
+      compute_chunk(lds + (j & 1) * S::BUF, t0, ba, bb, PaddedLayout<D, FP8>{});
+
+      if (j + 1 < nchunks) st.store(lds + ((j + 1) & 1) * S::BUF);
+      __syncthreads();
+      ba = nba;
+      bb = nbb;
+    }
   }
 
   const float v_scale = uniform_f32(a.v_scale_h ? a.v_scale_h[head] : a.v_out_scale);

@@ -116,3 +116,49 @@ def test_one_row_chunks_agree_with_decode():
     ref = np.concatenate([o.rows[i] for i in range(len(L))])
     assert_close_to_oracle(pre.cpu().numpy(), ref, "f16", "prefill")
     assert_close_to_oracle(dec.cpu().numpy(), ref, "f16", "decode")
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,kv", [(16, 8, 128, 16, "f16"), (8, 8, 64, 32, "f16"),
+                                           (16, 8, 128, 16, "fp8")])
+def test_out_of_range_block_ids_are_skipped(hq, hkv, d, bs, kv):
+    """Table entries outside the pool are never followed: their tokens are left
+    out of every row's attention (the rows at those positions still attend to
+    the other tokens they see). Caches and tables are built on the host; unused
+    slots are NaN."""
+    from oracle import attention as oattn
+    from oracle import fp8 as ofp8
+    from paged_kv_cache_60_amd import ops
+    g = np.random.default_rng(hq + d + bs)
+    L = 7 * bs - 5
+    nblk = -(-L // bs)
+    nb = nblk + 2
+    table = list(range(1, nblk + 1))
+    table[1], table[3] = 999, -5  # two tiles outside the pool
+    if kv == "f16":
+        kc = g.standard_normal((nb, hkv, bs, d), dtype=np.float32).astype(np.float16)
+        vc = g.standard_normal((nb, hkv, bs, d), dtype=np.float32).astype(np.float16)
+        kc[0], vc[0] = np.nan, np.nan  # the block invalid tiles are read from, masked
+    else:
+        kc = ofp8.quantize(g.standard_normal((nb, hkv, bs, d)).astype(np.float32), 1.0)
+        vc = ofp8.quantize(g.standard_normal((nb, hkv, bs, d)).astype(np.float32), 1.0)
+        kc[0], vc[0] = 0x7F, 0x7F
+    n = L  # every position is a query row
+    q = g.standard_normal((n, hq, d), dtype=np.float32).astype(np.float16)
+    sm = d ** -0.5
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")  # noqa: E731
+    out = torch.full((n, hq, d), 3.0, dtype=torch.float16, device="cuda")
+    ops.paged_attn_prefill(out, dev(q), dev(kc), dev(vc), dev(np.asarray([table], dtype=np.int32)),
+                           dev(np.asarray([L], dtype=np.int32)), dev(np.asarray([0, n], dtype=np.int32)), sm, kv)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    # reference: row at position p attends to the valid tokens 0..p
+    valid = [t for t in range(L) if 0 <= table[t // bs] < nb]
+    dec = (lambda x: x.astype(np.float64)) if kv == "f16" else (lambda x: ofp8.decode_table("e4m3")[x])
+    K = np.stack([dec(kc[table[t // bs], :, t % bs, :]) for t in valid])  # [n_valid, Hkv, D]
+    V = np.stack([dec(vc[table[t // bs], :, t % bs, :]) for t in valid])
+    ref = np.zeros((n, hq, d))
+    for p in range(n):
+        m = int(np.searchsorted(valid, p, side="right"))
+        for h in range(hq):
+            ref[p, h] = oattn.attend_one(q[p, h], K[:m, h // (hq // hkv)], V[:m, h // (hq // hkv)], sm)
+    assert_close_to_oracle(got, ref, kv, "prefill with skipped tiles")
