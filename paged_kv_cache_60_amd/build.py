@@ -31,10 +31,12 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# per-source extra flags: the prefill kernel keeps its matrix-core accumulators
-# in ordinary VGPRs (the accumulator-register form made the compiler copy all 64
-# output accumulators out and back on every iteration of the token loop)
-HIP_EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the matrix-core kernels (prefill, grouped-head decode)
+# keep their accumulators in ordinary VGPRs; in the accumulator-register form the
+# compiler copied every output accumulator out and back on each iteration of
+# the token loop (64 per step in prefill, 32 per unit in decode)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+HIP_EXTRA = {"attn_prefill.hip": VGPR_FORM, "attn_decode.hip": VGPR_FORM}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 

@@ -142,26 +142,25 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         const int blk_b = __builtin_amdgcn_readlane(my_blk, 2 * j + 1);
         const bool ok_a = (unsigned)blk_a < (unsigned)a.num_blocks;
         const bool ok_b = (unsigned)blk_b < (unsigned)a.num_blocks;
-        const size_t off_a = (size_t)blk_a * blk_stride + (size_t)(ta & bs_mask) * RB;
-        const size_t off_b = (size_t)blk_b * blk_stride + (size_t)((ta + 16) & bs_mask) * RB;
+        // a tile outside the pool reads block 0 and is masked below; a unit
+        // with both tiles in the pool and all 32 tokens inside the sequence
+        // (every unit but a sequence's last) skips the masking altogether
+        const size_t off_a = ok_a ? (size_t)blk_a * blk_stride + (size_t)(ta & bs_mask) * RB : 0;
+        const size_t off_b = ok_b ? (size_t)blk_b * blk_stride + (size_t)((ta + 16) & bs_mask) * RB : 0;
+        const bool full = ok_a && ok_b && ta + 32 <= L;
 
         // K rows (A operand of S) and V rows (to LDS)
         u32x4 ka[KLD], kb[KLD], vv[VLD];
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-          ka[i] = ok_a ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i))
-                       : u32x4{0u, 0u, 0u, 0u};
-          kb[i] = ok_b ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i))
-                       : u32x4{0u, 0u, 0u, 0u};
+          ka[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i));
+          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i));
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-          const bool in_b = i * RPL >= 16;
-          const bool ok = in_b ? ok_b : ok_a;
-          const size_t off = in_b ? off_b : off_a;
+          const size_t off = i * RPL >= 16 ? off_b : off_a;
           const int r = (i * RPL + v_row) & 15;
-          vv[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc_head + off + r * RB + v_cb))
-                     : u32x4{0u, 0u, 0u, 0u};
+          vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc_head + off + r * RB + v_cb));
         }
 
         // S = K . Q^T for both tiles
@@ -185,10 +184,22 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         float z[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int tka = ta + 4 * grp + v;
-          const int tkb = ta + 16 + 4 * grp + v;
-          z[v] = (ok_a && tka < L) ? sa[v] * qk_scale : -INFINITY;
-          z[4 + v] = (ok_b && tkb < L) ? sb[v] * qk_scale : -INFINITY;
+          z[v] = sa[v] * qk_scale;
+          z[4 + v] = sb[v] * qk_scale;
+        }
+        if (!full) {
+          // rows past the end of the sequence (possibly not finite in the
+          // pool) and tiles outside the pool: no logit, zero V rows
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (!(ok_a && ta + 4 * grp + v < L)) z[v] = -INFINITY;
+            if (!(ok_b && ta + 16 + 4 * grp + v < L)) z[4 + v] = -INFINITY;
+          }
+#pragma unroll
+          for (int i = 0; i < VLD; ++i) {
+            const int r = i * RPL + v_row;  // 0..31
+            if (!((r < 16 ? ok_a : ok_b) && ta + r < L)) vv[i] = u32x4{0u, 0u, 0u, 0u};
+          }
         }
         // the running max (log2 units) moves only when some lane's logits exceed
         // it by more than kLazy: between moves the accumulators are not
@@ -217,19 +228,16 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         }
         l_part += ps;
 
-        // V rows -> LDS as fp16 (rows past the end as zeros)
+        // V rows -> LDS as fp16 (masked rows are zero bytes, which widen to +0)
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
           const int r = i * RPL + v_row;  // 0..31
-          const bool ok = (r < 16 ? ok_a : ok_b) && (ta + r < L);
           _Float16* dst = vbuf + r * VS + v_cb / ELEM;
           if constexpr (FP8) {
-            const f16x8 lo = ok ? fp8x8_to_f16x8<FMT>(vv[i][0], vv[i][1]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            const f16x8 hi = ok ? fp8x8_to_f16x8<FMT>(vv[i][2], vv[i][3]) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            *reinterpret_cast<f16x8*>(dst) = lo;
-            *reinterpret_cast<f16x8*>(dst + 8) = hi;
+            *reinterpret_cast<f16x8*>(dst) = fp8x8_to_f16x8<FMT>(vv[i][0], vv[i][1]);
+            *reinterpret_cast<f16x8*>(dst + 8) = fp8x8_to_f16x8<FMT>(vv[i][2], vv[i][3]);
           } else {
-            *reinterpret_cast<u32x4*>(dst) = ok ? vv[i] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(dst) = vv[i];
           }
         }
 
