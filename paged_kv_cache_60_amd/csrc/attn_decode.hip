@@ -532,12 +532,42 @@ __device__ __forceinline__ void fold(Row<DL>& r, float m, float l, const float* 
   r.M = Mn;
 }
 
+// Adds to acc (the lane's DL elements) the weighted output rows of nk <= 64
+// pieces: lane j holds piece j's weight (0: no piece, nothing is added) and
+// the start of its row (any readable address when the weight is 0). The rows
+// are loaded eight pieces at a time so that their latencies overlap; the sum
+// runs in piece order.
+template <int DL>
+__device__ __forceinline__ void sum_rows(float* acc, float wgt, const float* row, int nk) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t rp = reinterpret_cast<uint64_t>(row);
+  for (int j0 = 0; j0 < nk; j0 += 8) {
+    float w[8], v[8][DL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, nk - 1);  // past nk: the last piece again, weight 0
+      w[u] = j0 + u < nk ? readlane_f32(wgt, j) : 0.0f;
+      const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rp >> 32), j) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, j);
+      const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) v[u][e] = oj[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (w[u] == 0.0f) continue;  // no piece, or a weight that underflowed
+#pragma unroll
+      for (int e = 0; e < DL; ++e) acc[e] = fmaf(w[u], v[u][e], acc[e]);
+    }
+  }
+}
+
 // Folds into r the pieces of the segment holding units [s0, s1) of a unit
 // space of `total` units cut into W shares. The piece of worker w sits in
 // slot 0 if it starts the worker's share, else in slot 1; a slot holds `cols`
 // columns of D + 2 floats (o in ws_o, (max, sum) in ws_ml) and the row is
-// column `col`. Lane k holds the weight of piece k (64 pieces at a time); each
-// lane owns D/64 output elements.
+// column `col`. Pieces are taken 64 at a time (lane k: piece k of the batch),
+// each batch folded into r; each lane owns D/64 output elements.
 template <int D>
 __device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_ml, int cols, int col,
                             int64_t s0, int64_t s1, int64_t total, int64_t W) {
@@ -548,46 +578,28 @@ __device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_m
   const int64_t wa = ((s0 + 1) * W - 1) / total;
   const int64_t wb = (s1 * W - 1) / total;
   const int np = (int)(wb - wa + 1);
-  float M = -INFINITY;
-  for (int k = lane; k < np; k += 64) {
-    const int64_t wk = wa + k;
-    const int64_t st = share_start(wk, total, W);
-    if (share_start(wk + 1, total, W) == st) continue;  // empty share
-    const int slot = st >= s0 ? 0 : 1;
-    M = fmaxf(M, ws_ml[2 * ((wk * 2 + slot) * cols + col)]);
-  }
-  M = wave_max(M);
-  const float Ms = safe_max(M);
-  float lsum = 0.0f;
-  float acc[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
   for (int k0 = 0; k0 < np; k0 += 64) {
-    float wgt = 0.0f;
-    int slot_k = 0;
     const int k = k0 + lane;
+    float m = -INFINITY, l = 0.0f;
+    const float* row = ws_o;
     if (k < np) {
       const int64_t wk = wa + k;
       const int64_t st = share_start(wk, total, W);
-      if (share_start(wk + 1, total, W) != st) {
-        slot_k = st >= s0 ? 0 : 1;
-        const int64_t pi = (wk * 2 + slot_k) * cols + col;
-        wgt = fast_exp2(ws_ml[2 * pi] - Ms);
-        lsum += ws_ml[2 * pi + 1] * wgt;
+      if (share_start(wk + 1, total, W) != st) {  // else an empty share
+        const int64_t pi = (wk * 2 + (st >= s0 ? 0 : 1)) * cols + col;
+        m = ws_ml[2 * pi];
+        l = ws_ml[2 * pi + 1];
+        row = ws_o + pi * D;
       }
     }
-    const int nk = min(64, np - k0);
-    for (int j = 0; j < nk; ++j) {
-      const float wj = readlane_f32(wgt, j);
-      if (wj == 0.0f) continue;  // empty share, or a weight that underflowed
-      const int slot = __builtin_amdgcn_readlane(slot_k, j);
-      const int64_t pi = ((wa + k0 + j) * 2 + slot) * cols + col;
-      const float* o = ws_o + pi * D + lane * DL;
+    const float M = wave_max(m);
+    const float wgt = m == -INFINITY ? 0.0f : fast_exp2(m - safe_max(M));
+    float acc[DL];
 #pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] = fmaf(wj, o[e], acc[e]);
-    }
+    for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
+    sum_rows<DL>(acc, wgt, row, min(64, np - k0));
+    fold(r, M, wave_sum(l * wgt), acc);
   }
-  fold(r, M, wave_sum(lsum), acc);
 }
 
 // Writes r, normalised, to the lane's DL elements of an output row.
@@ -759,17 +771,7 @@ __global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
     float acc[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-    const uint64_t op = reinterpret_cast<uint64_t>(o);
-    const int nk = min(64, N - k0);
-    for (int j = 0; j < nk; ++j) {
-      const float wj = readlane_f32(wgt, j);
-      if (wj == 0.0f) continue;  // empty share, or a weight that underflowed
-      const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(op >> 32), j) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)op, j);
-      const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] = fmaf(wj, oj[e], acc[e]);
-    }
+    sum_rows<DL>(acc, wgt, have ? o : a.ws_o, min(64, N - k0));
     fold(r, M, lsum, acc);
   }
   write_row(r, out);

@@ -9,8 +9,10 @@
 // Operand layouts (16x16x32 f16): A[i][k] in lane i + 16g, B[k][j] in lane
 // j + 16g, both holding 8 k values chosen by (g, slot); C[i][j] in lane
 // j + 16(i/4), register i%4.
-//   - K rows need no transpose: lane (token t, group g) loads 16..64 contiguous
-//     bytes of row t, and the d index of each MFMA slot is chosen to match.
+//   - K rows need no transpose: lane (token t, group g) loads 16-byte chunks
+//     g, 4 + g, 8 + g, .. of row t, so the four lanes of a row read 64
+//     contiguous bytes per load instruction; the d index of each MFMA slot
+//     (and of the query's B operand) is chosen to match (k_dim_of).
 //   - S's accumulator gives lane (head h, group g) the logits of tokens
 //     4g..4g+3 of a tile; two tiles give exactly the 8 token slots that P^T
 //     needs as the B operand of the P.V product, so P never moves between lanes.
@@ -46,6 +48,16 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   r[2] = fp8x2_to_f16x2<FMT>(w1, false);
   r[3] = fp8x2_to_f16x2<FMT>(w1, true);
   return __builtin_bit_cast(f16x8, r);
+}
+
+// First d index of the 8 that lane group g supplies to the q.k MFMA m, when
+// the lane holds 16-byte chunks g, 4 + g, .. of its K row (each chunk feeds one
+// fp16 MFMA or two fp8 MFMAs)
+template <int ELEM>
+__device__ __forceinline__ int k_dim_of(int m, int g) {
+  constexpr int EPC = 16 / ELEM;  // elements per chunk
+  constexpr int MPC = EPC / 8;    // MFMAs per chunk
+  return (4 * (m / MPC) + g) * EPC + 8 * (m % MPC);
 }
 
 template <int D, int G, int FMT, int NW>
@@ -87,7 +99,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   const size_t blk_stride = (size_t)a.Hkv * head_bytes;
   const int bs_mask = (1 << a.bs_log2) - 1;
   _Float16* vbuf = vlds + wave * 32 * VS;
-  const uint32_t k_lane_off = (uint32_t)(col * RB + grp * DQ * ELEM);
+  const uint32_t k_lane_off = (uint32_t)(col * RB + grp * 16);  // + 64 per chunk
   const int v_row = lane / LPR;        // row within a V load
   const int v_cb = (lane % LPR) * 16;  // byte offset within the row
   // tr16 read addresses: lane 16g + 4e + mm names row 4g + e (tile a) or
@@ -106,12 +118,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const float qk_scale = head_qk_scale(a, pc.head);
     const float v_scale = head_v_scale(a, pc.head);
 
-    // Q^T as the B operand: head = col (zero past G), d = grp * DQ + 8m + slot
+    // Q^T as the B operand: head = col (zero past G), d = k_dim_of(m, grp) + slot
     f16x8 qb[KM];
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
       if (col < G) {
-        const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + col) * D + grp * DQ + 8 * m;
+        const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + col) * D + k_dim_of<ELEM>(m, grp);
         qb[m] = *reinterpret_cast<const f16x8*>(qrow);
       } else {
         qb[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -153,8 +165,8 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
         u32x4 ka[KLD], kb[KLD], vv[VLD];
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-          ka[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i));
-          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i));
+          ka[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 64 * i));
+          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 64 * i));
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {

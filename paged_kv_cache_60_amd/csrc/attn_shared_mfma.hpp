@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(NW * 64, FMT == kF16 ? 1 : 2) attn_shared_mfma
   const size_t blk_stride = (size_t)a.Hkv * head_bytes;
   const int bs_mask = (1 << a.bs_log2) - 1;
   _Float16* vbuf = vlds + wave * 32 * VS;
-  const uint32_t k_lane_off = (uint32_t)(col * RB + grp * DQ * ELEM);
+  const uint32_t k_lane_off = (uint32_t)(col * RB + grp * 16);  // + 64 per chunk
   const int v_row = lane / LPR;
   const int v_cb = (lane % LPR) * 16;
   const int tr_row = 4 * grp + (col >> 2);
@@ -127,9 +127,9 @@ __global__ void __launch_bounds__(NW * 64, FMT == kF16 ? 1 : 2) attn_shared_mfma
       for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (m < nm) {
         Lc[cb] = min(pre, seq_len(a, lead + m));
-        const f16* qrow = a.q + ((size_t)(lead + m) * a.Hq + (head << gl) + gh) * D + grp * DQ;
+        const f16* qrow = a.q + ((size_t)(lead + m) * a.Hq + (head << gl) + gh) * D;
 #pragma unroll
-        for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = *reinterpret_cast<const f16x8*>(qrow + 8 * mm);
+        for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = *reinterpret_cast<const f16x8*>(qrow + k_dim_of<ELEM>(mm, grp));
       }
     }
 
@@ -176,8 +176,8 @@ __global__ void __launch_bounds__(NW * 64, FMT == kF16 ? 1 : 2) attn_shared_mfma
                                  ? (size_t)blk_b * blk_stride + (size_t)((ta + 16) & bs_mask) * RB : 0;
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-          d.ka[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 16 * i));
-          d.kb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 16 * i));
+          d.ka[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_a + k_lane_off + 64 * i));
+          d.kb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc_head + off_b + k_lane_off + 64 * i));
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
