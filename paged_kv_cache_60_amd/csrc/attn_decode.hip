@@ -715,12 +715,17 @@ __global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
   const int hq = wid - seq * a.Hq;
   const int kvh = hq / G;
   const int g = hq - kvh * G;
-  // written by pass 1 only when there are groups
-  const int gid = a.NG ? a.ws_gid[seq] : -1;
-  const int grp = gid >= 0 && gid < a.NG ? gid : -1;
+  // the index loads are issued together, unconditionally (the workspace
+  // always holds these arrays): the group map (written by pass 1 only when
+  // there are groups), pass 1's unit prefix and the shared pass's
+  const int gid_ws = a.ws_gid[seq];
   const int p0 = a.ws_pt[seq];
-  const int n_u = a.ws_pt[seq + 1] - p0;
+  const int p1 = a.ws_pt[seq + 1];
   const int P = a.ws_pt[a.B];
+  const int PS = a.ws_spt[a.NG];
+  const int gid = a.NG ? gid_ws : -1;
+  const int grp = gid >= 0 && gid < a.NG ? gid : -1;
+  const int n_u = p1 - p0;
   f16* out = a.out + (size_t)wid * D + lane * DL;
 
   const int64_t totalP = (int64_t)a.Hkv * P;
@@ -739,13 +744,14 @@ __global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
     sp = seg_pieces(s0P, s0P + n_u, totalP, a.workers, a.ws_o, a.ws_ml, G, g, a.ws_wo, a.ws_wml, wid, D);
   SegPieces ss;
   {
+    const int first = a.grp_first[grp];
+    const int spt = a.ws_spt[grp];
     const int ug = group_units(a, grp);
-    const int m = seq - a.grp_first[grp];
+    const int m = seq - first;
     if (ug > 0 && m >= 0) {
       const int part = m / MP;
       const int c = (m - part * MP) * G + g;
-      const int PS = a.ws_spt[a.NG];
-      const int64_t s0 = (int64_t)kvh * PS + a.ws_spt[grp] + (int64_t)part * ug;
+      const int64_t s0 = (int64_t)kvh * PS + spt + (int64_t)part * ug;
       ss = seg_pieces(s0, s0 + ug, (int64_t)a.Hkv * PS, a.s_workers, a.ws_so, a.ws_sml, kSharedCols, c, a.ws_swo,
                       a.ws_swml, wid, D);
     }
