@@ -374,7 +374,15 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const float qk_scale = uniform_f32(a.k_scale_h ? a.qk_base * a.k_scale_h[head] : a.qk_scale);
+  // The softmax below takes the running max of the raw logits before scaling
+  // them and masks a logit by setting it to -inf, which needs a scale > 0. A
+  // negative scale is moved into the sign of the query operands (exact), and
+  // a zero one becomes the smallest normal float: every visible p is then
+  // exactly 1, as with scale 0, and a masked one still 0.
+  const float qk_signed = uniform_f32(a.k_scale_h ? a.qk_base * a.k_scale_h[head] : a.qk_scale);
+  const bool q_neg = qk_signed < 0.0f;
+  const float qk_mag = q_neg ? -qk_signed : qk_signed;
+  const float qk_scale = qk_mag == 0.0f ? __FLT_MIN__ : qk_mag;
 
   // Q^T operands (B of S = K Q^T): column c = 32 wave + 16 cg + col holds query
   // token c / G, head c % G of the group; d = grp * DQ + 8 m + slot
@@ -388,8 +396,10 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
     qpos[cg] = live ? pos0 + tl : -1;  // -1: every token is masked
     const size_t qoff = live ? ((size_t)(qfirst + row0 + tl) * a.Hq + head * G + c % G) * D + grp * DQ : 0;
 #pragma unroll
-    for (int m = 0; m < KM; ++m)
+    for (int m = 0; m < KM; ++m) {
       qb[cg][m] = live ? *reinterpret_cast<const f16x8*>(a.q + qoff + 8 * m) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (q_neg) qb[cg][m] = -qb[cg][m];
+    }
   }
   const bool all_live = nt == QT;
 

@@ -82,6 +82,22 @@ def test_constant_v_and_identical_keys():
     np.testing.assert_allclose(attention.attend_one(q, K2, V2, 0.3), V2.mean(0), rtol=1e-13, atol=1e-13)
 
 
+def test_zero_and_negative_scales():
+    """Scale 0: every visible token weighs the same (the mean of V). A negative
+    scale is the positive one applied to -q. Both against a direct evaluation
+    of the softmax by an independent route (scipy's logsumexp)."""
+    from scipy.special import logsumexp
+    g = np.random.default_rng(11)
+    L, d = 53, 32
+    q, K, V = g.standard_normal(d), g.standard_normal((L, d)), g.standard_normal((L, d))
+    np.testing.assert_allclose(attention.attend_one(q, K, V, 0.0), V.mean(0), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(attention.attend_one(q, K, V, -0.4), attention.attend_one(-q, K, V, 0.4),
+                               rtol=1e-13, atol=1e-13)
+    z = -0.4 * (K @ q)
+    w = np.exp(z - logsumexp(z))
+    np.testing.assert_allclose(attention.attend_one(q, K, V, -0.4), w @ V, rtol=1e-12, atol=1e-12)
+
+
 def test_zero_length_is_zero():
     assert np.array_equal(attention.attend_one(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)), 1.0),
                           np.zeros(4))
