@@ -400,6 +400,100 @@ def bench_swap(args):
     print(json.dumps(result), flush=True)
 
 
+SCATTER_METRIC = "paged_kv_write / paged_block_copy: achieved HBM GB/s (bytes read + written)"
+SCATTER_SOURCES = ("kv_write.hip", "block_copy.hip", "device_common.hpp")
+
+
+def bench_scatter(args):
+    """paged_kv_write and paged_block_copy at sizes where HBM, not latency, is
+    the bound: a prefill-sized scatter of 65 536 tokens into shuffled slots of a
+    Llama-2-7B-shaped layer (fp16 copy) and of the beam workload's layer (e4m3
+    encode, one scale per tensor), and 2048 copy-on-write pairs of
+    Llama-2-7B-shaped blocks. Each is timed by events around every launch
+    (median of --steps). value = the fp16 scatter's GB/s."""
+    import torch
+
+    from paged_kv_cache_60_amd import ops
+    g = torch.Generator(device="cpu").manual_seed(60)
+    gd = torch.Generator(device="cuda").manual_seed(60)
+
+    def scatter_case(hkv, d, bs, kv, T):
+        nb = (T * 11 // 10 + bs - 1) // bs
+        slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64).cuda()
+        k = torch.randn((T, hkv, d), generator=gd, dtype=torch.float16, device="cuda")
+        v = torch.randn((T, hkv, d), generator=gd, dtype=torch.float16, device="cuda")
+        cdt = torch.float16 if kv == "f16" else torch.uint8
+        kc = torch.zeros((nb, hkv, bs, d), dtype=cdt, device="cuda")
+        vc = torch.zeros_like(kc)
+        e = 2 if kv == "f16" else 1
+        nbytes = 2 * T * hkv * d * 2 + 2 * T * hkv * d * e + T * 8
+        inv = 1.0 if kv == "f16" else 448.0 / 4.5
+        run = lambda: ops.paged_kv_write(k, v, kc, vc, slots, kv, inv, inv)  # noqa: E731
+        return run, nbytes, {"tokens": T, "kv_heads": hkv, "head_dim": d, "block_size": bs, "kv_dtype": kv}
+
+    def copy_case(hkv, d, bs, n):
+        nb = 2 * n + 16
+        perm = torch.randperm(nb, generator=g)
+        pairs = torch.stack([perm[:n], perm[n:2 * n]], 1).to(torch.int32).contiguous().cuda()
+        kc = torch.randn((nb, hkv, bs, d), generator=gd, dtype=torch.float16, device="cuda")
+        vc = torch.randn((nb, hkv, bs, d), generator=gd, dtype=torch.float16, device="cuda")
+        nbytes = 2 * 2 * n * hkv * bs * d * 2 + n * 8
+        run = lambda: ops.paged_block_copy(kc, vc, pairs)  # noqa: E731
+        return run, nbytes, {"pairs": n, "kv_heads": hkv, "head_dim": d, "block_size": bs, "kv_dtype": "f16"}
+
+    cases = {"write_f16_llama2_7b": scatter_case(32, 128, 16, "f16", 65536),
+             "write_e4m3_beam": scatter_case(8, 128, 64, "fp8", 65536),
+             "copy_f16_llama2_7b": copy_case(32, 128, 16, 2048)}
+    res = {}
+    for name, (run, nbytes, shape) in cases.items():
+        log(f"bench: scatter {name}")
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        t = float(np.median(ts))
+        res[name] = {**shape, "bytes": nbytes, "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 2),
+                     "us_p10_p50_p90": [round(float(x) * 1e6, 2) for x in np.percentile(ts, [10, 50, 90])]}
+    main_case = res["write_f16_llama2_7b"]
+    result = {
+        "metric": SCATTER_METRIC,
+        "value": main_case["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_case["us"] / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "scatter_llama2_7b_65536_tokens", **{k: v for k, v in main_case.items()
+                                                                     if k in ("tokens", "kv_heads", "head_dim",
+                                                                              "block_size", "kv_dtype")},
+                   "timing": "events around every launch, median"},
+        "cases": res,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": main_case["gbs"],
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(main_case["gbs"] / PEAK_GBS, 4),
+            "traffic": load_counters("scatter_llama2_7b_65536_tokens", SCATTER_SOURCES),
+            "kernel": "kv_write_kernel",
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +514,8 @@ def main():
                          "llama2: last-512-token chunks, batch 64)")
     ap.add_argument("--swap", action="store_true",
                     help="time paged_block_swap (preemption by swapping, 16 sequences of the Llama-2-7B batch)")
+    ap.add_argument("--scatter", action="store_true",
+                    help="time paged_kv_write (fp16 and e4m3, 65 536 tokens) and paged_block_copy (2048 pairs)")
     ap.add_argument("--shared", action="store_true",
                     help="attend with paged_attn_decode_shared: runs of the batch that share leading blocks "
                          "(beams of one prompt, a common prefix) read them once")
@@ -453,6 +549,9 @@ def main():
         return
     if args.swap:
         bench_swap(args)
+        return
+    if args.scatter:
+        bench_scatter(args)
         return
 
     total_steps = args.warmup + args.steps

@@ -21,49 +21,33 @@
 namespace pkv {
 namespace {
 
-// e4m3fn byte for a float: round to nearest even, saturate to +-448, keep the
-// sign of zero, NaN -> 0x7F. All steps are exact except the final rint, which
-// is the rounding itself.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  const uint32_t sign = (u >> 24) & 0x80u;
+// fp8 byte for a float, without branches: round to nearest even, saturate
+// (an infinite input too), keep the sign of zero, NaN -> 0x7F. In the normal
+// range the float's mantissa is rounded to M bits on its bit pattern (adding
+// half an ulp of the kept part, less one, plus the lowest kept bit carries
+// into the exponent exactly when the rounded value reaches the next binade);
+// below the smallest normal 2^(1-BIAS) the value is a multiple of the
+// subnormal step 2^(1-BIAS-M), and rint of the exact scaled value rounds it.
+template <int M, int BIAS>
+__device__ __forceinline__ uint32_t fp8_rne_sat(float f, float max_finite, uint32_t max_code) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, f) >> 24) & 0x80u;
   const float a = __builtin_fabsf(f);
-  if (!(a == a)) return 0x7Fu;
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal grid of 2^-9
-    const float q = __builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal, code 0x08
-    return sign | (uint32_t)q;
-  }
-  int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;  // -6..8
-  float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));                 // 8..16
-  if (q == 16.0f) {
-    q = 8.0f;
-    e += 1;
-  }
-  return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)q - 8u);
+  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+  constexpr int DROP = 23 - M;  // fp32 mantissa bits dropped
+  const uint32_t r = ua + ((1u << (DROP - 1)) - 1u) + ((ua >> DROP) & 1u);
+  const uint32_t normal = (((r >> 23) - (uint32_t)(127 - BIAS)) << M) | ((r >> DROP) & ((1u << M) - 1u));
+  const float min_normal = __builtin_ldexpf(1.0f, 1 - BIAS);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * __builtin_ldexpf(1.0f, BIAS - 1 + M));
+  uint32_t code = a < min_normal ? sub : normal;
+  code = a >= max_finite ? max_code : code;
+  return a == a ? (sign | code) : 0x7Fu;
 }
 
-// e5m2 byte for a float: round to nearest even, saturate to +-57344 (an
-// infinite input too), keep the sign of zero, NaN -> 0x7F. Exponent bias 15,
-// 2 mantissa bits, subnormals on a grid of 2^-16 below 2^-14.
-__device__ __forceinline__ uint32_t e5m2_rne_sat(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(f);
-  if (!(a == a)) return 0x7Fu;
-  if (a >= 57344.0f) return sign | 0x7Bu;
-  if (a < 6.103515625e-05f) {  // below 2^-14
-    const float q = __builtin_rintf(a * 65536.0f);  // 0..4; 4 is the smallest normal, code 0x04
-    return sign | (uint32_t)q;
-  }
-  int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;  // -14..15
-  float q = __builtin_rintf(__builtin_ldexpf(a, 2 - e));                 // 4..8
-  if (q == 8.0f) {
-    q = 4.0f;
-    e += 1;
-  }
-  return sign | ((uint32_t)(e + 15) << 2) | ((uint32_t)q - 4u);
-}
+// e4m3fn: bias 7, 3 mantissa bits, largest finite 448 (0x7E)
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) { return fp8_rne_sat<3, 7>(f, 448.0f, 0x7Eu); }
+
+// e5m2: bias 15, 2 mantissa bits, largest finite 57344 (0x7B)
+__device__ __forceinline__ uint32_t e5m2_rne_sat(float f) { return fp8_rne_sat<2, 15>(f, 57344.0f, 0x7Bu); }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t fp8_encode(float f) {
@@ -88,17 +72,20 @@ struct StepMeta {
 
 // k_inv_h / v_inv_h: one multiplier per KV head (device memory), or null to
 // use k_inv / v_inv for every head.
+// One grid row (blockIdx.y) per KV head; along x, the threads take the
+// head's 16-byte chunks (8 elements) token by token: chunk c of token t is
+// i = t * cpr + c with cpr = head_dim / 8 a power of two, so the index math is
+// shifts and masks (block_size is a power of two too).
 template <int FMT, bool META>
 __global__ void __launch_bounds__(256)
 kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
                 uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                const int64_t* __restrict__ slots, int64_t total_chunks, int chunks_per_token,
-                int chunks_per_row, int64_t num_slots, int bs, int64_t row_stride_blk,
-                int head_dim, float k_inv, float v_inv, const float* __restrict__ k_inv_h,
-                const float* __restrict__ v_inv_h, StepMeta meta) {
+                const int64_t* __restrict__ slots, int64_t num_tokens, int cpr_log2, int num_kv_heads,
+                int64_t num_slots, int bs_log2, float k_inv, float v_inv,
+                const float* __restrict__ k_inv_h, const float* __restrict__ v_inv_h, StepMeta meta) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if constexpr (META) {
+  if (META && blockIdx.y == 0) {
     for (int64_t i = gtid; i < meta.n_ctx; i += stride) meta.ctx_dst[i] = meta.ctx_src[i];
     for (int64_t k = gtid; k < meta.n_updates; k += stride) {
       const int row = meta.updates[3 * k];
@@ -107,19 +94,21 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
         meta.tables[(int64_t)row * meta.max_blocks + idx] = meta.updates[3 * k + 2];
     }
   }
-  for (int64_t i = gtid; i < total_chunks; i += stride) {
-    const int64_t t = i / chunks_per_token;
-    const int within = (int)(i - t * chunks_per_token);
-    const int h = within / chunks_per_row;
-    const int ch = within - h * chunks_per_row;
+  const int h = blockIdx.y;
+  const int cpr = 1 << cpr_log2;
+  const int64_t n = num_tokens << cpr_log2;  // this head's chunks
+  for (int64_t i = gtid; i < n; i += stride) {
+    const int64_t t = i >> cpr_log2;
+    const int ch = (int)i & (cpr - 1);
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / bs;
-    const int off = (int)(slot - blk * bs);
+    const int64_t blk = slot >> bs_log2;
+    const int off = (int)slot & ((1 << bs_log2) - 1);
+    const int64_t src = (t * num_kv_heads + h) * cpr + ch;  // chunk index in k_new / v_new
     // element index of the destination chunk
-    const int64_t dst = (blk * row_stride_blk + (int64_t)h * bs + off) * head_dim + (int64_t)ch * 8;
-    const u32x4 kv = k_new[i];
-    const u32x4 vv = v_new[i];
+    const int64_t dst = ((((blk * num_kv_heads + h) << bs_log2) + off) << (cpr_log2 + 3)) + (int64_t)ch * 8;
+    const u32x4 kv = k_new[src];
+    const u32x4 vv = v_new[src];
     if constexpr (FMT == kF16) {
       *reinterpret_cast<u32x4*>(k_cache + dst * 2) = kv;
       *reinterpret_cast<u32x4*>(v_cache + dst * 2) = vv;
@@ -164,15 +153,16 @@ int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v
   const int64_t meta_work = meta ? (meta->n_ctx > meta->n_updates ? meta->n_ctx : meta->n_updates) : 0;
   if (num_tokens == 0 && meta_work == 0) return PKV_OK;
   if (num_tokens > 0 && (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)) return PKV_ERR_INVALID;
-  const int chunks_per_row = head_dim / 8;
-  const int chunks_per_token = chunks_per_row * num_kv_heads;
-  const int64_t total = (int64_t)num_tokens * chunks_per_token;
+  if (num_kv_heads > 65535) return PKV_ERR_INVALID;  // one grid row per head
+  const int cpr_log2 = head_dim == 64 ? 3 : 4;      // log2(head_dim / 8)
+  const int bs_log2 = block_size == 16 ? 4 : (block_size == 32 ? 5 : 6);
+  const int64_t per_head = (int64_t)num_tokens << cpr_log2;
   const int64_t num_slots = (int64_t)num_blocks * block_size;
-  const int64_t row_stride_blk = (int64_t)num_kv_heads * block_size;
   const int threads = 256;
-  const int64_t work = total > meta_work ? total : meta_work;
+  const int64_t work = per_head > meta_work ? per_head : meta_work;
   int64_t blocks = (work + threads - 1) / threads;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t cap = 65536 / num_kv_heads > 0 ? 65536 / num_kv_heads : 1;  // ~64k workgroups in all
+  if (blocks > cap) blocks = cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* kn = static_cast<const u32x4*>(k_new);
   const auto* vn = static_cast<const u32x4*>(v_new);
@@ -189,9 +179,9 @@ int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v
     kern = meta ? kv_write_kernel<kE4M3, true> : kv_write_kernel<kE4M3, false>;
   else
     kern = meta ? kv_write_kernel<kE5M2, true> : kv_write_kernel<kE5M2, false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), 0, s, kn, vn, kc, vc, slot_mapping,
-                     total, chunks_per_token, chunks_per_row, num_slots, block_size, row_stride_blk,
-                     head_dim, ki, vi, fp8 ? k_inv_h : nullptr, fp8 ? v_inv_h : nullptr, m);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)num_kv_heads), dim3(threads), 0, s, kn, vn, kc, vc,
+                     slot_mapping, (int64_t)num_tokens, cpr_log2, num_kv_heads, num_slots, bs_log2, ki, vi,
+                     fp8 ? k_inv_h : nullptr, fp8 ? v_inv_h : nullptr, m);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
