@@ -397,7 +397,40 @@ def bench_swap(args):
             "kernel": "block_swap_kernel",
         },
     }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle block swap)")
+        result["cpu_baseline"] = swap_cpu_baseline(eng.block_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def swap_cpu_baseline(block_bytes, target_s=15.0, n=256):
+    """Oracle block swap (cache_ops.block_swap, whole blocks between two host
+    arrays standing for the device and host pools) of n blocks, out and in,
+    repeated until ~target_s."""
+    from oracle import cache_ops
+    elems = block_bytes // 2
+    g = np.random.default_rng(61)
+    dev_k = g.standard_normal((n, elems), dtype=np.float32).astype(np.float16)
+    dev_v = g.standard_normal((n, elems), dtype=np.float32).astype(np.float16)
+    host_k, host_v = np.zeros_like(dev_k), np.zeros_like(dev_v)
+    out_pairs = [(b, n - 1 - b) for b in range(n)]
+    in_pairs = [(h, b) for b, h in out_pairs]
+    rounds, elapsed = 0, 0.0
+    while elapsed < target_s and rounds < 10000:
+        t0 = time.perf_counter()
+        cache_ops.block_swap(dev_k, dev_v, host_k, host_v, out_pairs)
+        cache_ops.block_swap(host_k, host_v, dev_k, dev_v, in_pairs)
+        elapsed += time.perf_counter() - t0
+        rounds += 1
+    nbytes = 2 * 2 * n * block_bytes  # K and V, out and in
+    return {
+        "value": round(nbytes * rounds / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"cache_ops.block_swap of {n} blocks of {block_bytes} bytes (K and V), out and in, "
+                  f"{rounds} rounds, {elapsed:.1f} s on one host core (host arrays on both sides)",
+    }
 
 
 SCATTER_METRIC = "paged_kv_write / paged_block_copy: achieved HBM GB/s (bytes read + written)"
@@ -491,7 +524,43 @@ def bench_scatter(args):
             "kernel": "kv_write_kernel",
         },
     }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle scatter)")
+        result["cpu_baseline"] = scatter_cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def scatter_cpu_baseline(target_s=15.0, T=4096):
+    """Oracle scatter (cache_ops.scatter, token by token) of T tokens of the
+    Llama-2-7B layer shape into shuffled slots, repeated until ~target_s."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cache_ops
+    hkv, d, bs = 32, 128, 16
+    g = np.random.default_rng(60)
+    nb = (T * 11 // 10 + bs - 1) // bs
+    slots = g.permutation(nb * bs)[:T].astype(np.int64)
+    k = g.standard_normal((T, hkv, d), dtype=np.float32).astype(np.float16)
+    v = g.standard_normal((T, hkv, d), dtype=np.float32).astype(np.float16)
+    kc = np.zeros((nb, hkv, bs, d), dtype=np.float16)
+    vc = np.zeros_like(kc)
+    nbytes = 2 * T * hkv * d * 2 * 2 + T * 8
+    passes, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < target_s and passes < 1000:
+            t0 = time.perf_counter()
+            cache_ops.scatter(kc, vc, k, v, slots, bs)
+            elapsed += time.perf_counter() - t0
+            passes += 1
+    return {
+        "value": round(nbytes * passes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"cache_ops.scatter of {T} fp16 tokens (32 KV heads, head_dim 128, shuffled slots), "
+                  f"{passes} passes, {elapsed:.1f} s on one host core",
+        "tokens_per_s": round(T * passes / elapsed, 1),
+    }
 
 
 def main():
