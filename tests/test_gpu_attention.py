@@ -119,6 +119,19 @@ def test_small_shapes_all_outputs(hq, hkv, d, bs, kv):
         _check(wl, steps=1, partition_tokens=part, compare_caches=(part == 16))
 
 
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kv", ["f16", "fp8", "fp8_e5m2"])
+def test_matrix_core_path_every_variant(g, d, kv):
+    """Every instantiation of the matrix-core decode kernel (4 or 8 query heads
+    per KV head, head_dim 64 or 128, each KV format): ragged lengths around the
+    32-token unit and the block, at the default worker count."""
+    L = [1, 31, 32, 33, 95, 96, 97, 300]
+    wl = workloads.small_custom(seed=200 + g + d, lengths=L, num_q_heads=2 * g, num_kv_heads=2, head_dim=d,
+                                block_size=32, kv_dtype=kv, max_steps=1)
+    _check(wl, steps=1, compare_caches=False)
+
+
 def test_placement_invariance_bit_exact():
     """Same logical sequences, different physical placement: identical output bits."""
     wl1 = workloads.small_custom(seed=5, lengths=[100, 700, 33], num_q_heads=16, num_kv_heads=8,
