@@ -259,15 +259,20 @@ struct Direct {
   static constexpr int PPW = NP / kWaves;        // pairs per wave, per tensor
   static_assert(PPW >= 1 && NP % kWaves == 0, "chunk shape");
 
-  // halves offset of 16-byte chunk c of row r, plus e halves within the chunk
+  // halves offset of 16-byte chunk c of row r, plus e halves within the chunk.
+  // Rows 8-15 and 24-31 hold the two chunks of a pair swapped, so that the 16
+  // lanes of a K read (16 rows, one chunk each) fall on 16 different 16-byte
+  // bank groups instead of two rows per group.
   __device__ static __forceinline__ int at(int r, int c, int e) {
-    return (c >> 1) * PAIR_HALVES + r * 16 + (c & 1) * 8 + e;
+    return (c >> 1) * PAIR_HALVES + r * 16 + (((c & 1) ^ ((r >> 3) & 1)) * 8) + e;
   }
 
   // This lane's byte offset within its 16-token tile (the same for every pair,
-  // and every chunk of the token loop): row lane / 2 mod 16, chunk lane % 2.
+  // and every chunk of the token loop): row lane / 2 mod 16, and the chunk of
+  // the pair that at() places in LDS slot lane, i.e. lane % 2 swapped on rows
+  // 8-15 and 24-31 (lane / 16 odd).
   __device__ static __forceinline__ uint32_t lane_off(int lane) {
-    return (uint32_t)(((lane >> 1) & 15) * RB + (lane & 1) * 16);
+    return (uint32_t)(((lane >> 1) & 15) * RB + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
   }
 
   // K rows to buf[0, HALVES), V rows to buf[HALVES, 2 HALVES). Lanes 0-31 hold
