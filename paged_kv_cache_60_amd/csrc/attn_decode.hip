@@ -532,34 +532,53 @@ __device__ __forceinline__ void fold(Row<DL>& r, float m, float l, const float* 
   r.M = Mn;
 }
 
+// The lane's DL elements of the output rows of pieces j0 .. j0+7 of a batch
+// of nk <= 64 pieces, lane j holding the start of piece j's row (any readable
+// address for a piece that adds nothing); past nk, the last piece again.
+template <int DL>
+struct RowBatch {
+  float v[8][DL];
+};
+template <int DL>
+__device__ __forceinline__ RowBatch<DL> load_rows(const float* row, int j0, int nk) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t rp = reinterpret_cast<uint64_t>(row);
+  RowBatch<DL> b;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int j = min(j0 + u, nk - 1);
+    const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rp >> 32), j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, j);
+    const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) b.v[u][e] = oj[e];
+  }
+  return b;
+}
+
+// acc += the rows of b weighted by lane j's wgt for piece j0 + u, in piece
+// order (a weight of 0: no piece, or one that underflowed, adds nothing)
+template <int DL>
+__device__ __forceinline__ void add_rows(float* acc, float wgt, const RowBatch<DL>& b, int j0, int nk) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float w = j0 + u < nk ? readlane_f32(wgt, min(j0 + u, nk - 1)) : 0.0f;
+    if (w == 0.0f) continue;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) acc[e] = fmaf(w, b.v[u][e], acc[e]);
+  }
+}
+
 // Adds to acc (the lane's DL elements) the weighted output rows of nk <= 64
 // pieces: lane j holds piece j's weight (0: no piece, nothing is added) and
 // the start of its row (any readable address when the weight is 0). The rows
-// are loaded eight pieces at a time so that their latencies overlap; the sum
-// runs in piece order.
+// of the first eight pieces come in `first`, loaded by the caller before it
+// had the weights; the rest are loaded eight pieces at a time, so that their
+// latencies overlap. The sum runs in piece order.
 template <int DL>
-__device__ __forceinline__ void sum_rows(float* acc, float wgt, const float* row, int nk) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t rp = reinterpret_cast<uint64_t>(row);
-  for (int j0 = 0; j0 < nk; j0 += 8) {
-    float w[8], v[8][DL];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = min(j0 + u, nk - 1);  // past nk: the last piece again, weight 0
-      w[u] = j0 + u < nk ? readlane_f32(wgt, j) : 0.0f;
-      const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rp >> 32), j) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, j);
-      const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) v[u][e] = oj[e];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (w[u] == 0.0f) continue;  // no piece, or a weight that underflowed
-#pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] = fmaf(w[u], v[u][e], acc[e]);
-    }
-  }
+__device__ __forceinline__ void sum_rows(float* acc, float wgt, const float* row, int nk, const RowBatch<DL>& first) {
+  add_rows<DL>(acc, wgt, first, 0, nk);
+  for (int j0 = 8; j0 < nk; j0 += 8) add_rows<DL>(acc, wgt, load_rows<DL>(row, j0, nk), j0, nk);
 }
 
 // Folds into r the pieces of the segment holding units [s0, s1) of a unit
@@ -579,25 +598,28 @@ __device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_m
   const int64_t wb = (s1 * W - 1) / total;
   const int np = (int)(wb - wa + 1);
   for (int k0 = 0; k0 < np; k0 += 64) {
+    // every lane loads a slot of the buffers (past np, the last piece's), so
+    // that the loads are unconditional and the row loads below do not wait
+    // for them; lanes past np and empty shares then count as no piece
     const int k = k0 + lane;
-    float m = -INFINITY, l = 0.0f;
-    const float* row = ws_o;
-    if (k < np) {
-      const int64_t wk = wa + k;
-      const int64_t st = share_start(wk, total, W);
-      if (share_start(wk + 1, total, W) != st) {  // else an empty share
-        const int64_t pi = (wk * 2 + (st >= s0 ? 0 : 1)) * cols + col;
-        m = ws_ml[2 * pi];
-        l = ws_ml[2 * pi + 1];
-        row = ws_o + pi * D;
-      }
-    }
+    const int64_t wk = wa + min(k, np - 1);
+    const int64_t st = share_start(wk, total, W);
+    const bool live = k < np && share_start(wk + 1, total, W) != st;
+    const int64_t pi = (wk * 2 + (st >= s0 ? 0 : 1)) * cols + col;
+    const float m_ld = ws_ml[2 * pi];
+    const float l_ld = ws_ml[2 * pi + 1];
+    const float* row = ws_o + pi * D;
+    const int nk = min(64, np - k0);
+    const RowBatch<DL> first = load_rows<DL>(row, 0, nk);  // in flight while the weights are made
+    __builtin_amdgcn_sched_barrier(0);  // keep the uses of m_ld and l_ld below the row loads
+    const float m = live ? m_ld : -INFINITY;
+    const float l = live ? l_ld : 0.0f;
     const float M = wave_max(m);
     const float wgt = m == -INFINITY ? 0.0f : fast_exp2(m - safe_max(M));
     float acc[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-    sum_rows<DL>(acc, wgt, row, min(64, np - k0));
+    sum_rows<DL>(acc, wgt, row, nk, first);
     fold(r, M, wave_sum(l * wgt), acc);
   }
 }
@@ -761,15 +783,21 @@ __global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
   const int N = sp.n + ss.n;
   for (int k0 = 0; k0 < N; k0 += 64) {
     const int k = k0 + lane;
-    const float* ml = nullptr;
-    const float* o = nullptr;
+    // readable defaults, so that the loads below are unconditional
+    const float* ml = a.ws_ml;
+    const float* o = a.ws_o;
     bool have = false;
     if (k < sp.n)
       have = piece_at(sp, k, D, &ml, &o);
     else if (k < N)
       have = piece_at(ss, k - sp.n, D, &ml, &o);
-    const float m = have ? ml[0] : -INFINITY;
-    const float l = have ? ml[1] : 0.0f;
+    const float m_ld = ml[0];
+    const float l_ld = ml[1];
+    const float* row = have ? o : a.ws_o;
+    const int nk = min(64, N - k0);
+    const RowBatch<DL> first = load_rows<DL>(row, 0, nk);  // in flight while the weights are made
+    const float m = have ? m_ld : -INFINITY;
+    const float l = have ? l_ld : 0.0f;
     const float M = wave_max(m);
     const float Ms = safe_max(M);
     const float wgt = have ? fast_exp2(m - Ms) : 0.0f;
@@ -777,7 +805,7 @@ __global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
     float acc[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-    sum_rows<DL>(acc, wgt, have ? o : a.ws_o, min(64, N - k0));
+    sum_rows<DL>(acc, wgt, row, nk, first);
     fold(r, M, lsum, acc);
   }
   write_row(r, out);
