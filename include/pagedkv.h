@@ -180,7 +180,10 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  *   ctx_lens       device, int32 [num_seqs], tokens to attend (includes the
  *                  token written this step). Clamped to
  *                  [0, max_blocks_per_seq*block_size]; 0 gives a zero output.
- *   sm_scale       softmax scale (1/sqrt(head_dim) usually).
+ *   sm_scale       softmax scale (1/sqrt(head_dim) usually); any real value:
+ *                  a negative scale is softmax of the negated logits, 0 the
+ *                  plain average of V over the context (so is an fp8 K
+ *                  multiplier of 0, e.g. for a head of zeros).
  *   k_scale/v_scale fp8 only: dequantisation multipliers (K = byte * k_scale);
  *                  kv_dtype PKV_KV_FP8_E4M3 or PKV_KV_FP8_E5M2 (both widened
  *                  to fp16 exactly before the arithmetic).
