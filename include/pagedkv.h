@@ -435,10 +435,13 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* sl
  * updates_out[3*k .. 3*k+2] = (batch row, logical block index, physical
  * block) for every table entry the step added or replaced by copy-on-write
  * (at most one per sequence), *n_updates their count; ctx_lens_out[n_seqs]
- * gets the new token counts. Capacity of updates_out: 3*n_seqs. */
+ * gets the new token counts. Capacity of updates_out: 3*n_seqs. max_blocks
+ * is the column count of the device tables: a sequence whose new token
+ * would need a table entry at index >= max_blocks makes the call INVALID
+ * before any state changes (max_blocks < 1 is INVALID too). */
 int pkv_bm_decode_step(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
                        int32_t* cow_pairs_out, int* n_cow, int32_t* updates_out, int* n_updates,
-                       int32_t* ctx_lens_out);
+                       int32_t* ctx_lens_out, int max_blocks);
 
 /* child shares every block of parent (refcount +1 each) and its token
  * count: beams / parallel samples ([VLLM] §3.2). */

@@ -22,20 +22,21 @@ from . import fp8
 
 
 def gather_sequence(cache, table, length, block_size, kv_dtype="f16", scale=1.0):
-    """Contiguous [length, Hkv, D] float64 copy of one sequence's K or V."""
+    """Contiguous [length, Hkv, D] float64 copy of one sequence's K or V.
+
+    Position t lives in physical block table[t // block_size] at offset
+    t % block_size: take the sequence's first ceil(length / block_size) table
+    entries, pick those blocks out of the pool in table order, lay their
+    slots end to end and keep the first `length` positions."""
     cache = np.asarray(cache)
     hkv, d = cache.shape[1], cache.shape[3]
-    out = np.empty((length, hkv, d), dtype=np.float64)
-    for t in range(0, length, block_size):
-        phys = int(table[t // block_size])
-        n = min(block_size, length - t)
-        rows = cache[phys, :, :n, :]  # [Hkv, n, D]
-        if kv_dtype in fp8.KV_FORMATS:
-            vals = fp8.dequantize(rows, scale, fp8.KV_FORMATS[kv_dtype])  # per tensor or per KV head
-        else:
-            vals = rows.astype(np.float64)
-        out[t:t + n] = np.transpose(vals, (1, 0, 2))
-    return out
+    nblk = -(-length // block_size)
+    phys = np.asarray(table[:nblk], dtype=np.int64)
+    blocks = cache[phys]                       # [nblk, Hkv, bs, D] stored values, logical block order
+    rows = np.transpose(blocks, (0, 2, 1, 3)).reshape(nblk * block_size, hkv, d)[:length]
+    if kv_dtype in fp8.KV_FORMATS:
+        return fp8.dequantize(rows, scale, fp8.KV_FORMATS[kv_dtype], head_axis=1)  # per tensor or KV head
+    return rows.astype(np.float64)
 
 
 def attend_one(q_h, K, V, sm_scale):

@@ -14,6 +14,8 @@ e4m3fn) so that a kernel reading past a sequence's tokens shows up.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+from contextlib import nullcontext
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -118,10 +120,51 @@ def _host_pool(wl, alloc):
             empty_cache(n, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype))
 
 
-def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) -> OracleRun:
+def _blas_one_thread():
+    """Keep BLAS to one thread while sequences are spread over Python threads."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl ships with scikit-learn
+        return nullcontext()
+    return threadpool_limits(1)
+
+
+def per_sequence(fn, seqs, threads: int):
+    """Call fn(s) for every s in seqs, on `threads` threads when threads > 1.
+
+    Sequences are independent (each reads the caches and writes its own output
+    rows), so spreading them over threads changes no arithmetic: every
+    sequence's result is the same call as in a serial loop."""
+    seqs = list(seqs)
+    if threads <= 1 or len(seqs) <= 1:
+        for s in seqs:
+            fn(s)
+        return
+    with _blas_one_thread(), ThreadPoolExecutor(max_workers=threads) as ex:
+        for _ in ex.map(fn, seqs):
+            pass
+
+
+def _decode_step(wl, step, kc, vc, tables, lens, seqs, heads, threads):
+    q = wl.queries(step)
+    if threads <= 1:
+        return decode_attention(q, kc, vc, tables, lens, wl.block_size, wl.sm_scale, wl.kv_dtype,
+                                wl.k_scale, wl.v_scale, seqs=seqs, heads=heads)
+    out = np.full((len(wl.batch), wl.num_q_heads, wl.head_dim), np.nan, dtype=np.float64)
+
+    def one(s):
+        out[s] = decode_attention(q, kc, vc, tables, lens, wl.block_size, wl.sm_scale, wl.kv_dtype,
+                                  wl.k_scale, wl.v_scale, seqs=[s], heads=heads)[s]
+
+    per_sequence(one, range(len(wl.batch)) if seqs is None else seqs, threads)
+    return out
+
+
+def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False, threads: int = 1) -> OracleRun:
     """Apply the setup rounds and `steps` decode steps; attention after each step.
 
     seqs / heads restrict attention to a sample of batch positions / query heads.
+    threads > 1 spreads the sequences of each step's attention over threads.
     """
     alloc = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
     kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
@@ -139,9 +182,7 @@ def run(wl, steps: int = 1, seqs=None, heads=None, keep_rounds: bool = False) ->
             run_.rounds.append(r)
         tables = [alloc.block_table(s) for s in wl.batch]
         lens = [alloc.num_tokens(s) for s in wl.batch]
-        out = decode_attention(wl.queries(step), kc, vc, tables, lens, wl.block_size,
-                               wl.sm_scale, wl.kv_dtype, wl.k_scale, wl.v_scale,
-                               seqs=seqs, heads=heads)
+        out = _decode_step(wl, step, kc, vc, tables, lens, seqs, heads, threads)
         run_.outputs.append(out)
         run_.tables.append(tables)
         run_.ctx_lens.append(lens)
@@ -171,12 +212,13 @@ class PrefillRun:
         return out
 
 
-def run_prefill(wl, seqs=None) -> PrefillRun:
+def run_prefill(wl, seqs=None, threads: int = 1) -> PrefillRun:
     """Apply the setup rounds, then one prefill pass: every batch sequence's
     chunk (the positions its prompt did not find in the prefix cache, or its
     scripted last positions) attends causally over its context
     ("Where Did the VRAM Go (KV cache tutorial)", §4.2). seqs restricts
-    attention to a sample of batch positions."""
+    attention to a sample of batch positions; threads > 1 spreads the
+    sequences over threads."""
     alloc = BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
     kc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
     vc = empty_cache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
@@ -191,9 +233,13 @@ def run_prefill(wl, seqs=None) -> PrefillRun:
     tables = [alloc.block_table(s) for s in wl.batch]
     lens = [alloc.num_tokens(s) for s in wl.batch]
     rows = {}
-    for i in (range(len(wl.batch)) if seqs is None else seqs):
+
+    def one(i):
         s, n = wl.batch[i], chunks[i]
         q = wl.prefill_queries(s, n)
         rows[i] = prefill_attention(q, [0, n], kc, vc, [tables[i]], [lens[i]], wl.block_size, wl.sm_scale,
                                     wl.kv_dtype, wl.k_scale, wl.v_scale)
+
+    per_sequence(one, range(len(wl.batch)) if seqs is None else seqs, threads)
+    rows = dict(sorted(rows.items()))
     return PrefillRun(alloc, kc, vc, cached, chunks, q_start, tables, lens, rows)

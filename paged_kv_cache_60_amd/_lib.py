@@ -100,7 +100,7 @@ SIGNATURES = {
     "pkv_bm_allocate_prompt": (_c_int, [_vp, _c_i64, _p_i32, _c_int, _p_int, _p_i64]),
     "pkv_bm_append": (_c_int, [_vp, _c_i64, _c_int, _p_i64, _p_i32, _p_i32]),
     "pkv_bm_append_batch": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int]),
-    "pkv_bm_decode_step": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int, _p_i32, _p_int, _p_i32]),
+    "pkv_bm_decode_step": (_c_int, [_vp, _p_i64, _c_int, _p_i64, _p_i32, _p_int, _p_i32, _p_int, _p_i32, _c_int]),
     "pkv_bm_fork": (_c_int, [_vp, _c_i64, _c_i64]),
     "pkv_bm_share_prefix": (_c_int, [_vp, _c_i64, _c_int, _c_i64]),
     "pkv_bm_free": (_c_int, [_vp, _c_i64]),

@@ -96,13 +96,14 @@ class BlockManager:
         return n.value
 
     def decode_step(self, seqs: np.ndarray, slot_out: np.ndarray, cow_out: np.ndarray,
-                    upd_out: np.ndarray, ctx_out: np.ndarray):
-        """One token per sequence plus the block-table updates; returns (#pairs, #updates)."""
+                    upd_out: np.ndarray, ctx_out: np.ndarray, max_blocks: int):
+        """One token per sequence plus the block-table updates; returns (#pairs, #updates).
+        Raises (state unchanged) if a table would need more than max_blocks entries."""
         n_cow = ctypes.c_int(0)
         n_upd = ctypes.c_int(0)
         check(self._lib.pkv_bm_decode_step(self._h, _i64p(seqs), len(seqs), _i64p(slot_out), _i32p(cow_out),
                                            ctypes.byref(n_cow), _i32p(upd_out), ctypes.byref(n_upd),
-                                           _i32p(ctx_out)), "pkv_bm_decode_step")
+                                           _i32p(ctx_out), int(max_blocks)), "pkv_bm_decode_step")
         return n_cow.value, n_upd.value
 
     def fork(self, parent: int, child: int) -> None:

@@ -445,14 +445,21 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* sl
 
 int pkv_bm_decode_step(pkv_bm* bm, const int64_t* seqs, int n_seqs, int64_t* slot_mapping_out,
                        int32_t* cow_pairs_out, int* n_cow, int32_t* updates_out, int* n_updates,
-                       int32_t* ctx_lens_out) {
-  if (!bm || !n_updates || n_seqs < 0 || (n_seqs > 0 && (!seqs || !updates_out || !ctx_lens_out)))
+                       int32_t* ctx_lens_out, int max_blocks) {
+  if (!bm || !n_updates || n_seqs < 0 || max_blocks < 1 ||
+      (n_seqs > 0 && (!seqs || !updates_out || !ctx_lens_out)))
     return PKV_ERR_INVALID;
   // Table sizes before the step tell which entries the appends replace or add.
+  // A sequence whose next token would need a table entry past the device
+  // table's max_blocks columns is rejected before anything changes (the
+  // device tables could not hold the entry).
   std::vector<int32_t> before(n_seqs, 0);
   for (int i = 0; i < n_seqs; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    if (it != bm->seqs.end()) before[i] = static_cast<int32_t>(it->second.table.size());
+    if (it == bm->seqs.end()) continue;  // append_batch_impl reports NO_SEQ
+    before[i] = static_cast<int32_t>(it->second.table.size());
+    const int64_t need = (it->second.count + bm->bs) / bm->bs;  // ceil((count + 1) / bs)
+    if (need > max_blocks) return PKV_ERR_INVALID;
   }
   std::vector<char> cow_row(n_seqs, 0);
   const int st = append_batch_impl(bm, seqs, n_seqs, slot_mapping_out, cow_pairs_out, n_cow,

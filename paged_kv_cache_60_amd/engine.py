@@ -201,7 +201,7 @@ class PagedKVEngine:
             ev = self._events[((k - RING) // EVENT_EVERY) % len(self._events)]
             ev.synchronize()
         slots, ctx, cow, upd = (v.numpy() for v in self._views[slot])
-        n_cow, n_upd = self.bm.decode_step(self.batch, slots, cow, upd, ctx)
+        n_cow, n_upd = self.bm.decode_step(self.batch, slots, cow, upd, ctx, self.max_blocks)
         return slot, n_cow, n_upd
 
     def _end_device_step(self):

@@ -246,7 +246,7 @@ def test_decode_step_updates_reproduce_tables(cfg):
         slots = np.empty(B, dtype=np.int64)
         cow = np.empty(2 * B, dtype=np.int32)
         upd = np.empty(3 * B, dtype=np.int32)
-        n_cow, n_upd = c.decode_step(batch, slots, cow, upd, ctx)
+        n_cow, n_upd = c.decode_step(batch, slots, cow, upd, ctx, mb)
         assert slots.tolist() == ro.slots
         assert [tuple(p) for p in cow[:2 * n_cow].reshape(-1, 2).tolist()] == ro.cow_pairs
         for row, idx, blk in upd[:3 * n_upd].reshape(-1, 3).tolist():
@@ -262,6 +262,32 @@ def test_decode_step_updates_reproduce_tables(cfg):
     assert total_upd > 0
     if cfg == "5cow":
         assert total_cow > 0  # beams whose tail starts in the decode step copy their block
+
+
+def test_decode_step_rejects_table_overflow():
+    """A sequence whose next token needs a table entry past max_blocks makes the
+    step INVALID, and nothing changes (the device tables could not hold it)."""
+    c = BlockManager(16, 4, None)
+    c.allocate(0, 8)        # 2 full blocks: the next token needs a third entry
+    c.allocate(1, 5)        # 2 blocks, the second partly filled
+    batch = np.asarray([1, 0], dtype=np.int64)
+    slots = np.empty(2, dtype=np.int64)
+    cow = np.empty(4, dtype=np.int32)
+    upd = np.empty(6, dtype=np.int32)
+    ctx = np.full(2, -7, dtype=np.int32)
+    before = c.state([0, 1])
+    free_before = c.free_list()
+    with pytest.raises(PkvError):
+        c.decode_step(batch, slots, cow, upd, ctx, 2)
+    assert c.state([0, 1]) == before and c.free_list() == free_before
+    assert ctx.tolist() == [-7, -7]
+    with pytest.raises(PkvError):
+        c.decode_step(batch, slots, cow, upd, ctx, 0)
+    assert c.state([0, 1]) == before
+    # with room for the third entry the same step goes through
+    n_cow, n_upd = c.decode_step(batch, slots, cow, upd, ctx, 3)
+    assert (n_cow, n_upd) == (0, 1) and ctx.tolist() == [6, 9]
+    assert upd[:3].tolist() == [1, 2, c.block_table(0)[2]]
 
 
 # ------------------------------------------------------------------ prefix cache
