@@ -22,6 +22,15 @@
  *     work queued on `stream` has finished. `stream` is a hipStream_t passed
  *     as void* (NULL = the null stream). Kernels allocate nothing and return
  *     as soon as the work is queued.
+ *   - Alignment: the kernels move K/V rows, queries, outputs, host-pool
+ *     blocks and workspaces with 16-byte vector accesses, so every such
+ *     pointer (k_new, v_new, k_cache, v_cache, k_host, v_host, q, out,
+ *     workspace) must be 16-byte aligned; index and scale arrays must be
+ *     aligned to their element size (8 bytes for int64 slot mappings, 4 for
+ *     int32 tables, lengths, pairs, updates and groups, and float scales).
+ *     A misaligned pointer makes the call PKV_ERR_INVALID before anything is
+ *     queued. (hipMalloc and torch allocations are 256-byte aligned; a view
+ *     that starts inside an allocation may not be.)
  *   - Every call returns a pkv_status. Argument errors are detected on the
  *     host before anything is queued and leave all state unchanged.
  *   - Out-of-range indices that only the device can see (a slot, a block

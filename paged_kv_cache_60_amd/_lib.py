@@ -145,9 +145,32 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+_bm_lib = None
+
+
+def load_block_manager() -> ctypes.CDLL:
+    """The library whose pkv_bm_* functions BlockManager calls: libpagedkv.so,
+    unless $PKV_BM_LIB names a host-only build of the block manager (the tests
+    build one with the address and undefined-behaviour sanitizers and run the
+    block-manager suite against it). Only the pkv_* symbols are bound then."""
+    global _bm_lib
+    path = os.environ.get("PKV_BM_LIB")
+    if not path:
+        return load()
+    if _bm_lib is None:
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            if name.startswith("pkv_"):
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+        _bm_lib = lib
+    return _bm_lib
+
+
 class PkvError(RuntimeError):
     def __init__(self, code: int, where: str):
-        msg = load().pkv_status_str(code).decode()
+        msg = load_block_manager().pkv_status_str(code).decode()
         super().__init__(f"{where}: {msg} ({code})")
         self.code = code
 

@@ -30,7 +30,7 @@ class BlockManager:
     full blocks (host, C++)."""
 
     def __init__(self, num_blocks: int, block_size: int, free_order=None):
-        lib = _lib.load()
+        lib = _lib.load_block_manager()
         self._lib = lib
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)

@@ -1113,6 +1113,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (rc != PKV_OK) return rc;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
+  if (!vec_aligned(out) || !vec_aligned(q) || !vec_aligned(k_cache) || !vec_aligned(v_cache) ||
+      !vec_aligned(workspace) || !aligned_to(block_tables, 4) || !aligned_to(ctx_lens, 4) ||
+      !aligned_to(k_scales, 4) || !aligned_to(v_scales, 4))
+    return PKV_ERR_INVALID;
   const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                         max_blocks_per_seq, block_size, partition_tokens);
   if (!workspace || workspace_bytes < need) return PKV_ERR_INVALID;
@@ -1239,6 +1243,11 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
   if (num_groups > 0 && (!group_first || !group_size || !group_prefix)) return PKV_ERR_INVALID;
+  if (!vec_aligned(out) || !vec_aligned(q) || !vec_aligned(k_cache) || !vec_aligned(v_cache) ||
+      !vec_aligned(workspace) || !aligned_to(block_tables, 4) || !aligned_to(ctx_lens, 4) ||
+      !aligned_to(k_scales, 4) || !aligned_to(v_scales, 4) || !aligned_to(group_first, 4) ||
+      !aligned_to(group_size, 4) || !aligned_to(group_prefix, 4))
+    return PKV_ERR_INVALID;
   const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_INVALID;
   rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,

@@ -696,6 +696,10 @@ int prefill_impl(void* out, const void* q, const void* k_cache, const void* v_ca
   if ((int64_t)max_blocks_per_seq * block_size > 0x7FFFFFFF) return PKV_ERR_INVALID;
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !q_start) return PKV_ERR_INVALID;
+  if (!vec_aligned(out) || !vec_aligned(q) || !vec_aligned(k_cache) || !vec_aligned(v_cache) ||
+      !aligned_to(block_tables, 4) || !aligned_to(ctx_lens, 4) || !aligned_to(q_start, 4) ||
+      !aligned_to(k_scales, 4) || !aligned_to(v_scales, 4))
+    return PKV_ERR_INVALID;
 
   const bool fp8 = kv_dtype != PKV_KV_F16;
   const float kLog2e = 1.4426950408889634f;

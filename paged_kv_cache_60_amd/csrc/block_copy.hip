@@ -74,6 +74,9 @@ extern "C" int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void
     return PKV_ERR_INVALID;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !k_host || !v_host || !pairs) return PKV_ERR_INVALID;
+  if (!pkv::vec_aligned(k_cache) || !pkv::vec_aligned(v_cache) || !pkv::vec_aligned(k_host) ||
+      !pkv::vec_aligned(v_host) || !pkv::aligned_to(pairs, 4))
+    return PKV_ERR_INVALID;
   if (num_pairs > 0x7FFFFFFF / 2) return PKV_ERR_INVALID;
   const bool out = direction == PKV_SWAP_OUT;
   using pkv::u32x4;
@@ -93,6 +96,8 @@ extern "C" int paged_block_copy(void* k_cache, void* v_cache, const int32_t* pai
     return PKV_ERR_INVALID;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID;
+  if (!pkv::vec_aligned(k_cache) || !pkv::vec_aligned(v_cache) || !pkv::aligned_to(pairs, 4))
+    return PKV_ERR_INVALID;
   if (num_pairs > 65535) return PKV_ERR_INVALID;
   hipLaunchKernelGGL(pkv::block_copy_kernel, dim3(num_pairs, 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<pkv::u32x4*>(k_cache),

@@ -40,6 +40,15 @@ __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Host-side argument check: the kernels read and write K/V rows, queries,
+// outputs, host-pool blocks and workspaces with 16-byte vector accesses, and
+// index arrays element by element, so each pointer must be aligned to
+// kVecAlign or to its element size. A null pointer passes (null checks are
+// separate).
+constexpr uintptr_t kVecAlign = 16;
+inline bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline bool vec_aligned(const void* p) { return aligned_to(p, kVecAlign); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // dot of two packed fp16 pairs, accumulated in fp32

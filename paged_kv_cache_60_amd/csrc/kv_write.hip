@@ -153,6 +153,12 @@ int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v
   const int64_t meta_work = meta ? (meta->n_ctx > meta->n_updates ? meta->n_ctx : meta->n_updates) : 0;
   if (num_tokens == 0 && meta_work == 0) return PKV_OK;
   if (num_tokens > 0 && (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)) return PKV_ERR_INVALID;
+  if (!vec_aligned(k_new) || !vec_aligned(v_new) || !vec_aligned(k_cache) || !vec_aligned(v_cache) ||
+      !aligned_to(slot_mapping, 8) || !aligned_to(k_inv_h, 4) || !aligned_to(v_inv_h, 4))
+    return PKV_ERR_INVALID;
+  if (meta && (!aligned_to(meta->ctx_src, 4) || !aligned_to(meta->ctx_dst, 4) || !aligned_to(meta->updates, 4) ||
+               !aligned_to(meta->tables, 4)))
+    return PKV_ERR_INVALID;
   if (num_kv_heads > 65535) return PKV_ERR_INVALID;  // one grid row per head
   const int cpr_log2 = head_dim == 64 ? 3 : 4;      // log2(head_dim / 8)
   const int bs_log2 = block_size == 16 ? 4 : (block_size == 32 ? 5 : 6);

@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "../../include/pagedkv.h"
+#include "device_common.hpp"
 
 namespace pkv {
 namespace {
@@ -53,6 +54,10 @@ extern "C" int paged_step_metadata(const int64_t* slots_src, int64_t* slots_dst,
   if (n_seqs > 0 && (!slots_src || !slots_dst || !ctx_src || !ctx_dst)) return PKV_ERR_INVALID;
   if (n_cow > 0 && (!cow_src || !cow_dst)) return PKV_ERR_INVALID;
   if (n_updates > 0 && (!updates || !block_tables)) return PKV_ERR_INVALID;
+  if (!pkv::aligned_to(slots_src, 8) || !pkv::aligned_to(slots_dst, 8) || !pkv::aligned_to(ctx_src, 4) ||
+      !pkv::aligned_to(ctx_dst, 4) || !pkv::aligned_to(cow_src, 4) || !pkv::aligned_to(cow_dst, 4) ||
+      !pkv::aligned_to(updates, 4) || !pkv::aligned_to(block_tables, 4))
+    return PKV_ERR_INVALID;
   const int work = n_seqs > n_updates ? (n_seqs > 2 * n_cow ? n_seqs : 2 * n_cow)
                                       : (n_updates > 2 * n_cow ? n_updates : 2 * n_cow);
   if (work == 0) return PKV_OK;

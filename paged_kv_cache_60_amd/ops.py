@@ -10,7 +10,7 @@ import ctypes
 
 import torch
 
-from . import _lib
+from . import _lib, guards
 from ._lib import PkvError, check
 
 F16 = "f16"
@@ -56,6 +56,20 @@ def _require(cond: bool, where: str, what: str):
         raise PkvError(_lib.PKV_ERR_INVALID, f"{where}: {what}")
 
 
+def _guard_slots(slot_mapping, T, num_slots, where):
+    """With debug checks on: no two valid tokens may share a slot."""
+    if guards.debug_checks() and T > 0:
+        dup = guards.slot_conflicts(slot_mapping[:T].cpu().numpy(), num_slots)
+        _require(len(dup) == 0, where, f"slots written by more than one token: {dup[:8].tolist()}")
+
+
+def _guard_pairs(pairs, n_src, n_dst, where):
+    """With debug checks on: no pair's destination is another pair's source or destination."""
+    if guards.debug_checks() and pairs.shape[0] > 0:
+        bad = guards.pair_conflicts(pairs.cpu().numpy(), n_src, n_dst)
+        _require(len(bad) == 0, where, f"copy pairs that race with another pair: {bad[:8]}")
+
+
 def _cache_ok(c: torch.Tensor, kv_dtype: str) -> bool:
     if not (c.is_cuda and c.is_contiguous() and c.dim() == 4):
         return False
@@ -76,6 +90,7 @@ def paged_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, kv_dtype=F16,
     _require(k_new.dim() == 3 and k_new.shape[1] == hkv and k_new.shape[2] == d, w, "k_new shape")
     _require(slot_mapping.is_cuda and slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,)
              and slot_mapping.is_contiguous(), w, "slot_mapping")
+    _guard_slots(slot_mapping, T, nb * bs, w)
     lib = _lib.load()
     if _per_head(k_inv_scale):
         _require(_scales_ok(k_inv_scale, v_inv_scale, hkv), w, "per-head inverse scales")
@@ -102,6 +117,7 @@ def paged_block_copy(k_cache, v_cache, pairs, stream=None):
              and pairs.shape[1] == 2 and pairs.is_contiguous(), w, "pairs")
     nb = k_cache.shape[0]
     block_bytes = k_cache[0].numel() * k_cache.element_size()
+    _guard_pairs(pairs, nb, None, w)
     lib = _lib.load()
     check(lib.paged_block_copy(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], nb, block_bytes,
                                _stream_ptr(stream)), w)
@@ -120,6 +136,8 @@ def paged_block_swap(k_cache, v_cache, k_host, v_host, pairs, direction, stream=
     _require(_device_readable(pairs) and pairs.dtype == torch.int32 and pairs.dim() == 2
              and pairs.shape[1] == 2 and pairs.is_contiguous(), w, "pairs")
     _require(direction in ("out", "in"), w, "direction")
+    n_dev, n_host = k_cache.shape[0], k_host.shape[0]
+    _guard_pairs(pairs, *((n_dev, n_host) if direction == "out" else (n_host, n_dev)), w)
     block_bytes = k_cache[0].numel() * k_cache.element_size()
     lib = _lib.load()
     check(lib.paged_block_swap(_p(k_cache), _p(v_cache), _p(k_host), _p(v_host), _p(pairs), pairs.shape[0],
@@ -150,6 +168,7 @@ def paged_kv_write_step(k_new, v_new, k_cache, v_cache, slot_mapping, ctx_src, c
              w, "updates")
     _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2, w, "tables")
     rows, maxb = block_tables.shape
+    _guard_slots(slot_mapping, T, nb * bs, w)
     lib = _lib.load()
     if _per_head(k_inv_scale):
         _require(_scales_ok(k_inv_scale, v_inv_scale, hkv), w, "per-head inverse scales")

@@ -144,3 +144,111 @@ def test_shared_workspace_bytes():
     assert f(256, 16, 8, 128) == expect(256, 16, 8, 128)
     assert f(3, 8, 8, 64) == expect(3, 8, 8, 64)
     assert f(4097, 8, 8, 64) == 0 and f(0, 8, 8, 64) == 0 and f(4, 12, 8, 64) == 0 and f(4, 8, 8, 96) == 0
+
+
+# ------------------------------------------------------------ alignment contract
+# Each call below is valid except for one pointer that breaks the alignment the
+# kernels need (16 bytes for row data and workspaces, the element size for
+# index arrays); it must be rejected on the host before anything is queued.
+# The pointers are fake, so these calls must never reach a launch: they are
+# skipped where a GPU is visible.
+try:
+    import torch
+    _GPU = torch.cuda.is_available()
+except ImportError:  # pragma: no cover
+    _GPU = False
+no_gpu = pytest.mark.skipif(_GPU, reason="fake pointers: only where no launch can happen")
+
+MIS16 = ctypes.c_void_p(0x1008)  # 8-byte aligned, not 16
+MIS4 = ctypes.c_void_p(0x1002)   # 2-byte aligned
+MIS8 = ctypes.c_void_p(0x1004)   # 4-byte aligned, not 8
+
+
+@no_gpu
+@pytest.mark.parametrize("bad", [dict(out=MIS16), dict(q=MIS16), dict(k=MIS16), dict(v=MIS16), dict(ws=MIS16),
+                                 dict(tab=MIS4), dict(ctx=MIS4)])
+def test_attention_rejects_misaligned_pointers(bad):
+    assert attn(wsb=1 << 30, **bad) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("bad", [dict(out=MIS16), dict(q=MIS16), dict(k=MIS16), dict(v=MIS16), dict(ws=MIS16),
+                                 dict(tab=MIS4), dict(ctx=MIS4), dict(gf=MIS4), dict(gs=MIS4), dict(gp=MIS4)])
+def test_shared_decode_rejects_misaligned_pointers(bad):
+    assert shared(**bad) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+def test_scaled_decode_rejects_misaligned_scales():
+    lib = _lib.load()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 8, 8, 128, 16, 16, 0.1, 1]
+    assert lib.paged_attn_decode_scaled(*args, MIS4, FAKE, 0, FAKE, 1 << 30, 3, N) == _lib.PKV_ERR_INVALID
+    assert lib.paged_attn_decode_scaled(*args, FAKE, MIS4, 0, FAKE, 1 << 30, 3, N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos,ptr", [(0, MIS16), (1, MIS16), (2, MIS16), (3, MIS16), (4, MIS8)])
+def test_write_rejects_misaligned_pointers(pos, ptr):
+    lib = _lib.load()
+    p = [FAKE] * 5
+    p[pos] = ptr
+    assert lib.paged_kv_write(*p, 3, 4, 2, 64, 16, 0, 1.0, 1.0, N) == _lib.PKV_ERR_INVALID
+    assert lib.paged_kv_write_step(*p, 3, 4, 2, 64, 16, 0, 1.0, 1.0, FAKE, FAKE, 3, FAKE, 1, FAKE, 3, 4,
+                                   N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos", [0, 1, 2, 3])
+def test_write_step_rejects_misaligned_metadata(pos):
+    lib = _lib.load()
+    m = [FAKE] * 4  # ctx_src, ctx_dst, updates, block_tables
+    m[pos] = MIS4
+    assert lib.paged_kv_write_step(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 64, 16, 0, 1.0, 1.0, m[0], m[1], 3,
+                                   m[2], 1, m[3], 3, 4, N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+def test_write_scaled_rejects_misaligned_scales():
+    lib = _lib.load()
+    assert lib.paged_kv_write_scaled(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 64, 16, 1, MIS4, FAKE,
+                                     N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos,ptr", [(0, MIS16), (1, MIS16), (2, MIS4)])
+def test_block_copy_rejects_misaligned_pointers(pos, ptr):
+    lib = _lib.load()
+    p = [FAKE] * 3
+    p[pos] = ptr
+    assert lib.paged_block_copy(*p, 2, 4, 4096, N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos,ptr", [(0, MIS16), (1, MIS16), (2, MIS16), (3, MIS16), (4, MIS4)])
+def test_block_swap_rejects_misaligned_pointers(pos, ptr):
+    lib = _lib.load()
+    p = [FAKE] * 5
+    p[pos] = ptr
+    assert lib.paged_block_swap(*p, 2, 4, 4, 4096, 0, N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos,ptr", [(0, MIS16), (1, MIS16), (2, MIS16), (3, MIS16), (4, MIS4), (5, MIS4),
+                                     (6, MIS4)])
+def test_prefill_rejects_misaligned_pointers(pos, ptr):
+    lib = _lib.load()
+    p = [FAKE] * 7  # out, q, k, v, tables, ctx, q_start
+    p[pos] = ptr
+    assert lib.paged_attn_prefill(p[0], p[1], p[2], p[3], p[4], 8, p[5], p[6], 2, 10, 8, 8, 128, 16, 16, 0.1, 0,
+                                  1.0, 1.0, N) == _lib.PKV_ERR_INVALID
+
+
+@no_gpu
+@pytest.mark.parametrize("pos,ptr", [(0, MIS8), (1, MIS8), (2, MIS4), (3, MIS4), (4, MIS4), (5, MIS4), (6, MIS4),
+                                     (7, MIS4)])
+def test_step_metadata_rejects_misaligned_pointers(pos, ptr):
+    lib = _lib.load()
+    p = [FAKE] * 8  # slots src/dst, ctx src/dst, cow src/dst, updates, tables
+    p[pos] = ptr
+    assert lib.paged_step_metadata(p[0], p[1], p[2], p[3], 3, p[4], p[5], 1, p[6], 1, p[7], 3, 4,
+                                   N) == _lib.PKV_ERR_INVALID
