@@ -248,6 +248,37 @@ int paged_attn_decode_scaled(void* out, const void* q, const void* k_cache, cons
                              int partition_tokens, void* workspace, size_t workspace_bytes,
                              int passes, void* stream);
 
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, kernels and results as paged_attn_decode with the same
+ * partition_tokens (bit for bit: the same workers and the same sums); the
+ * pass-1 partials and unit prefix live instead in a device array of
+ * PKV_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on each device
+ * for the life of the process, laid out for the workers actually launched:
+ * W * 2 * G * (head_dim + 2) * 4 bytes plus (min(num_seqs, 4096) + 1) * 4,
+ * each part rounded up to 256 (W = paged_attn_decode_workers(...)). With
+ * partition_tokens = 0 every supported shape fits on a 256-CU MI355X (at
+ * most 2048 workers: 17 MB for 8 query heads per KV head and head_dim 128);
+ * a shape or
+ * partition_tokens whose partials do not fit returns PKV_ERR_INVALID before
+ * anything is queued. The call allocates nothing: its first use on a device
+ * only looks up that device's copy of the array (PKV_ERR_HIP if the lookup
+ * fails). Every call on a device shares its array, so calls that overlap on
+ * one device (two streams, or two host threads) race and give wrong results;
+ * queue them on one stream or serialise them. Nothing in the array needs to
+ * start at zero.
+ */
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                              int partition_tokens, void* stream);
+
 /* The number of workers (waves) pass 1 uses for this shape on the current
  * device (for one launch of up to 4096 sequences), or a negative status for an
  * invalid shape or a failed device query. */

@@ -28,6 +28,8 @@ SWAP_IN = 1
 PREEMPT_RECOMPUTE = 0
 PREEMPT_SWAP = 1
 
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_DECODE_NOALLOC_SCRATCH_BYTES
+
 _c_int = ctypes.c_int
 _c_i64 = ctypes.c_int64
 _c_f = ctypes.c_float
@@ -85,6 +87,8 @@ SIGNATURES = {
     "paged_attn_decode_passes": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int,
                                           _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f,
                                           _c_int, _vp, _c_sz, _c_int, _vp]),
+    "paged_attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _c_int, _vp]),
     "paged_attn_decode_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_decode_shared_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int]),
     "paged_attn_decode_shared": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,

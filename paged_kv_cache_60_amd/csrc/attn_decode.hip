@@ -1101,11 +1101,32 @@ int shared_workers(KernFn fn, int B, int NG, int Hkv, int G, int max_blocks, int
   return PKV_OK;
 }
 
+// Bytes of pass-1 partials and unit prefix for W workers: [W][2][G][D] outputs,
+// [W][2][G][2] (max, sum), then [B + 1] ints, each region 256-byte aligned.
+// paged_attn_decode lays them out for kMaxWorkers workers, so that its
+// workspace size does not depend on the device; the allocation-free call
+// for the workers it actually launches.
+struct DecodeLayout {
+  size_t o, ml, pt, total;
+};
+
+DecodeLayout decode_layout(int W, int G, int D, int B) {
+  DecodeLayout L;
+  const size_t pieces = (size_t)W * 2 * G;
+  L.o = 0;
+  L.ml = (pieces * D * sizeof(float) + 255) / 256 * 256;
+  L.pt = L.ml + (pieces * 2 * sizeof(float) + 255) / 256 * 256;
+  L.total = L.pt + ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  return L;
+}
+
+// compact_ws: partials laid out for the workers launched (decode_layout with
+// the plan's worker count) instead of kMaxWorkers.
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                 int max_blocks_per_seq, const int32_t* ctx_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int num_blocks, float sm_scale, int kv_dtype, float k_scale,
                 float v_scale, const float* k_scales, const float* v_scales, int partition_tokens,
-                void* workspace, size_t workspace_bytes, int passes, void* stream) {
+                void* workspace, size_t workspace_bytes, int passes, void* stream, bool compact_ws = false) {
   if (passes < 1 || passes > 3 || num_blocks <= 0) return PKV_ERR_INVALID;
   Plan pl;
   int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
@@ -1117,14 +1138,21 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       !vec_aligned(workspace) || !aligned_to(block_tables, 4) || !aligned_to(ctx_lens, 4) ||
       !aligned_to(k_scales, 4) || !aligned_to(v_scales, 4))
     return PKV_ERR_INVALID;
-  const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                        max_blocks_per_seq, block_size, partition_tokens);
-  if (!workspace || workspace_bytes < need) return PKV_ERR_INVALID;
+  const int G = num_q_heads / num_kv_heads;
+  DecodeLayout lay{};
+  if (!compact_ws) {
+    const size_t need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                          max_blocks_per_seq, block_size, partition_tokens);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_INVALID;
+  }
   rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
             partition_tokens, true, &pl);
   if (rc != PKV_OK) return rc;
+  if (compact_ws) {
+    lay = decode_layout(pl.workers, G, head_dim, num_seqs < kMaxSeqs ? num_seqs : kMaxSeqs);
+    if (!workspace || workspace_bytes < lay.total) return PKV_ERR_INVALID;
+  }
 
-  const int G = num_q_heads / num_kv_heads;
   const bool fp8 = kv_dtype != PKV_KV_F16;
   const float kLog2e = 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1137,9 +1165,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.vc = static_cast<const uint8_t*>(v_cache);
     a.tables = block_tables + (size_t)b0 * max_blocks_per_seq;
     a.ctx_lens = ctx_lens + b0;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = a.ws_o + (size_t)kMaxWorkers * 2 * G * head_dim;
-    a.ws_pt = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)kMaxWorkers * 2 * G * 2);
+    if (compact_ws) {
+      uint8_t* ws = static_cast<uint8_t*>(workspace);
+      a.ws_o = reinterpret_cast<float*>(ws + lay.o);
+      a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+      a.ws_pt = reinterpret_cast<int32_t*>(ws + lay.pt);
+    } else {
+      a.ws_o = static_cast<float*>(workspace);
+      a.ws_ml = a.ws_o + (size_t)kMaxWorkers * 2 * G * head_dim;
+      a.ws_pt = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)kMaxWorkers * 2 * G * 2);
+    }
     a.out = static_cast<f16*>(out) + (size_t)b0 * num_q_heads * head_dim;
     a.max_blocks = max_blocks_per_seq;
     a.B = B;
@@ -1209,6 +1244,58 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_cache, 
                                   ctx_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   block_size, num_blocks, sm_scale, kv_dtype, k_scale, v_scale,
                                   partition_tokens, workspace, workspace_bytes, 3, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the pass-1 partials live in a file-scope device
+// array instead of a caller workspace. Each device holds its own copy of the
+// array (for the life of the process); its address on a device is looked up
+// once, with that device current, and kept.
+
+namespace pkv {
+namespace {
+
+constexpr size_t kNoAllocBytes = PKV_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+// The device address of `scratch` on the current device, or null on error.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kNoAllocDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* ctx_lens, int num_seqs, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                         float sm_scale, int kv_dtype, float k_scale, float v_scale,
+                                         int partition_tokens, void* stream) {
+  using namespace pkv;
+  // shape errors first (no device query), then the scratch address
+  Plan pl;
+  int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
+                partition_tokens, false, &pl);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs == 0) return PKV_OK;
+  void* ws = scratch_ptr();
+  if (!ws) return PKV_ERR_HIP;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, sm_scale, kv_dtype, k_scale, v_scale, nullptr,
+                     nullptr, partition_tokens, ws, kNoAllocBytes, 3, stream, true);
 }
 
 extern "C" size_t paged_attn_decode_shared_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,

@@ -243,6 +243,30 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale
                                        _stream_ptr(stream)), w)
 
 
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale, kv_dtype=F16,
+                              k_scale=1.0, v_scale=1.0, partition_tokens=0, stream=None):
+    """paged_attn_decode with no workspace: the library's per-device scratch array
+    holds the partials, and neither this wrapper nor the call allocates device
+    memory. Calls that overlap on one device race (they share the array)."""
+    w = "paged_attn_decode_noalloc"
+    _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
+    _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")
+    _require(_cache_ok(k_cache, kv_dtype) and _cache_ok(v_cache, kv_dtype) and k_cache.shape == v_cache.shape,
+             w, "caches")
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    _require(d == d2, w, "head_dim")
+    _require(block_tables.is_cuda and block_tables.dtype == torch.int32 and block_tables.dim() == 2
+             and block_tables.shape[0] == B and block_tables.is_contiguous(), w, "block_tables")
+    _require(ctx_lens.is_cuda and ctx_lens.dtype == torch.int32 and ctx_lens.shape == (B,)
+             and ctx_lens.is_contiguous(), w, "ctx_lens")
+    _require(not _per_head(k_scale), w, "per-tensor scales only")
+    check(_lib.load().paged_attn_decode_noalloc(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                                block_tables.shape[1], _p(ctx_lens), B, hq, hkv, d, bs, nb,
+                                                float(sm_scale), kv_dtype_code(kv_dtype), float(k_scale),
+                                                float(v_scale), int(partition_tokens), _stream_ptr(stream)), w)
+
+
 # query columns (sequence, query head) of one pass over a group's shared blocks;
 # a group of more than SHARED_COLUMNS / G members takes several passes
 SHARED_COLUMNS = 32
