@@ -46,7 +46,7 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 EVENT_EVERY = 5  # timed steps per pass-1 event pair
 
 
-KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "attn_shared_mfma.hpp", "device_common.hpp")
+KERNEL_SOURCES = ("attn_decode.hip", "attn_gqa_mfma.hpp", "attn_group_mfma.hpp", "device_common.hpp")
 PREFILL_SOURCES = ("attn_prefill.hip", "device_common.hpp")
 
 
@@ -641,8 +641,8 @@ def main():
     group = wl.num_q_heads // wl.num_kv_heads
     kernel = "attn_partition_mfma_kernel" if group >= 4 else "attn_partition_kernel"
     if args.shared:
-        # the pass-1 events bracket both launches: the shared-prefix pass and pass 1 over the rest
-        kernel = "attn_shared_mfma_kernel + " + kernel
+        # one grouped pass 1 over every sequence: each group's shared blocks once, then the members' tails
+        kernel = "attn_group_mfma_kernel"
         log(f"bench: {eng.groups.shape[1]} shared-prefix groups")
 
     # stage every step's inputs in HBM before timing

@@ -58,8 +58,7 @@ constexpr int kTile = 16;
 constexpr int kWaves = 4;          // waves (workers) per workgroup
 constexpr int kMaxWorkers = 8192;  // the workspace holds partials for this many workers
 constexpr int kMaxSeqs = 4096;     // sequences per launch (their unit prefix lives in LDS)
-constexpr int kSharedCols = 32;    // query columns (member, head) of one shared pass over a prefix
-constexpr int kMaxSharedWorkers = 2048;
+constexpr int kMaxGroupWorkers = 2048;  // the shared-prefix workspace holds partials for this many workers
 
 struct AttnArgs {
   const f16* q;
@@ -89,22 +88,14 @@ struct AttnArgs {
   float qk_base;      // sm_scale * log2(e)
   // Shared-prefix groups (paged_attn_decode_shared; NG = 0 otherwise). Group
   // g is the batch sequences grp_first[g] .. + grp_size[g] - 1; their first
-  // group_tokens(g) tokens are attended in a pass of their own, through the
-  // table of sequence grp_first[g], and pass 1 covers only the rest.
+  // group_tokens(g) tokens are read through the table of sequence
+  // grp_first[g] once for all of them (attn_group_mfma.hpp).
   const int32_t* grp_first = nullptr;
   const int32_t* grp_size = nullptr;
   const int32_t* grp_prefix = nullptr;
   int NG = 0;
-  int g_log2 = 0;           // log2(query heads per KV head)
-  int s_workers = 0;        // workers of the shared pass
-  float* ws_wo = nullptr;   // [B * Hq][D]  whole pass-1 pieces of grouped sequences
-  float* ws_wml = nullptr;  // [B * Hq][2]
-  float* ws_swo = nullptr;  // [B * Hq][D]  whole shared pieces, by (member, query head)
-  float* ws_swml = nullptr; // [B * Hq][2]
-  float* ws_so = nullptr;   // [kMaxSharedWorkers][2][kSharedCols][D]  split shared pieces
-  float* ws_sml = nullptr;  // [kMaxSharedWorkers][2][kSharedCols][2]
-  int32_t* ws_spt = nullptr;  // [NG + 1]  unit prefix over the groups (shared pass -> merge)
-  int32_t* ws_gid = nullptr;  // [B]       group of each sequence or -1 (pass 1 -> merge)
+  int g_log2 = 0;              // log2(query heads per KV head)
+  int32_t* ws_part = nullptr;  // [B] each sequence's part record (grouped pass 1 -> merge)
 };
 
 // The logit and output scales of KV head h.
@@ -144,83 +135,54 @@ __device__ __forceinline__ int group_tokens(const AttnArgs& a, int g) {
   return clamp_len(a.grp_prefix[g], a.max_blocks << a.bs_log2) & ~15;
 }
 
-// Shared tokens of every batch sequence's group, or -1 for a sequence in no
-// group, into the LDS array pre[B] (pass 1 with shared-prefix groups); the
-// first workgroup also writes each sequence's group to ws_gid for the merge.
-// One scatter over the groups: a group's members are consecutive. Ends with a
-// barrier.
-__device__ void build_group_map(const AttnArgs& a, int* pre) {
-  const int T = blockDim.x;
-  const int tid = threadIdx.x;
-  const bool first_wg = blockIdx.x == 0;
-  for (int i = tid; i < a.B; i += T) {
-    pre[i] = -1;
-    if (first_wg) a.ws_gid[i] = -1;
-  }
-  __syncthreads();
-  for (int g = tid; g < a.NG; g += T) {
-    const int n = group_members(a, g);
-    if (n == 0) continue;
-    const int f = a.grp_first[g];
-    const int tok = group_tokens(a, g);
-    for (int m = 0; m < n; ++m) {
-      pre[f + m] = tok;
-      if (first_wg) a.ws_gid[f + m] = g;
-    }
-  }
-  __syncthreads();
-}
-
-// First token pass 1 covers for a sequence of L tokens whose group shares
-// `pre` tokens (-1: no group): 0, or the shared tokens (all L tokens if the
-// prefix is longer).
-__device__ __forceinline__ int private_start(int pre, int L) { return pre < 0 ? 0 : min(pre, L); }
-
-// Units of the shared pass for one part of group g: its prefix's 32-token
-// units (a part is up to kSharedCols query columns of the group's members).
-__device__ __forceinline__ int group_units(const AttnArgs& a, int g) {
-  return (group_tokens(a, g) + 31) / 32;
-}
-
 // pt[0] = 0, pt[i + 1] = pt[i] + units(i) for i < n, by all threads of the
-// workgroup; scan holds blockDim ints. Ends with a barrier.
+// workgroup. units(i) may read pt[i + 1], which the caller may have filled
+// with entry i's own value (a context length) before a barrier. Each wave
+// scans a contiguous quarter of the entries (each lane a run of them, the
+// runs combined with shuffles), the waves' totals go through `scan`
+// (blockDim / 64 ints), and each wave adds the totals of the waves before
+// it: two barriers in all. Ends with a barrier.
 template <class Units>
 __device__ void build_scan(int n, int* pt, int* scan, Units units) {
-  const int T = blockDim.x;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < n; i += T) pt[i + 1] = units(i);
-  __syncthreads();
-  // each thread sums a run of consecutive sequences; the runs are scanned
-  const int per = (n + T - 1) / T;
-  const int b0 = min(n, tid * per);
-  const int b1 = min(n, b0 + per);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int per_wave = (n + nw - 1) / nw;
+  const int w0 = min(n, wv * per_wave);
+  const int w1 = min(n, w0 + per_wave);
+  const int per = (w1 - w0 + 63) / 64;
+  const int b0 = min(w1, w0 + lane * per);
+  const int b1 = min(w1, b0 + per);
   int s = 0;
-  for (int i = b0; i < b1; ++i) s += pt[i + 1];
-  scan[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < T; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  for (int i = b0; i < b1; ++i) {
+    const int u = units(i);
+    pt[i + 1] = u;
+    s += u;
   }
-  int run = scan[tid] - s;
+  int x = s;  // inclusive scan of the runs over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scan[wv] = x;
+  __syncthreads();
+  int run = x - s;
+  for (int k = 0; k < wv; ++k) run += scan[k];
   for (int i = b0; i < b1; ++i) {
     run += pt[i + 1];
     pt[i + 1] = run;
   }
-  if (tid == 0) pt[0] = 0;
+  if (threadIdx.x == 0) pt[0] = 0;
   __syncthreads();
 }
 
-// Dynamic LDS of a pass-1 workgroup: pt[B + 1], scan[blockDim], then with
-// shared-prefix groups pre[B] (build_group_map).
-__device__ void build_prefix(const AttnArgs& a, int* pt, int* scan, int* pre) {
-  if (a.NG) build_group_map(a, pre);
-  build_scan(a.B, pt, scan, [&](int i) {
-    const int L = seq_len(a, i);
-    return (L - (a.NG ? private_start(pre[i], L) : 0) + a.unit_tokens - 1) / a.unit_tokens;
-  });
+// Dynamic LDS of a pass-1 workgroup: pt[B + 1], scan[blockDim]. The context
+// lengths are loaded by every thread at once into pt[i + 1] first.
+__device__ void build_prefix(const AttnArgs& a, int* pt, int* scan) {
+  for (int i = threadIdx.x; i < a.B; i += blockDim.x) pt[i + 1] = seq_len(a, i);
+  __syncthreads();
+  build_scan(a.B, pt, scan, [&](int i) { return (pt[i + 1] + a.unit_tokens - 1) / a.unit_tokens; });
 }
 
 // The last sequence s in [0, B) with pt[s] <= q; pt is non-decreasing, so
@@ -289,8 +251,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
 
   extern __shared__ int dyn_smem[];
   int* pt = dyn_smem;
-  int* pre = pt + a.B + 1 + NW * 64;
-  build_prefix(a, pt, pt + a.B + 1, pre);
+  build_prefix(a, pt, pt + a.B + 1);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -314,10 +275,6 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
-    // a member of a shared-prefix group starts after the shared tokens
-    const int pre_s = a.NG ? wave_uniform(pre[seq]) : -1;
-    const int grp = pre_s;  // >= 0 for a group member
-    const int base = private_start(pre_s, L);
     const float qk_scale = head_qk_scale(a, pc.head);
     const float v_scale = head_v_scale(a, pc.head);
 
@@ -353,12 +310,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
       // block ids of up to 64 tiles, one per lane, fetched together so that
       // no tile waits on its own table read
       int my_blk = -1;
-      if (j0 + lane < pc.u1) my_blk = tab[(base + (j0 + lane) * kTile) >> a.bs_log2];
+      if (j0 + lane < pc.u1) my_blk = tab[((j0 + lane) * kTile) >> a.bs_log2];
       const int nj = min(64, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
         const int blk = __builtin_amdgcn_readlane(my_blk, j);
         if ((unsigned)blk >= (unsigned)a.num_blocks) continue;  // never followed
-        const int t0 = base + (j0 + j) * kTile;
+        const int t0 = (j0 + j) * kTile;
         // A tile lies inside one block, so all 16 rows are in bounds even past
         // the sequence end; rows at or past L are masked below.
         const bool full = t0 + kTile <= L;
@@ -464,27 +421,25 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
       }
     }
 
-    // the whole segment -> output (or, for a group member, the buffer the
-    // merge reads); part of one -> this worker's slot
+    // the whole segment -> output; part of one -> this worker's slot
     const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
     const int slot = t == start ? 0 : 1;
     if (lane < LPR) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (whole && grp < 0) {
+        if (whole) {
           const float sc = l[g] > 0.0f ? v_scale / l[g] : 0.0f;
           f16* o = a.out + ((size_t)seq * a.Hq + hq0 + g) * D + c * E;
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = (f16)(acc[g][e] * sc);
         } else {
-          const size_t pi = whole ? (size_t)seq * a.Hq + hq0 + g : ((size_t)w * 2 + slot) * G + g;
-          float* o = (whole ? a.ws_wo : a.ws_o) + pi * D + c * E;
-          float* ml = whole ? a.ws_wml : a.ws_ml;
+          const size_t pi = ((size_t)w * 2 + slot) * G + g;
+          float* o = a.ws_o + pi * D + c * E;
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = acc[g][e] * v_scale;
           if (lane == 0) {
-            ml[2 * pi] = m[g];
-            ml[2 * pi + 1] = l[g];
+            a.ws_ml[2 * pi] = m[g];
+            a.ws_ml[2 * pi + 1] = l[g];
           }
         }
       }
@@ -664,158 +619,11 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
   write_row(r, out);
 }
 
-// Where the merge finds the pieces of one segment of one output row: split
-// between the workers [wa, wb] of a unit space (slots of `cols` columns, this
-// row's column `col`), or held whole by one worker (one piece at row `wid` of
-// the whole-piece buffers).
-struct SegPieces {
-  int n = 0;  // pieces (0: no segment)
-  bool whole = false;
-  int64_t wa = 0, s0 = 0, total = 1, W = 1;
-  const float* o = nullptr;
-  const float* ml = nullptr;
-  int cols = 0, col = 0;
-};
-
-__device__ __forceinline__ SegPieces seg_pieces(int64_t s0, int64_t s1, int64_t total, int64_t W, const float* o,
-                                                const float* ml, int cols, int col, const float* wo,
-                                                const float* wml, int64_t wid, int D) {
-  SegPieces p;
-  if (s0 < 0 || s0 >= s1 || s1 > total) return p;  // empty (or inconsistent group entries)
-  const int64_t wa = ((s0 + 1) * W - 1) / total;
-  const int64_t wb = (s1 * W - 1) / total;
-  if (wa == wb) {
-    p.n = 1;
-    p.whole = true;
-    p.o = wo + wid * D;
-    p.ml = wml + 2 * wid;
-    return p;
-  }
-  p.n = (int)(wb - wa + 1);
-  p.wa = wa;
-  p.s0 = s0;
-  p.total = total;
-  p.W = W;
-  p.o = o;
-  p.ml = ml;
-  p.cols = cols;
-  p.col = col;
-  return p;
-}
-
-// Piece k of a segment: its (max, sum) pair and output row, or false for the
-// empty share of a worker.
-__device__ __forceinline__ bool piece_at(const SegPieces& p, int k, int D, const float** ml, const float** o) {
-  if (p.whole) {
-    *ml = p.ml;
-    *o = p.o;
-    return true;
-  }
-  const int64_t wk = p.wa + k;
-  const int64_t st = share_start(wk, p.total, p.W);
-  if (share_start(wk + 1, p.total, p.W) == st) return false;
-  const int slot = st >= p.s0 ? 0 : 1;  // slot 0: the piece starts the worker's share
-  const int64_t pi = (wk * 2 + slot) * p.cols + p.col;
-  *ml = p.ml + 2 * pi;
-  *o = p.o + pi * D;
-  return true;
-}
-
-// Pass 2 of the shared-prefix decode. One wave per (sequence, query head). A
-// sequence outside every group is handled exactly as in attn_reduce_kernel. A group
-// member merges the pieces of its pass-1 segment and of its columns in the
-// shared pass over its group's prefix: every piece's (max, sum) is loaded at
-// once (lane k holds piece k), then the output rows, weighted.
-template <int D, int G>
-__global__ void __launch_bounds__(256) attn_reduce_shared_kernel(AttnArgs a) {
-  constexpr int DL = D / 64;
-  constexpr int MP = kSharedCols / G;  // members per shared pass
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= a.B * a.Hq) return;
-  const int lane = threadIdx.x & 63;
-  const int seq = wid / a.Hq;
-  const int hq = wid - seq * a.Hq;
-  const int kvh = hq / G;
-  const int g = hq - kvh * G;
-  // the index loads are issued together, unconditionally (the workspace
-  // always holds these arrays): the group map (written by pass 1 only when
-  // there are groups), pass 1's unit prefix and the shared pass's
-  const int gid_ws = a.ws_gid[seq];
-  const int p0 = a.ws_pt[seq];
-  const int p1 = a.ws_pt[seq + 1];
-  const int P = a.ws_pt[a.B];
-  const int PS = a.ws_spt[a.NG];
-  const int gid = a.NG ? gid_ws : -1;
-  const int grp = gid >= 0 && gid < a.NG ? gid : -1;
-  const int n_u = p1 - p0;
-  f16* out = a.out + (size_t)wid * D + lane * DL;
-
-  const int64_t totalP = (int64_t)a.Hkv * P;
-  const int64_t s0P = (int64_t)kvh * P + p0;
-  if (grp < 0) {  // exactly as attn_reduce_kernel: the same bits as paged_attn_decode
-    Row<DL> r;
-    if (n_u > 0) {
-      if (held_whole(s0P, s0P + n_u, totalP, a.workers)) return;  // written by pass 1
-      fold_pieces<D>(r, a.ws_o, a.ws_ml, G, g, s0P, s0P + n_u, totalP, a.workers);
-    }
-    write_row(r, out);
-    return;
-  }
-  SegPieces sp;
-  if (n_u > 0)
-    sp = seg_pieces(s0P, s0P + n_u, totalP, a.workers, a.ws_o, a.ws_ml, G, g, a.ws_wo, a.ws_wml, wid, D);
-  SegPieces ss;
-  {
-    const int first = a.grp_first[grp];
-    const int spt = a.ws_spt[grp];
-    const int ug = group_units(a, grp);
-    const int m = seq - first;
-    if (ug > 0 && m >= 0) {
-      const int part = m / MP;
-      const int c = (m - part * MP) * G + g;
-      const int64_t s0 = (int64_t)kvh * PS + spt + (int64_t)part * ug;
-      ss = seg_pieces(s0, s0 + ug, (int64_t)a.Hkv * PS, a.s_workers, a.ws_so, a.ws_sml, kSharedCols, c, a.ws_swo,
-                      a.ws_swml, wid, D);
-    }
-  }
-
-  Row<DL> r;
-  const int N = sp.n + ss.n;
-  for (int k0 = 0; k0 < N; k0 += 64) {
-    const int k = k0 + lane;
-    // readable defaults, so that the loads below are unconditional
-    const float* ml = a.ws_ml;
-    const float* o = a.ws_o;
-    bool have = false;
-    if (k < sp.n)
-      have = piece_at(sp, k, D, &ml, &o);
-    else if (k < N)
-      have = piece_at(ss, k - sp.n, D, &ml, &o);
-    const float m_ld = ml[0];
-    const float l_ld = ml[1];
-    const float* row = have ? o : a.ws_o;
-    const int nk = min(64, N - k0);
-    const RowBatch<DL> first = load_rows<DL>(row, 0, nk);  // in flight while the weights are made
-    const float m = have ? m_ld : -INFINITY;
-    const float l = have ? l_ld : 0.0f;
-    const float M = wave_max(m);
-    const float Ms = safe_max(M);
-    const float wgt = have ? fast_exp2(m - Ms) : 0.0f;
-    const float lsum = wave_sum(l * wgt);
-    float acc[DL];
-#pragma unroll
-    for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-    sum_rows<DL>(acc, wgt, row, nk, first);
-    fold(r, M, lsum, acc);
-  }
-  write_row(r, out);
-}
-
 }  // namespace
 }  // namespace pkv
 
 #include "attn_gqa_mfma.hpp"
-#include "attn_shared_mfma.hpp"
+#include "attn_group_mfma.hpp"
 
 namespace pkv {
 namespace {
@@ -867,31 +675,31 @@ KernFn pick_reduce(int D, int G) {
 }
 
 template <int D>
-KernFn pick_reduce_shared_d(int G) {
+KernFn pick_reduce_group_d(int G) {
   switch (G) {
-    case 1: return attn_reduce_shared_kernel<D, 1>;
-    case 2: return attn_reduce_shared_kernel<D, 2>;
-    case 4: return attn_reduce_shared_kernel<D, 4>;
-    case 8: return attn_reduce_shared_kernel<D, 8>;
+    case 1: return attn_reduce_group_kernel<D, 1>;
+    case 2: return attn_reduce_group_kernel<D, 2>;
+    case 4: return attn_reduce_group_kernel<D, 4>;
+    case 8: return attn_reduce_group_kernel<D, 8>;
     default: return nullptr;
   }
 }
 
 template <int D>
-KernFn pick_shared_d(int fmt) {
+KernFn pick_group_d(int fmt) {
   switch (fmt) {
-    case kF16: return attn_shared_mfma_kernel<D, kF16, kWaves>;
-    case kE4M3: return attn_shared_mfma_kernel<D, kE4M3, kWaves>;
-    case kE5M2: return attn_shared_mfma_kernel<D, kE5M2, kWaves>;
+    case kF16: return attn_group_mfma_kernel<D, kF16, kWaves>;
+    case kE4M3: return attn_group_mfma_kernel<D, kE4M3, kWaves>;
+    case kE5M2: return attn_group_mfma_kernel<D, kE5M2, kWaves>;
     default: return nullptr;
   }
 }
 
-// (shared pass, merge) kernels of paged_attn_decode_shared
-bool pick_shared(int D, int G, int fmt, KernFn* shared, KernFn* reduce) {
-  *shared = D == 64 ? pick_shared_d<64>(fmt) : D == 128 ? pick_shared_d<128>(fmt) : nullptr;
-  *reduce = D == 64 ? pick_reduce_shared_d<64>(G) : D == 128 ? pick_reduce_shared_d<128>(G) : nullptr;
-  return *shared && *reduce;
+// (grouped pass 1, merge) kernels of paged_attn_decode_shared
+bool pick_group(int D, int G, int fmt, KernFn* pass1, KernFn* reduce) {
+  *pass1 = D == 64 ? pick_group_d<64>(fmt) : D == 128 ? pick_group_d<128>(fmt) : nullptr;
+  *reduce = D == 64 ? pick_reduce_group_d<64>(G) : D == 128 ? pick_reduce_group_d<128>(G) : nullptr;
+  return *pass1 && *reduce;
 }
 
 int log2_exact(int v) {
@@ -902,6 +710,7 @@ int log2_exact(int v) {
 
 int unit_tokens_for(int group) { return group >= 4 ? 32 : kTile; }
 
+// pt[B + 1] and scan[blockDim]; the grouped pass 1 adds the part records [B]
 size_t dyn_lds_bytes(int B, bool groups = false) {
   return (size_t)(B + 1 + kWaves * 64 + (groups ? B : 0)) * sizeof(int);
 }
@@ -967,8 +776,7 @@ struct Plan {
 // Validates the shape and picks the kernels and the worker count; returns a
 // status code.
 int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-         int max_blocks_per_seq, int kv_dtype, int partition_tokens, bool need_workers, Plan* p,
-         bool groups = false) {
+         int max_blocks_per_seq, int kv_dtype, int partition_tokens, bool need_workers, Plan* p) {
   if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
@@ -995,7 +803,7 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
     W = (ub_all + per - 1) / per;
   } else {
     int wgs = 0, cus = 0;
-    if (!device_capacity(p->fn, dyn_lds_bytes(B, groups), &wgs, &cus)) return PKV_ERR_HIP;
+    if (!device_capacity(p->fn, dyn_lds_bytes(B), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
     const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype != PKV_KV_F16) * 4 * cus;
     if (W > by_simd) W = by_simd;
@@ -1040,62 +848,56 @@ namespace pkv {
 namespace {
 
 // Workspace of paged_attn_decode_shared, byte offsets of its regions (each
-// 256-byte aligned): pass-1 slots and unit prefix as paged_attn_decode's,
-// then the merge buffers of whole pieces, the shared pass's slots and its
-// unit prefix over the groups.
-struct SharedLayout {
-  size_t o, ml, pt, wo, wml, swo, swml, so, sml, spt, gid, total;
+// 256-byte aligned): the grouped pass 1's slots ([kMaxGroupWorkers][2]
+// [kGroupCols] columns of D outputs, then of (max, sum)), the unit prefix
+// over the sequences and their part records. Without groups the call is
+// paged_attn_decode's, so the total also covers that workspace.
+struct GroupLayout {
+  size_t o, ml, pt, part, total;
 };
 
-SharedLayout shared_layout(int B, int Hq, int Hkv, int D) {
-  const size_t G = (size_t)(Hq / Hkv);
-  const size_t rows = (size_t)B * Hq;
-  SharedLayout L;
+GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
+  GroupLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = (off + bytes + 255) / 256 * 256;
     return at;
   };
-  L.o = take((size_t)kMaxWorkers * 2 * G * D * sizeof(float));
-  L.ml = take((size_t)kMaxWorkers * 2 * G * 2 * sizeof(float));
+  const size_t cols = (size_t)kMaxGroupWorkers * 2 * kGroupCols;
+  L.o = take(cols * D * sizeof(float));
+  L.ml = take(cols * 2 * sizeof(float));
   L.pt = take((size_t)(B + 1) * sizeof(int32_t));
-  L.wo = take(rows * D * sizeof(float));
-  L.wml = take(rows * 2 * sizeof(float));
-  L.swo = take(rows * D * sizeof(float));
-  L.swml = take(rows * 2 * sizeof(float));
-  L.so = take((size_t)kMaxSharedWorkers * 2 * kSharedCols * D * sizeof(float));
-  L.sml = take((size_t)kMaxSharedWorkers * 2 * kSharedCols * 2 * sizeof(float));
-  L.spt = take((size_t)(B + 1) * sizeof(int32_t));
-  L.gid = take((size_t)B * sizeof(int32_t));
-  L.total = off;
+  L.part = take((size_t)B * sizeof(int32_t));
+  const size_t plain = paged_attn_decode_workspace_bytes(B, Hq, Hkv, D, 1, 16, 0);
+  L.total = off > plain ? off : plain;
   return L;
 }
 
-// Dynamic LDS of the shared pass: unit prefix, scan space, three per-group arrays.
-size_t shared_lds_bytes(int NG) { return (size_t)(4 * NG + 1 + kWaves * 64) * sizeof(int); }
-
-// Workers of the shared pass: two per SIMD (a kSharedCols-column tile keeps
-// about 200 registers per lane), within what the device holds at once; with
-// partition_tokens, about that many tokens each of the largest shared unit
-// space the groups can describe.
-int shared_workers(KernFn fn, int B, int NG, int Hkv, int G, int max_blocks, int block_size,
-                   int partition_tokens, int* W_out) {
+// Workers of the grouped pass 1: one per SIMD (its 32-column tiles and
+// several units of loads in flight keep about 300 registers per lane; two
+// per SIMD measured slower for fp8 as well), within what the device holds at
+// once; with partition_tokens, about that
+// many tokens each of the largest unit space the batch can describe (every
+// sequence's tail plus a part's shared units, each at most the table width,
+// and a part's setup charge).
+int group_workers(KernFn fn, int B, int Hkv, int max_blocks, int block_size, int kv_dtype, int partition_tokens,
+                  int* W_out) {
   const int64_t max_units = ((int64_t)max_blocks * block_size + 31) / 32;
-  const int64_t parts = (int64_t)NG + ((int64_t)B * G + kSharedCols - 1) / kSharedCols;
-  const int64_t ub = (int64_t)Hkv * parts * max_units;
+  const int64_t ub = (int64_t)Hkv * B * (2 * max_units + kPieceCost);
   int64_t W;
   if (partition_tokens > 0) {
     const int64_t per = (partition_tokens + 31) / 32;
     W = (ub + per - 1) / per;
   } else {
     int wgs = 0, cus = 0;
-    if (!device_capacity(fn, shared_lds_bytes(NG), &wgs, &cus)) return PKV_ERR_HIP;
+    if (!device_capacity(fn, dyn_lds_bytes(B, true), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
-    if (W > (int64_t)2 * 4 * cus) W = (int64_t)2 * 4 * cus;
+    const int64_t by_simd = (int64_t)4 * cus;
+    if (W > by_simd) W = by_simd;
   }
   if (W > ub) W = ub;
-  if (W > kMaxSharedWorkers) W = kMaxSharedWorkers;
+  if (W > kMaxGroupWorkers) W = kMaxGroupWorkers;
   if (W < kWaves) W = kWaves;
   *W_out = (int)(W / kWaves * kWaves);
   return PKV_OK;
@@ -1304,7 +1106,7 @@ extern "C" size_t paged_attn_decode_shared_workspace_bytes(int num_seqs, int num
       num_q_heads % num_kv_heads != 0)
     return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
-  return pkv::shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
+  return pkv::group_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
 }
 
 extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -1325,8 +1127,8 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
                 partition_tokens, false, &pl);
   if (rc != PKV_OK) return rc;
   const int G = num_q_heads / num_kv_heads;
-  KernFn shared_fn, reduce_fn;
-  if (!pick_shared(head_dim, G, kv_dtype, &shared_fn, &reduce_fn)) return PKV_ERR_INVALID;
+  KernFn group_fn, reduce_fn;
+  if (!pick_group(head_dim, G, kv_dtype, &group_fn, &reduce_fn)) return PKV_ERR_INVALID;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens) return PKV_ERR_INVALID;
   if (num_groups > 0 && (!group_first || !group_size || !group_prefix)) return PKV_ERR_INVALID;
@@ -1335,20 +1137,26 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
       !aligned_to(k_scales, 4) || !aligned_to(v_scales, 4) || !aligned_to(group_first, 4) ||
       !aligned_to(group_size, 4) || !aligned_to(group_prefix, 4))
     return PKV_ERR_INVALID;
-  const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  const GroupLayout lay = group_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_INVALID;
-  rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
-            partition_tokens, true, &pl, num_groups > 0);
-  if (rc != PKV_OK) return rc;
-  int s_workers = kWaves;
-  if (num_groups > 0) {
-    rc = shared_workers(shared_fn, num_seqs, num_groups, num_kv_heads, G, max_blocks_per_seq, block_size,
-                        partition_tokens, &s_workers);
-    if (rc != PKV_OK) return rc;
-  }
-
   const bool fp8 = kv_dtype != PKV_KV_F16;
   const bool per_head = fp8 && k_scales != nullptr;
+  if (num_groups == 0) {  // nothing shared: paged_attn_decode itself, the same bits
+    const int p = ((passes & 3) ? 1 : 0) | ((passes & 4) ? 2 : 0);
+    return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale, kv_dtype, k_scale,
+                       v_scale, per_head ? k_scales : nullptr, per_head ? v_scales : nullptr, partition_tokens,
+                       workspace, workspace_bytes, p, stream);
+  }
+  // every unit of the batch (tail, shared units and setup charge of one part
+  // per sequence at most) must fit the int32 prefix
+  if ((int64_t)num_seqs * (2 * (((int64_t)max_blocks_per_seq * block_size + 31) / 32) + kPieceCost) > 0x7FFFFFFF)
+    return PKV_ERR_INVALID;
+  int W = kWaves;
+  rc = group_workers(group_fn, num_seqs, num_kv_heads, max_blocks_per_seq, block_size, kv_dtype, partition_tokens,
+                     &W);
+  if (rc != PKV_OK) return rc;
+
   const float kLog2e = 1.4426950408889634f;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   AttnArgs a;
@@ -1360,6 +1168,7 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   a.ws_o = reinterpret_cast<float*>(ws + lay.o);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a.ws_pt = reinterpret_cast<int32_t*>(ws + lay.pt);
+  a.ws_part = reinterpret_cast<int32_t*>(ws + lay.part);
   a.out = static_cast<f16*>(out);
   a.max_blocks = max_blocks_per_seq;
   a.B = num_seqs;
@@ -1367,8 +1176,8 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   a.Hq = num_q_heads;
   a.bs_log2 = log2_exact(block_size);
   a.num_blocks = num_blocks;
-  a.unit_tokens = pl.unit;
-  a.workers = pl.workers;
+  a.unit_tokens = 32;
+  a.workers = W;
   a.qk_scale = sm_scale * kLog2e * (fp8 && !per_head ? k_scale : 1.0f);
   a.v_out_scale = fp8 && !per_head ? v_scale : 1.0f;
   a.k_scale_h = per_head ? k_scales : nullptr;
@@ -1379,24 +1188,10 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   a.grp_prefix = group_prefix;
   a.NG = num_groups;
   a.g_log2 = log2_exact(G);
-  a.s_workers = s_workers;
-  a.ws_wo = reinterpret_cast<float*>(ws + lay.wo);
-  a.ws_wml = reinterpret_cast<float*>(ws + lay.wml);
-  a.ws_swo = reinterpret_cast<float*>(ws + lay.swo);
-  a.ws_swml = reinterpret_cast<float*>(ws + lay.swml);
-  a.ws_so = reinterpret_cast<float*>(ws + lay.so);
-  a.ws_sml = reinterpret_cast<float*>(ws + lay.sml);
-  a.ws_spt = reinterpret_cast<int32_t*>(ws + lay.spt);
-  a.ws_gid = reinterpret_cast<int32_t*>(ws + lay.gid);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((passes & 1) && num_groups > 0) {
-    hipLaunchKernelGGL(shared_fn, dim3((unsigned)(s_workers / kWaves)), dim3(kWaves * 64),
-                       shared_lds_bytes(num_groups), s, a);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
-  }
-  if (passes & 2) {
-    hipLaunchKernelGGL(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64),
-                       dyn_lds_bytes(num_seqs, num_groups > 0), s, a);
+  if (passes & 3) {
+    hipLaunchKernelGGL(group_fn, dim3((unsigned)(W / kWaves)), dim3(kWaves * 64), dyn_lds_bytes(num_seqs, true), s,
+                       a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   if (passes & 4) {

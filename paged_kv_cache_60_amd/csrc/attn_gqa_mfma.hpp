@@ -80,8 +80,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
   __shared__ __align__(16) _Float16 vlds[NW * 32 * VS];
   extern __shared__ int dyn_smem[];
   int* pt = dyn_smem;
-  int* pre = pt + a.B + 1 + NW * 64;
-  build_prefix(a, pt, pt + a.B + 1, pre);
+  build_prefix(a, pt, pt + a.B + 1);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -112,9 +111,6 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
     const int L = wave_uniform(seq_len(a, seq));
-    // a member of a shared-prefix group starts after the shared tokens
-    const int sgrp = a.NG ? wave_uniform(pre[seq]) : -1;  // >= 0 for a group member
-    const int base = private_start(sgrp, L);
     const float qk_scale = head_qk_scale(a, pc.head);
     const float v_scale = head_v_scale(a, pc.head);
 
@@ -144,12 +140,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
       int my_blk = -1;
       {
         const int jj = j0 + (lane >> 1);
-        const int tt = base + 32 * jj + 16 * (lane & 1);
+        const int tt = 32 * jj + 16 * (lane & 1);
         if (jj < pc.u1 && tt < L) my_blk = tab[tt >> a.bs_log2];
       }
       const int nj = min(32, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
-        const int ta = base + 32 * (j0 + j);
+        const int ta = 32 * (j0 + j);
         const int blk_a = __builtin_amdgcn_readlane(my_blk, 2 * j);
         const int blk_b = __builtin_amdgcn_readlane(my_blk, 2 * j + 1);
         const bool ok_a = (unsigned)blk_a < (unsigned)a.num_blocks;
@@ -276,7 +272,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const bool whole = pc.u0 == 0 && pc.u1 == pc.n_u;
     const int slot = t == start ? 0 : 1;
     if (col < G) {
-      if (whole && sgrp < 0) {
+      if (whole) {
         const float sc = l_part > 0.0f ? v_scale / l_part : 0.0f;
         f16* orow = a.out + ((size_t)seq * a.Hq + hq0 + col) * D + 4 * grp;
 #pragma unroll
@@ -287,15 +283,13 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           *reinterpret_cast<f16x4*>(orow + 16 * c) = h;
         }
       } else {
-        // a group member's whole segment goes to the buffer the merge reads
-        const size_t pi = whole ? (size_t)seq * a.Hq + hq0 + col : ((size_t)w * 2 + slot) * G + col;
-        float* orow = (whole ? a.ws_wo : a.ws_o) + pi * D + 4 * grp;
-        float* ml = whole ? a.ws_wml : a.ws_ml;
+        const size_t pi = ((size_t)w * 2 + slot) * G + col;
+        float* orow = a.ws_o + pi * D + 4 * grp;
 #pragma unroll
         for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * v_scale;
         if (grp == 0) {
-          ml[2 * pi] = m_run;
-          ml[2 * pi + 1] = l_part;
+          a.ws_ml[2 * pi] = m_run;
+          a.ws_ml[2 * pi + 1] = l_part;
         }
       }
     }

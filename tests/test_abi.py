@@ -135,10 +135,11 @@ def test_shared_workspace_bytes():
     lib = _lib.load()
 
     def expect(b, hq, hkv, d):
-        g, rows = hq // hkv, b * hq
-        regions = [8192 * 2 * g * d * 4, 8192 * 2 * g * 2 * 4, (b + 1) * 4, rows * d * 4, rows * 2 * 4,
-                   rows * d * 4, rows * 2 * 4, 2048 * 2 * 32 * d * 4, 2048 * 2 * 32 * 2 * 4, (b + 1) * 4, b * 4]
-        return sum(-(-n // 256) * 256 for n in regions)
+        # grouped pass-1 slots for 2048 workers x 2 x 32 columns, the unit prefix and
+        # the part records (256-aligned each), and at least paged_attn_decode's workspace
+        regions = [2048 * 2 * 32 * d * 4, 2048 * 2 * 32 * 2 * 4, (b + 1) * 4, b * 4]
+        grouped = sum(-(-n // 256) * 256 for n in regions)
+        return max(grouped, lib.paged_attn_decode_workspace_bytes(b, hq, hkv, d, 1, 16, 0))
     f = lib.paged_attn_decode_shared_workspace_bytes
     assert f(128, 64, 8, 128) == expect(128, 64, 8, 128)
     assert f(256, 16, 8, 128) == expect(256, 16, 8, 128)
