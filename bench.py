@@ -585,9 +585,12 @@ def main():
                     help="time paged_block_swap (preemption by swapping, 16 sequences of the Llama-2-7B batch)")
     ap.add_argument("--scatter", action="store_true",
                     help="time paged_kv_write (fp16 and e4m3, 65 536 tokens) and paged_block_copy (2048 pairs)")
-    ap.add_argument("--shared", action="store_true",
+    ap.add_argument("--shared", dest="shared", action="store_true", default=None,
                     help="attend with paged_attn_decode_shared: runs of the batch that share leading blocks "
-                         "(beams of one prompt, a common prefix) read them once")
+                         "(beams of one prompt, a common prefix) read them once (default: when the block "
+                         "manager finds such runs)")
+    ap.add_argument("--no-shared", dest="shared", action="store_false",
+                    help="attend with paged_attn_decode even where sequences share blocks")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one plain 256 MiB device copy (known bytes, for counter scaling)")
     args = ap.parse_args()
@@ -640,7 +643,10 @@ def main():
                                  wl.max_blocks_per_seq, wl.kv_dtype, args.partition)
     group = wl.num_q_heads // wl.num_kv_heads
     kernel = "attn_partition_mfma_kernel" if group >= 4 else "attn_partition_kernel"
-    if args.shared:
+    shared = eng.groups is not None
+    if shared:
+        # the grouped pass 1 runs one worker (wave) per SIMD
+        workers = 4 * torch.cuda.get_device_properties(0).multi_processor_count
         # one grouped pass 1 over every sequence: each group's shared blocks once, then the members' tails
         kernel = "attn_group_mfma_kernel"
         log(f"bench: {eng.groups.shape[1]} shared-prefix groups")
@@ -721,7 +727,7 @@ def main():
     p1_avg_s = sum(p1_ms) / len(p1_ms) / 1e3
     achieved = (sum(p1_bytes) / len(p1_bytes)) / p1_avg_s / 1e9
     achieved_logical = (sum(p1_bytes_logical) / len(p1_bytes_logical)) / p1_avg_s / 1e9
-    traffic = load_counters(wl.name + ("_shared" if args.shared else ""))
+    traffic = load_counters(wl.name + ("_shared" if shared else ""))
 
     result = {
         "metric": METRIC,
@@ -741,7 +747,7 @@ def main():
             "mean_ctx_len": round(float(np.mean([c.mean() for c in ctx_steps])), 1),
             "partition_tokens": args.partition,
             "attention_workers": workers,
-            "shared_prefix_groups": int(eng.groups.shape[1]) if args.shared else 0,
+            "shared_prefix_groups": int(eng.groups.shape[1]) if shared else 0,
             "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
         },
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),

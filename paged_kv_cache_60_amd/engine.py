@@ -146,14 +146,16 @@ class PagedKVEngine:
                            self.k_inv_scale, self.v_inv_scale)
 
     # ------------------------------------------------------ decode steps
-    def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0, shared_prefix=False):
+    def prepare_steps(self, batch_seqs, max_blocks, partition_tokens=0, shared_prefix=None):
         """Set up a decode batch: device-resident block tables (uploaded once
         here), the per-step metadata buffers (two pinned halves on the host,
         one set on the device) and the attention workspace. shared_prefix:
         find the runs of the batch that share leading full blocks (forked
         beams, common prefixes) and attend with paged_attn_decode_shared,
         which reads those blocks once per run; decode steps only append, so
-        the runs stay valid until the batch is set up again."""
+        the runs stay valid until the batch is set up again. None (default):
+        do so when the block manager finds a run of two or more sequences
+        sharing at least one 32-token unit; True / False force either call."""
         torch.cuda.synchronize(self.device)  # queued kernels may still read the previous buffers
         B = len(batch_seqs)
         self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
@@ -181,6 +183,8 @@ class PagedKVEngine:
         self.tables_dev = torch.from_numpy(tab).to(self.device)
         self.ctx_dev.copy_(torch.from_numpy(ctx))
         self.groups = None
+        if shared_prefix is None:
+            shared_prefix = B <= ops.SHARED_MAX_SEQS and self._sharing_found()
         if shared_prefix:
             g = self.bm.prefix_groups(self.batch, ops.SHARED_COLUMNS // (self.hq // self.hkv))
             self.groups = torch.from_numpy(np.ascontiguousarray(g)).to(self.device)
@@ -189,6 +193,12 @@ class PagedKVEngine:
             wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
         torch.cuda.synchronize(self.device)
+
+    def _sharing_found(self) -> bool:
+        """Whether the batch holds a run of sequences sharing leading blocks
+        worth reading once (two or more members, 32 or more shared tokens)."""
+        g = self.bm.prefix_groups(self.batch, ops.SHARED_COLUMNS // (self.hq // self.hkv))
+        return bool(((g[1] >= 2) & (g[2] >= 32)).any()) if g.shape[1] else False
 
     def host_step(self):
         """Step part 1: host bookkeeping into the next pinned slot.

@@ -267,9 +267,11 @@ def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, ctx_lens, 
                                                 float(v_scale), int(partition_tokens), _stream_ptr(stream)), w)
 
 
-# query columns (sequence, query head) of one pass over a group's shared blocks;
-# a group of more than SHARED_COLUMNS / G members takes several passes
+# query columns (sequence, query head) of one part of a group: the columns
+# that one read of the group's shared blocks serves; a group of more than
+# SHARED_COLUMNS / G members is cut into several parts
 SHARED_COLUMNS = 32
+SHARED_MAX_SEQS = 4096  # paged_attn_decode_shared takes batches up to this size
 
 
 def shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) -> int:
