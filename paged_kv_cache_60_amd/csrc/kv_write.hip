@@ -21,40 +21,30 @@
 namespace pkv {
 namespace {
 
-// fp8 byte for a float, without branches: round to nearest even, saturate
-// (an infinite input too), keep the sign of zero, NaN -> 0x7F. In the normal
-// range the float's mantissa is rounded to M bits on its bit pattern (adding
-// half an ulp of the kept part, less one, plus the lowest kept bit carries
-// into the exponent exactly when the rounded value reaches the next binade);
-// below the smallest normal 2^(1-BIAS) the value is a multiple of the
-// subnormal step 2^(1-BIAS-M), and rint of the exact scaled value rounds it.
-template <int M, int BIAS>
-__device__ __forceinline__ uint32_t fp8_rne_sat(float f, float max_finite, uint32_t max_code) {
-  const uint32_t sign = (__builtin_bit_cast(uint32_t, f) >> 24) & 0x80u;
-  const float a = __builtin_fabsf(f);
-  const uint32_t ua = __builtin_bit_cast(uint32_t, a);
-  constexpr int DROP = 23 - M;  // fp32 mantissa bits dropped
-  const uint32_t r = ua + ((1u << (DROP - 1)) - 1u) + ((ua >> DROP) & 1u);
-  const uint32_t normal = (((r >> 23) - (uint32_t)(127 - BIAS)) << M) | ((r >> DROP) & ((1u << M) - 1u));
-  const float min_normal = __builtin_ldexpf(1.0f, 1 - BIAS);
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * __builtin_ldexpf(1.0f, BIAS - 1 + M));
-  uint32_t code = a < min_normal ? sub : normal;
-  code = a >= max_finite ? max_code : code;
-  return a == a ? (sign | code) : 0x7Fu;
-}
-
-// e4m3fn: bias 7, 3 mantissa bits, largest finite 448 (0x7E)
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float f) { return fp8_rne_sat<3, 7>(f, 448.0f, 0x7Eu); }
-
-// e5m2: bias 15, 2 mantissa bits, largest finite 57344 (0x7B)
-__device__ __forceinline__ uint32_t e5m2_rne_sat(float f) { return fp8_rne_sat<2, 15>(f, 57344.0f, 0x7Bu); }
-
+// Four fp8 bytes (value j in byte j) for four floats: round to nearest even,
+// saturate (an infinite input too), keep the sign of zero, NaN -> 0x7F.
+// gfx950's packed conversion (two floats per instruction, OCP e4m3fn or e5m2)
+// rounds to nearest even but does not saturate -- past the largest finite
+// value it gives NaN (e4m3) or infinity (e5m2) -- so the inputs are clamped to
+// +-max first (a value between max and the next half step rounds to max
+// either way), and its NaN code is replaced by 0x7F. Equal to the plain
+// bit-pattern definition of both formats on every fp16 input at several
+// scales (checked on the device against that definition and the oracle).
 template <int FMT>
-__device__ __forceinline__ uint32_t fp8_encode(float f) {
-  if constexpr (FMT == kE4M3)
-    return e4m3_rne_sat(f);
-  else
-    return e5m2_rne_sat(f);
+__device__ __forceinline__ uint32_t fp8x4_encode(float a, float b, float c, float d) {
+  constexpr float kMax = FMT == kE4M3 ? 448.0f : 57344.0f;
+  auto sat = [](float x) { return fminf(fmaxf(x, -kMax), kMax); };
+  uint32_t w;
+  if constexpr (FMT == kE4M3) {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), (int)w, true);
+  } else {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(sat(a), sat(b), 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(sat(c), sat(d), (int)w, true);
+  }
+  const uint32_t nan = (a != a ? 0x000000FFu : 0u) | (b != b ? 0x0000FF00u : 0u) | (c != c ? 0x00FF0000u : 0u) |
+                       (d != d ? 0xFF000000u : 0u);
+  return (w & ~nan) | (0x7F7F7F7Fu & nan);
 }
 
 // Step metadata applied by the write kernel of a decode step (see
@@ -116,18 +106,15 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
       const float kinv = k_inv_h ? k_inv_h[h] : k_inv;
       const float vinv = v_inv_h ? v_inv_h[h] : v_inv;
       u32x2 ko, vo;
+#pragma unroll
       for (int w = 0; w < 2; ++w) {
-        uint32_t kb = 0, vb = 0;
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t kw = kv[w * 2 + j / 2];
-          const uint32_t vw = vv[w * 2 + j / 2];
-          const float kf = (j & 1) ? h_hi(kw) : h_lo(kw);
-          const float vf = (j & 1) ? h_hi(vw) : h_lo(vw);
-          kb |= fp8_encode<FMT>(__fmul_rn(kf, kinv)) << (8 * j);
-          vb |= fp8_encode<FMT>(__fmul_rn(vf, vinv)) << (8 * j);
-        }
-        ko[w] = kb;
-        vo[w] = vb;
+        // fp16 pairs 2w, 2w + 1: values 4w .. 4w + 3, scaled in fp32
+        const uint32_t k0 = kv[2 * w], k1 = kv[2 * w + 1];
+        const uint32_t v0 = vv[2 * w], v1 = vv[2 * w + 1];
+        ko[w] = fp8x4_encode<FMT>(__fmul_rn(h_lo(k0), kinv), __fmul_rn(h_hi(k0), kinv), __fmul_rn(h_lo(k1), kinv),
+                                  __fmul_rn(h_hi(k1), kinv));
+        vo[w] = fp8x4_encode<FMT>(__fmul_rn(h_lo(v0), vinv), __fmul_rn(h_hi(v0), vinv), __fmul_rn(h_lo(v1), vinv),
+                                  __fmul_rn(h_hi(v1), vinv));
       }
       *reinterpret_cast<u32x2*>(k_cache + dst) = ko;
       *reinterpret_cast<u32x2*>(v_cache + dst) = vo;
