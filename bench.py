@@ -766,6 +766,10 @@ def main():
             "traffic": traffic,
             "kernel": kernel,
             "achieved_logical": round(achieved_logical, 2),
+            # algorithmic bytes per launch (unique K/V), over the event-timed launches and over
+            # every timed step (the average a kernel trace of the run compares with)
+            "bytes_per_launch": int(np.mean(p1_bytes)),
+            "bytes_per_launch_all_steps": int(np.mean([u[0] for u in uniq])),
         },
     }
     if not args.no_cpu_baseline:
