@@ -202,3 +202,42 @@ def test_kv_write_step_bit_exact(kv_dtype):
     assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
     assert np.array_equal(t_dev.cpu().numpy(), expect)
     assert np.array_equal(c_dev.cpu().numpy(), ctx)
+
+
+def test_debug_checks_refuse_racing_slots_and_pairs_before_queuing():
+    """With the opt-in race guards on, a slot mapping with two valid tokens on one
+    slot, or copy pairs where one pair writes another's source, raise before any
+    launch and leave the caches untouched; valid inputs still run and match the
+    oracle with the guards on."""
+    from paged_kv_cache_60_amd import guards
+    from paged_kv_cache_60_amd._lib import PkvError
+    log("debug checks: racing slots and pairs refused")
+    nb, hkv, bs, d = 8, 4, 16, 64
+    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, "f16")
+    before_k, before_v = cache_bits(g_k), cache_bits(g_v)
+    g = np.random.default_rng(7)
+    k_new = torch.from_numpy(g.standard_normal((3, hkv, d)).astype(np.float16)).to(DEV)
+    v_new = torch.from_numpy(g.standard_normal((3, hkv, d)).astype(np.float16)).to(DEV)
+    was = guards.debug_checks()
+    try:
+        guards.set_debug_checks(True)
+        dup = torch.tensor([5, 17, 5], dtype=torch.int64, device=DEV)
+        with pytest.raises(PkvError):
+            ops.paged_kv_write(k_new, v_new, g_k, g_v, dup)
+        pairs = torch.tensor([[0, 3], [3, 6]], dtype=torch.int32, device=DEV)
+        with pytest.raises(PkvError):
+            ops.paged_block_copy(g_k, g_v, pairs)
+        torch.cuda.synchronize()
+        assert np.array_equal(cache_bits(g_k), before_k) and np.array_equal(cache_bits(g_v), before_v)
+        # valid inputs pass the guards and give the oracle's bytes
+        slots = np.array([5, 17, -1], dtype=np.int64)
+        ops.paged_kv_write(k_new, v_new, g_k, g_v, torch.from_numpy(slots).to(DEV))
+        ok_pairs = np.array([[0, 3], [1, 6]], dtype=np.int32)
+        ops.paged_block_copy(g_k, g_v, torch.from_numpy(ok_pairs).to(DEV))
+        torch.cuda.synchronize()
+    finally:
+        guards.set_debug_checks(was)
+    cache_ops.scatter(o_k, o_v, k_new.cpu().numpy(), v_new.cpu().numpy(), slots, bs)
+    cache_ops.block_copy(o_k, o_v, ok_pairs)
+    assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
+    assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
