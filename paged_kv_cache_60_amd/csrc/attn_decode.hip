@@ -88,7 +88,7 @@ struct AttnArgs {
   float qk_base;      // sm_scale * log2(e)
   // Shared-prefix groups (paged_attn_decode_shared; NG = 0 otherwise). Group
   // g is the batch sequences grp_first[g] .. + grp_size[g] - 1; their first
-  // group_tokens(g) tokens are read through the table of sequence
+  // group_tokens(grp_prefix[g]) tokens are read through the table of sequence
   // grp_first[g] once for all of them (attn_group_mfma.hpp).
   const int32_t* grp_first = nullptr;
   const int32_t* grp_size = nullptr;
@@ -121,18 +121,17 @@ __device__ __forceinline__ int seq_len(const AttnArgs& a, int s) {
   return clamp_len(a.ctx_lens[s], a.max_blocks << a.bs_log2);
 }
 
-// Members of group g inside the batch (0 for an entry outside it).
-__device__ __forceinline__ int group_members(const AttnArgs& a, int g) {
-  const int f = a.grp_first[g];
-  if (f < 0 || f >= a.B) return 0;
-  const int n = a.grp_size[g];
-  return n < 0 ? 0 : min(n, a.B - f);
+// Members inside the batch of a group entry (first, size): 0 for an entry
+// outside it.
+__device__ __forceinline__ int group_members(const AttnArgs& a, int first, int size) {
+  if (first < 0 || first >= a.B) return 0;
+  return size < 0 ? 0 : min(size, a.B - first);
 }
 
-// Shared tokens of group g: a multiple of 16 (tiles never straddle the edge),
-// within the table width.
-__device__ __forceinline__ int group_tokens(const AttnArgs& a, int g) {
-  return clamp_len(a.grp_prefix[g], a.max_blocks << a.bs_log2) & ~15;
+// Shared tokens of a group entry's prefix: a multiple of 16 (tiles never
+// straddle the edge), within the table width.
+__device__ __forceinline__ int group_tokens(const AttnArgs& a, int prefix) {
+  return clamp_len(prefix, a.max_blocks << a.bs_log2) & ~15;
 }
 
 // pt[0] = 0, pt[i + 1] = pt[i] + units(i) for i < n, by all threads of the

@@ -65,17 +65,18 @@ __device__ __forceinline__ int group_seq_units(int v, int L) {
 
 // info[B]: every sequence's part record; pt[B + 1]: the unit prefix over the
 // sequences. A group of n members splits into parts of kGroupCols / G members;
-// a sequence in no group is a part of its own. The context lengths and the
-// first blockDim groups are loaded at once; ends with a barrier.
+// a sequence in no group is a part of its own. The three entries of the first
+// blockDim groups and the context lengths are all loaded before the first
+// wait (one round trip to memory, not one per array); ends with a barrier.
 __device__ void build_group_parts(const AttnArgs& a, int* pt, int* scan, int* info) {
   const int T = blockDim.x;
   const int tid = threadIdx.x;
   const int MP = kGroupCols >> a.g_log2;
-  int n0 = 0, f0 = 0, p0 = 0;
+  int f0 = -1, s0 = 0, p0 = 0;
   if (tid < a.NG) {
-    n0 = group_members(a, tid);
     f0 = a.grp_first[tid];
-    p0 = group_tokens(a, tid);
+    s0 = a.grp_size[tid];
+    p0 = a.grp_prefix[tid];
   }
   for (int i = tid; i < a.B; i += T) {
     info[i] = pack_part(0, 1, 0);
@@ -83,11 +84,11 @@ __device__ void build_group_parts(const AttnArgs& a, int* pt, int* scan, int* in
   }
   __syncthreads();
   for (int g = tid; g < a.NG; g += T) {
-    const int n = g == tid ? n0 : group_members(a, g);
-    if (n == 0) continue;
     const int f = g == tid ? f0 : a.grp_first[g];
+    const int n = group_members(a, f, g == tid ? s0 : a.grp_size[g]);
+    if (n == 0) continue;
     // past 2^20 * 16 shared tokens the rest are taken as each member's own
-    const int pre16 = min((g == tid ? p0 : group_tokens(a, g)) >> 4, (1 << 20) - 1);
+    const int pre16 = min(group_tokens(a, g == tid ? p0 : a.grp_prefix[g]) >> 4, (1 << 20) - 1);
     for (int m = 0; m < n; ++m) {
       const int part = m / MP;
       info[f + m] = pack_part(pre16, min(MP, n - part * MP), m - part * MP);
@@ -169,33 +170,27 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
     const int64_t seg_end = t - u0 + n_u;
     const int64_t next_t = end < seg_end ? end : seg_end;
     const int u1 = u0 + (int)(next_t - t);
-    const float qk_scale = head_qk_scale(a, head);
-    const float v_scale = head_v_scale(a, head);
-
-    // lane m < nm: member m's context length; lane column cb*16+col -> member
-    // memc[cb], query head gh; its length against the shared tokens Lc[cb]
-    const int Lm = lane < nm ? seq_len(a, pf + lane) : 0;
+    // The piece's setup loads -- the members' lengths, the query columns and
+    // the first batch's table entries -- are all issued before the first wait
+    // (one round trip): a load behind a branch leaves the compiler unsure,
+    // where the paths join, how many loads are in flight, and the wait it puts
+    // there costs a round trip per load.
+    // lane m < nm: member m's context length (lanes past nm read the last one's)
+    const int Lraw = seq_len(a, pf + min(lane, nm - 1));
+    // lane column cb*16+col -> member memc[cb], query head gh; a column past
+    // the part's members reads the first member's query and is zeroed below
     f16x8 qb[CB][KM];
-    int memc[CB], Lc[CB];
+    int memc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int c = cb * 16 + col;
       const int m = c >> gl;
       const int gh = c & ((1 << gl) - 1);
       memc[cb] = m;
-      Lc[cb] = 0;
+      const f16* qrow = a.q + ((size_t)(pf + (m < nm ? m : 0)) * a.Hq + (head << gl) + gh) * D;
 #pragma unroll
-      for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (m < nm) {
-        Lc[cb] = min(pre, seq_len(a, pf + m));
-        const f16* qrow = a.q + ((size_t)(pf + m) * a.Hq + (head << gl) + gh) * D;
-#pragma unroll
-        for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = *reinterpret_cast<const f16x8*>(qrow + k_dim_of<ELEM>(mm, grp));
-      }
+      for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = *reinterpret_cast<const f16x8*>(qrow + k_dim_of<ELEM>(mm, grp));
     }
-    // the shortest live column's shared tokens: shared units below it need no masks
-    int Lmin_sh = pre;
-    for (int m = 0; m < nm; ++m) Lmin_sh = min(Lmin_sh, __builtin_amdgcn_readlane(Lm, m));
 
     f32x4 o[CB][NT];
     float m_run[CB], l_part[CB];
@@ -214,16 +209,17 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
       u32x4 ka[KLD], kb[KLD], vv[VLD];
     };
     // Descriptors of a batch of up to 32 units of the piece: lane l holds tile
-    // l & 1 of unit b0 + l / 2 -- its block id (-1: past its region or the
-    // piece), the unit's first token, its live member (-1: shared tokens,
-    // every column live) and the length its rows are valid below. Every region
-    // of the batch is resolved here at once, so that the loads run on across
-    // region edges without a dependent table read between them.
+    // l & 1 of unit b0 + l / 2 -- its block id (-1 or past the pool: masked),
+    // the unit's first token and its live member (-1: shared tokens,
+    // every column live; nm: none). Every region of the batch is resolved here
+    // at once, so that the loads run on across region edges without a
+    // dependent table read between them. Every lane reads a table entry (the
+    // index clamped into the row), so that the read is not behind a branch.
     struct Desc {
-      int blk, ta, mem, len;
+      int blk, ta, mem;
     };
     auto describe = [&](int b0) {
-      Desc d{-1, 0, -1, 0};
+      Desc d{-1, 0, -1};
       const int u = b0 + (lane >> 1);
       int m = -1, ts = 0;
       if (u >= US && u < u1) {
@@ -240,20 +236,44 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
           }
         }
       }
-      if (u < u1) {
-        // the table entry is read whatever the member's length (an entry past
-        // it is in the table and its rows are masked), so that this read does
-        // not wait for the lengths
-        const int row = m < 0 ? pf : pf + (m < nm ? m : 0);
-        d.ta = m < 0 ? 32 * (u - kPieceCost) : pre + 32 * (u - ts);
-        d.mem = m;
-        const int idx = min((d.ta + 16 * (lane & 1)) >> a.bs_log2, a.max_blocks - 1);
-        d.blk = a.tables[(size_t)row * a.max_blocks + idx];
-      }
-      const int Lmem = __shfl(Lm, m < 0 || m >= nm ? 0 : m, 64);
-      d.len = m < 0 ? pre : (m < nm ? Lmem : 0);
+      // the table entry is read whatever the member's length (an entry past
+      // it is in the table and its rows are masked)
+      const int row = m < 0 ? pf : pf + (m < nm ? m : 0);
+      d.ta = m < 0 ? 32 * (u - kPieceCost) : pre + 32 * (u - ts);
+      d.mem = m;
+      const int idx = min(max((d.ta + 16 * (lane & 1)) >> a.bs_log2, 0), a.max_blocks - 1);
+      // (lanes past the piece, u >= u1, are never read: a batch processes its
+      // first min(32, u1 - b0) units)
+      d.blk = a.tables[(size_t)row * a.max_blocks + idx];
       return d;
     };
+
+    // the setup loads are in flight; their uses follow
+    const int ud = max(u0, kPieceCost);  // the setup charge holds no data
+    Desc cur = describe(ud);
+    const int Lm = lane < nm ? Lraw : 0;
+    int Lc[CB];  // each column's length against the shared tokens
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int m = memc[cb];
+      const int Lmem = __shfl(Lm, m < nm ? m : 0, 64);
+      Lc[cb] = m < nm ? min(pre, Lmem) : 0;
+      if (m >= nm) {
+#pragma unroll
+        for (int mm = 0; mm < KM; ++mm) qb[cb][mm] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    // the shortest live column's shared tokens: shared units below it need no masks
+    int Lmin_sh = pre;
+    for (int m = 0; m < nm; ++m) Lmin_sh = min(Lmin_sh, __builtin_amdgcn_readlane(Lm, m));
+    // the logit and output scales of the head (both loads at once)
+    float qk_scale = a.qk_scale, v_scale = a.v_out_scale;
+    if (a.k_scale_h) {
+      const float ks = a.k_scale_h[head];
+      const float vs = a.v_scale_h[head];
+      qk_scale = a.qk_base * ks;
+      v_scale = vs;
+    }
 
     // One unit: S for the live column blocks, online softmax, V to LDS, O += P.V.
     // mact: the live member (-1: every column, each masked at its Lc); live0,
@@ -369,11 +389,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
 
     // batches of 32 units; the next batch's descriptors (table reads) are in
     // flight while the current batch streams
-    // the setup charge holds no data
-    const int ud = max(u0, kPieceCost);
-    Desc cur = describe(ud);
     for (int b0 = ud; b0 < u1; b0 += 32) {
-      const Desc nxt = b0 + 32 < u1 ? describe(b0 + 32) : Desc{-1, 0, -1, 0};
+      const Desc nxt = b0 + 32 < u1 ? describe(b0 + 32) : Desc{-1, 0, -1};
       const int nj = min(32, u1 - b0);
       auto issue = [&](int j, Ld& d) {
         const int ta = __builtin_amdgcn_readlane(cur.ta, 2 * j);
@@ -399,7 +416,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
       auto unit = [&](const Ld& d, int j) {
         const int ta = __builtin_amdgcn_readlane(cur.ta, 2 * j);
         const int mem = __builtin_amdgcn_readlane(cur.mem, 2 * j);
-        const int len = __builtin_amdgcn_readlane(cur.len, 2 * j);
+        // rows are valid below the shared tokens, the live member's length, or
+        // nowhere (no member)
+        const int len = mem < 0 ? pre : (mem < nm ? __builtin_amdgcn_readlane(Lm, mem) : 0);
         const bool ok_a = (unsigned)__builtin_amdgcn_readlane(cur.blk, 2 * j) < (unsigned)a.num_blocks;
         const bool ok_b = (unsigned)__builtin_amdgcn_readlane(cur.blk, 2 * j + 1) < (unsigned)a.num_blocks;
         // a member's columns lie in one 16-column block

@@ -65,7 +65,12 @@ struct StepMeta {
 // One grid row (blockIdx.y) per KV head; along x, the threads take the
 // head's 16-byte chunks (8 elements) token by token: chunk c of token t is
 // i = t * cpr + c with cpr = head_dim / 8 a power of two, so the index math is
-// shifts and masks (block_size is a power of two too).
+// shifts and masks (block_size is a power of two too). With META, grid row 0
+// also copies item i of the context lengths and applies item i of the table
+// updates. Every load of an iteration (the slot, the K and V chunks, the
+// metadata items; the slots and metadata may sit in host memory) is issued
+// before the first store, so an iteration costs one round trip, not a chain
+// of them.
 template <int FMT, bool META>
 __global__ void __launch_bounds__(256)
 kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
@@ -75,36 +80,57 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
                 const float* __restrict__ k_inv_h, const float* __restrict__ v_inv_h, StepMeta meta) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (META && blockIdx.y == 0) {
-    for (int64_t i = gtid; i < meta.n_ctx; i += stride) meta.ctx_dst[i] = meta.ctx_src[i];
-    for (int64_t k = gtid; k < meta.n_updates; k += stride) {
-      const int row = meta.updates[3 * k];
-      const int idx = meta.updates[3 * k + 1];
-      if (row >= 0 && row < meta.rows && idx >= 0 && idx < meta.max_blocks)
-        meta.tables[(int64_t)row * meta.max_blocks + idx] = meta.updates[3 * k + 2];
-    }
-  }
   const int h = blockIdx.y;
   const int cpr = 1 << cpr_log2;
   const int64_t n = num_tokens << cpr_log2;  // this head's chunks
-  for (int64_t i = gtid; i < n; i += stride) {
+  const bool meta_row = META && h == 0;
+  const int64_t n_meta = meta_row ? (meta.n_ctx > meta.n_updates ? meta.n_ctx : meta.n_updates) : 0;
+  const int64_t n_all = n > n_meta ? n : n_meta;
+  float kinv = k_inv, vinv = v_inv;
+  if (FMT != kF16 && k_inv_h) {
+    kinv = k_inv_h[h];
+    vinv = v_inv_h[h];
+  }
+  for (int64_t i = gtid; i < n_all; i += stride) {
+    // loads
+    const bool do_ctx = meta_row && i < meta.n_ctx;
+    const bool do_upd = meta_row && i < meta.n_updates;
+    int ctx = 0, row = -1, idx = -1, blk = 0;
+    if (do_ctx) ctx = meta.ctx_src[i];
+    if (do_upd) {
+      row = meta.updates[3 * i];
+      idx = meta.updates[3 * i + 1];
+      blk = meta.updates[3 * i + 2];
+    }
+    const bool chunk = i < n;
     const int64_t t = i >> cpr_log2;
     const int ch = (int)i & (cpr - 1);
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot >> bs_log2;
-    const int off = (int)slot & ((1 << bs_log2) - 1);
     const int64_t src = (t * num_kv_heads + h) * cpr + ch;  // chunk index in k_new / v_new
+    int64_t slot = -1;
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+    if (chunk) {
+      slot = slots[t];
+      kv = k_new[src];
+      vv = v_new[src];
+      // keeps the three loads ahead of the slot test below (the compiler would
+      // otherwise move the K/V loads behind it, or the test between them, and
+      // wait for the slot first): the test reads the slot only through this
+      // statement, which needs the K/V data
+      asm volatile("" : "+v"(slot) : "v"(kv), "v"(vv));
+    }
+    // stores
+    if (do_ctx) meta.ctx_dst[i] = ctx;
+    if (do_upd && row >= 0 && row < meta.rows && idx >= 0 && idx < meta.max_blocks)
+      meta.tables[(int64_t)row * meta.max_blocks + idx] = blk;
+    if (!chunk || slot < 0 || slot >= num_slots) continue;
+    const int64_t blk_id = slot >> bs_log2;
+    const int off = (int)slot & ((1 << bs_log2) - 1);
     // element index of the destination chunk
-    const int64_t dst = ((((blk * num_kv_heads + h) << bs_log2) + off) << (cpr_log2 + 3)) + (int64_t)ch * 8;
-    const u32x4 kv = k_new[src];
-    const u32x4 vv = v_new[src];
+    const int64_t dst = ((((blk_id * num_kv_heads + h) << bs_log2) + off) << (cpr_log2 + 3)) + (int64_t)ch * 8;
     if constexpr (FMT == kF16) {
       *reinterpret_cast<u32x4*>(k_cache + dst * 2) = kv;
       *reinterpret_cast<u32x4*>(v_cache + dst * 2) = vv;
     } else {
-      const float kinv = k_inv_h ? k_inv_h[h] : k_inv;
-      const float vinv = v_inv_h ? v_inv_h[h] : v_inv;
       u32x2 ko, vo;
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
