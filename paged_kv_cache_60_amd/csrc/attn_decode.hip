@@ -273,9 +273,16 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
     const Piece pc = locate(pt, a.B, P, t, end);
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
-    const int L = wave_uniform(seq_len(a, seq));
-    const float qk_scale = head_qk_scale(a, pc.head);
-    const float v_scale = head_v_scale(a, pc.head);
+    // The piece's setup loads (its length, the query fragments, the first 64
+    // tiles' block ids) are all issued before the first wait: one round trip.
+    const int L_raw = seq_len(a, seq);
+    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
+    // lane l: the block of tile u0 + l (lanes past the piece read an entry
+    // inside the row that no tile uses)
+    auto tile_block = [&](int j0) {
+      return tab[min(((j0 + lane) * kTile) >> a.bs_log2, a.max_blocks - 1)];
+    };
+    int my_blk = tile_block(pc.u0);
 
     // Query fragments: head hq0+g, elements c*E .. c*E+E-1, as fp16 pairs.
     uint32_t qf[G][W];
@@ -293,6 +300,16 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
         }
     }
 
+    // the logit and output scales of the head (both loads at once)
+    float qk_scale = a.qk_scale, v_scale = a.v_out_scale;
+    if (a.k_scale_h) {
+      const float ks = a.k_scale_h[pc.head];
+      const float vs = a.v_scale_h[pc.head];
+      qk_scale = a.qk_base * ks;
+      v_scale = vs;
+    }
+    const int L = wave_uniform(L_raw);
+
     float m[G], l[G], acc[G][E];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -302,14 +319,12 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
       for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
     }
 
-    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
     const uint8_t* kc_head = a.kc + (size_t)pc.head * head_bytes;
     const uint8_t* vc_head = a.vc + (size_t)pc.head * head_bytes;
     for (int j0 = pc.u0; j0 < pc.u1; j0 += 64) {
       // block ids of up to 64 tiles, one per lane, fetched together so that
-      // no tile waits on its own table read
-      int my_blk = -1;
-      if (j0 + lane < pc.u1) my_blk = tab[((j0 + lane) * kTile) >> a.bs_log2];
+      // no tile waits on its own table read (the first 64 with the setup)
+      if (j0 != pc.u0) my_blk = tile_block(j0);
       const int nj = min(64, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
         const int blk = __builtin_amdgcn_readlane(my_blk, j);
