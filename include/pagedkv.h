@@ -184,8 +184,10 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  *   out            device, fp16 [num_seqs][num_q_heads][head_dim]
  *   q              device, fp16 [num_seqs][num_q_heads][head_dim]
  *   block_tables   device, int32 [num_seqs][max_blocks_per_seq]; entries past
- *                  ceil(ctx_len/block_size) are never read; entries outside
- *                  [0, num_blocks) are never followed (their tokens are skipped).
+ *                  ceil(ctx_len/block_size) are ignored (they may be read,
+ *                  as every entry of the row must be readable, but their
+ *                  values never matter); entries outside [0, num_blocks) are
+ *                  never followed (their tokens are skipped).
  *   ctx_lens       device, int32 [num_seqs], tokens to attend (includes the
  *                  token written this step). Clamped to
  *                  [0, max_blocks_per_seq*block_size]; 0 gives a zero output.
@@ -347,7 +349,7 @@ int paged_attn_decode_shared(void* out, const void* q, const void* k_cache, cons
  *   out, q         device, fp16 [total_q][num_q_heads][head_dim]; rows of
  *                  sequence s at q_start[s] .. q_start[s+1]-1
  *   block_tables   device, int32 [num_seqs][max_blocks_per_seq], as in
- *                  paged_attn_decode (entries past ceil(L/bs) never read,
+ *                  paged_attn_decode (entries past ceil(L/bs) ignored,
  *                  ids outside [0, num_blocks) never followed: their tokens
  *                  are skipped)
  *   ctx_lens       device, int32 [num_seqs]; clamped to

@@ -110,20 +110,37 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     const Piece pc = locate(pt, a.B, P, t, end);
     const int seq = pc.seq;
     const int hq0 = pc.head * G;
-    const int L = wave_uniform(seq_len(a, seq));
-    const float qk_scale = head_qk_scale(a, pc.head);
-    const float v_scale = head_v_scale(a, pc.head);
+    // The piece's setup loads (its length, the query columns, the first 32
+    // units' block ids, the head's scales) are all issued before the first
+    // wait: one round trip.
+    const int L_raw = seq_len(a, seq);
+    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
+    // lane l: tile l & 1 of unit j0 + l / 2; read whatever the length (the
+    // index kept inside the row), tiles past the sequence are dropped below
+    auto unit_block = [&](int j0) {
+      const int tt = 32 * (j0 + (lane >> 1)) + 16 * (lane & 1);
+      return tab[min(tt >> a.bs_log2, a.max_blocks - 1)];
+    };
+    int blk_raw = unit_block(pc.u0);
 
     // Q^T as the B operand: head = col (zero past G), d = k_dim_of(m, grp) + slot
     f16x8 qb[KM];
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      if (col < G) {
-        const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + col) * D + k_dim_of<ELEM>(m, grp);
-        qb[m] = *reinterpret_cast<const f16x8*>(qrow);
-      } else {
-        qb[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const f16* qrow = a.q + ((size_t)seq * a.Hq + hq0 + (col < G ? col : 0)) * D + k_dim_of<ELEM>(m, grp);
+      qb[m] = *reinterpret_cast<const f16x8*>(qrow);
+    }
+    float qk_scale = a.qk_scale, v_scale = a.v_out_scale;
+    if (a.k_scale_h) {
+      const float ks = a.k_scale_h[pc.head];
+      const float vs = a.v_scale_h[pc.head];
+      qk_scale = a.qk_base * ks;
+      v_scale = vs;
+    }
+    const int L = wave_uniform(L_raw);
+    if (col >= G) {
+#pragma unroll
+      for (int m = 0; m < KM; ++m) qb[m] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
 
     f32x4 o[NT];
@@ -132,16 +149,17 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     float m_run = -INFINITY;
     float l_part = 0.0f;
 
-    const int32_t* tab = a.tables + (size_t)seq * a.max_blocks;
     const uint8_t* kc_head = a.kc + (size_t)pc.head * head_bytes;
     const uint8_t* vc_head = a.vc + (size_t)pc.head * head_bytes;
     for (int j0 = pc.u0; j0 < pc.u1; j0 += 32) {
-      // block ids of up to 32 chunks (two tiles each), one per lane
-      int my_blk = -1;
+      // block ids of up to 32 chunks (two tiles each), one per lane (the
+      // first 32 with the setup); -1 for a tile past the sequence
+      if (j0 != pc.u0) blk_raw = unit_block(j0);
+      int my_blk;
       {
         const int jj = j0 + (lane >> 1);
         const int tt = 32 * jj + 16 * (lane & 1);
-        if (jj < pc.u1 && tt < L) my_blk = tab[tt >> a.bs_log2];
+        my_blk = jj < pc.u1 && tt < L ? blk_raw : -1;
       }
       const int nj = min(32, pc.u1 - j0);
       for (int j = 0; j < nj; ++j) {
