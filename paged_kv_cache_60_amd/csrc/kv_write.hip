@@ -67,10 +67,10 @@ struct StepMeta {
 // i = t * cpr + c with cpr = head_dim / 8 a power of two, so the index math is
 // shifts and masks (block_size is a power of two too). With META, grid row 0
 // also copies item i of the context lengths and applies item i of the table
-// updates. Every load of an iteration (the slot, the K and V chunks, the
-// metadata items; the slots and metadata may sit in host memory) is issued
-// before the first store, so an iteration costs one round trip, not a chain
-// of them.
+// updates. With META every load of an iteration (the slot, the K and V
+// chunks, the metadata items; the slots and metadata may sit in host memory)
+// is issued before the first store, so an iteration costs one round trip, not
+// a chain of them.
 template <int FMT, bool META>
 __global__ void __launch_bounds__(256)
 kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
@@ -112,11 +112,14 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
       slot = slots[t];
       kv = k_new[src];
       vv = v_new[src];
-      // keeps the three loads ahead of the slot test below (the compiler would
-      // otherwise move the K/V loads behind it, or the test between them, and
-      // wait for the slot first): the test reads the slot only through this
-      // statement, which needs the K/V data
-      asm volatile("" : "+v"(slot) : "v"(kv), "v"(vv));
+      // In a decode step (META: a few tokens, one round trip decides the
+      // time) the three loads are kept ahead of the slot test below: the test
+      // reads the slot only through this statement, which needs the K/V data
+      // (else the compiler moves the K/V loads behind the test, or the test
+      // between them, and waits for the slot first). A large scatter is
+      // throughput-bound, and there the statement, which also stops the
+      // compiler from overlapping consecutive iterations, measured slower.
+      if constexpr (META) asm volatile("" : "+v"(slot) : "v"(kv), "v"(vv));
     }
     // stores
     if (do_ctx) meta.ctx_dst[i] = ctx;
