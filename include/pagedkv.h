@@ -294,30 +294,31 @@ int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, i
  * forked from one prompt ([VLLM] §3.2) or requests mapped onto the same
  * prefix-cache blocks ([VRAM] §4.2-4.4). The output is the same attention as
  * paged_attn_decode's; only the order of the sums differs.
- * Group g is the sequences first[g] .. first[g] + size[g] - 1 of the batch;
- * its first prefix[g] tokens (rounded down to a multiple of 16) are read once
- * for all its members, through the table of sequence first[g], as the
- * contraction of every member's query heads with the shared K/V on the
- * matrix cores (up to 32 query columns per pass over the shared blocks; a
- * larger group is covered by several passes). Each member's remaining tokens
- * go through paged_attn_decode's pass 1, and a last pass merges the two
- * partial softmax states of each (sequence, query head), which is exact up to
- * rounding: the softmax of a concatenation is the weighted merge of the
- * softmaxes of its parts.
+ * Group g is the sequences first[g] .. first[g] + size[g] - 1 of the batch.
+ * Its shared tokens -- the first prefix[g] (rounded down to a multiple of 16,
+ * and to no more than the first sequence's ctx_len) -- are read through the
+ * table of sequence first[g]. One pass 1 launch covers the whole batch on the
+ * matrix cores: a group is cut into parts of up to 32 query columns (members x
+ * query heads of a KV head); a part reads each shared block once for all its
+ * columns, then each member's own tokens through that member's table; a
+ * sequence in no group is a part of its own. A merge pass combines the parts
+ * that were split between workers (exact up to rounding: the softmax of a
+ * concatenation is the weighted merge of the softmaxes of its parts).
  *   group_first, group_size, group_prefix  device, int32 [num_groups]
  *                  (pkv_bm_prefix_groups computes them). Precondition: groups
  *                  ascending and disjoint, and every member maps its first
- *                  prefix tokens to the same physical blocks as the group's
- *                  first sequence. A member with fewer tokens than the prefix
+ *                  shared tokens to the same physical blocks as the group's
+ *                  first sequence. A member with fewer tokens than that
  *                  attends only to its own ctx_len of them. Entries that break
  *                  the precondition give wrong results but never an access
  *                  outside the buffers (members past the batch are dropped).
+ *                  With num_groups = 0 the call is paged_attn_decode (the
+ *                  same bits).
  *   k_scale, v_scale, k_scales, v_scales  fp8 only: per-tensor multipliers, or
  *                  one per KV head when k_scales and v_scales (device float
  *                  [num_kv_heads]) are both non-NULL.
- *   passes         bit 0: pass over the shared blocks; bit 1: pass 1 over the
- *                  members' own tokens and every other sequence; bit 2: merge.
- *                  7 = the whole call (each bit exists so a pass can be timed).
+ *   passes         bits 0 or 1: pass 1; bit 2: the merge. 7 = the whole call
+ *                  (each pass can be queued on its own to be timed).
  *   workspace      device, >= paged_attn_decode_shared_workspace_bytes(...).
  * Other arguments, shapes and errors as paged_attn_decode; num_seqs at most
  * 4096, num_groups in [0, num_seqs].

@@ -87,8 +87,11 @@ __device__ void build_group_parts(const AttnArgs& a, int* pt, int* scan, int* in
     const int f = g == tid ? f0 : a.grp_first[g];
     const int n = group_members(a, f, g == tid ? s0 : a.grp_size[g]);
     if (n == 0) continue;
-    // past 2^20 * 16 shared tokens the rest are taken as each member's own
-    const int pre16 = min(group_tokens(a, g == tid ? p0 : a.grp_prefix[g]) >> 4, (1 << 20) - 1);
+    // the shared tokens are read through the first member's table: no more
+    // of them than it holds (pt[f + 1] is still its length here); past
+    // 2^20 * 16 shared tokens the rest are taken as each member's own
+    const int pre = min(group_tokens(a, g == tid ? p0 : a.grp_prefix[g]), pt[f + 1] & ~15);
+    const int pre16 = min(pre >> 4, (1 << 20) - 1);
     for (int m = 0; m < n; ++m) {
       const int part = m / MP;
       info[f + m] = pack_part(pre16, min(MP, n - part * MP), m - part * MP);

@@ -227,3 +227,56 @@ def test_direct_repeat_calls_bit_identical():
     a = _run_direct(c, 64, 128, "fp8", 0)
     b = _run_direct(c, 64, 128, "fp8", 0)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# ---------------------------------------------------------- seeded random cases
+
+_SHAPES = [(hq, hkv, d, bs, kv) for (hq, hkv) in ((8, 8), (16, 8), (32, 8), (64, 8))
+           for d in (64, 128) for bs in (16, 32, 64) for kv in ("f16", "fp8", "fp8_e5m2")]
+
+
+def _random_spec(g, bs):
+    """A random batch: independent sequences and groups (shared full blocks,
+    members' offsets from -(prefix) to a few blocks past it, prefix argument
+    anywhere from below 16 to the full shared length)."""
+    spec = []
+    for _ in range(int(g.integers(3, 9))):
+        if g.random() < 0.4:
+            spec.append(("single", int(g.integers(0, 700))))
+        else:
+            nsh = int(g.integers(1, 12))
+            nm = int(g.integers(1, 12))
+            offs = [int(g.integers(-nsh * bs + 1, 3 * bs)) for _ in range(nm)]
+            prefix = int(g.choice([nsh * bs, nsh * bs - int(g.integers(0, bs)), int(g.integers(0, 16))]))
+            spec.append(("group", nsh, offs, max(prefix, 0)))
+    return spec
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batches_grouped_and_plain(seed):
+    """Seeded random shapes and group layouts: the grouped call (and plain
+    decode on the same caches and tables) within tolerance of the oracle at
+    three worker counts; no groups reproduces plain decode's bits."""
+    g = np.random.default_rng(1000 + seed)
+    hq, hkv, d, bs, kv = _SHAPES[int(g.integers(0, len(_SHAPES)))]
+    spec = _random_spec(g, bs)
+    c = _direct_case(2000 + seed, hq, hkv, d, bs, kv, spec, per_head=bool(kv != "f16" and g.random() < 0.5))
+    log(f"random {seed}: {hq}/{hkv} d{d} bs{bs} {kv} B={c['B']} groups={c['groups'].shape[1]}")
+    ref = oattn.decode_attention(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], bs, d ** -0.5, kv,
+                                 c["ks"], c["vs"])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    per_head = np.ndim(c["ks"]) > 0
+    ks = dev(c["ks"]) if per_head else float(c["ks"])
+    vs = dev(c["vs"]) if per_head else float(c["vs"])
+    for part in (16, 48, 0):
+        got = _run_direct(c, hq, d, kv, part)
+        assert_close_to_oracle(got, ref, kv, f"random {seed} grouped part {part}")
+        plain = torch.full((c["B"], hq, d), 5.0, dtype=torch.float16, device=DEV)
+        ops.paged_attn_decode(plain, dev(c["q"]), dev(c["kc"]), dev(c["vc"]), dev(c["tab"]),
+                              dev(np.asarray(c["ctx"], dtype=np.int32)), d ** -0.5, kv, ks, vs,
+                              partition_tokens=part)
+        torch.cuda.synchronize()
+        plain = plain.cpu().numpy()
+        assert_close_to_oracle(plain, ref, kv, f"random {seed} plain part {part}")
+        c0 = dict(c, groups=np.zeros((3, 0), dtype=np.int32))
+        assert np.array_equal(_run_direct(c0, hq, d, kv, part).view(np.uint16), plain.view(np.uint16))
