@@ -45,6 +45,8 @@ def prefill_sequence(q_rows, K, V, L, sm_scale, group):
     pos = L - n + np.arange(n)                       # position of each query row
     visible = np.arange(L)[None, :] <= pos[:, None]  # [n, L] causal mask
     live = pos >= 0                                  # rows with something to attend
+    if not live.any():                               # an empty context: every row is 0
+        return out
     for h in range(hq):
         kv = h // group
         z = sm_scale * (q_rows[live, h, :] @ K[:, kv, :].T)  # [rows, L]

@@ -218,3 +218,17 @@ def test_pipeline_qwen3_prefill_small():
         ref = causal_sdpa64(full_q, K.astype(np.float64), V.astype(np.float64), wl.sm_scale)
         np.testing.assert_allclose(r.output[r.q_start[i]:r.q_start[i + 1]], ref[len(K) - n:],
                                    rtol=1e-11, atol=1e-11)
+
+
+def test_chunk_over_an_empty_context_is_zero():
+    """A sequence with no tokens but a chunk of rows: every row sits at a
+    position < 0, has nothing to attend and is 0; its neighbours are
+    unaffected."""
+    kc, vc, tables, logical = _paged(21, [0, 4], 2, 8, 4)
+    q = _queries(22, 5, 2, 8)
+    out = prefill.prefill_attention(q, [0, 3, 5], kc, vc, tables, [0, 4], 4, 0.5)
+    assert np.array_equal(out[:3], np.zeros((3, 2, 8)))
+    full_q = np.zeros((4, 2, 8))
+    full_q[2:] = q[3:]
+    ref = causal_sdpa64(full_q, logical[1][0].astype(np.float64), logical[1][1].astype(np.float64), 0.5)
+    np.testing.assert_allclose(out[3:], ref[2:], rtol=1e-12, atol=1e-12)
