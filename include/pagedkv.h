@@ -295,20 +295,20 @@ int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, i
  * prefix-cache blocks ([VRAM] §4.2-4.4). The output is the same attention as
  * paged_attn_decode's; only the order of the sums differs.
  * Group g is the sequences first[g] .. first[g] + size[g] - 1 of the batch.
- * Its shared tokens -- the first prefix[g] (rounded down to a multiple of 16,
- * and to no more than the first sequence's ctx_len) -- are read through the
- * table of sequence first[g]. One pass 1 launch covers the whole batch on the
- * matrix cores: a group is cut into parts of up to 32 query columns (members x
- * query heads of a KV head); a part reads each shared block once for all its
- * columns, then each member's own tokens through that member's table; a
- * sequence in no group is a part of its own. A merge pass combines the parts
+ * Its shared tokens are the first prefix[g], rounded down to a multiple of
+ * 16. One pass 1 launch covers the whole batch on the matrix cores: a group is
+ * cut into parts of up to 32 query columns (members x query heads of a KV
+ * head); a part reads the shared tokens once for all its columns, through the
+ * table of its first member (and no more of them than that member's ctx_len,
+ * rounded down to 16), then each member's remaining tokens through that
+ * member's own table; a sequence in no group is a part of its own. A merge pass combines the parts
  * that were split between workers (exact up to rounding: the softmax of a
  * concatenation is the weighted merge of the softmaxes of its parts).
  *   group_first, group_size, group_prefix  device, int32 [num_groups]
  *                  (pkv_bm_prefix_groups computes them). Precondition: groups
  *                  ascending and disjoint, and every member maps its first
- *                  shared tokens to the same physical blocks as the group's
- *                  first sequence. A member with fewer tokens than that
+ *                  prefix[g] tokens (as far as its ctx_len reaches) to the
+ *                  same physical blocks as the group's first sequence. A member with fewer tokens than that
  *                  attends only to its own ctx_len of them. Entries that break
  *                  the precondition give wrong results but never an access
  *                  outside the buffers (members past the batch are dropped).

@@ -87,14 +87,15 @@ __device__ void build_group_parts(const AttnArgs& a, int* pt, int* scan, int* in
     const int f = g == tid ? f0 : a.grp_first[g];
     const int n = group_members(a, f, g == tid ? s0 : a.grp_size[g]);
     if (n == 0) continue;
-    // the shared tokens are read through the first member's table: no more
-    // of them than it holds (pt[f + 1] is still its length here); past
-    // 2^20 * 16 shared tokens the rest are taken as each member's own
-    const int pre = min(group_tokens(a, g == tid ? p0 : a.grp_prefix[g]), pt[f + 1] & ~15);
-    const int pre16 = min(pre >> 4, (1 << 20) - 1);
+    const int pre_g = group_tokens(a, g == tid ? p0 : a.grp_prefix[g]);
     for (int m = 0; m < n; ++m) {
       const int part = m / MP;
-      info[f + m] = pack_part(pre16, min(MP, n - part * MP), m - part * MP);
+      // a part reads the shared tokens through its first member's table: no
+      // more of them than that member holds (pt[i + 1] is still sequence i's
+      // length here); past 2^20 * 16 shared tokens the rest are taken as each
+      // member's own
+      const int pre = min(pre_g, pt[f + part * MP + 1] & ~15);
+      info[f + m] = pack_part(min(pre >> 4, (1 << 20) - 1), min(MP, n - part * MP), m - part * MP);
     }
   }
   __syncthreads();

@@ -17,6 +17,8 @@ ORACLE_THREADS = int(os.environ.get("PKV_ORACLE_THREADS", "16"))
 # Block slice for bit-exact cache comparisons (bounded host memory: a slice of
 # 1024 blocks is 160 MiB at 40 KV heads x 32 slots x 128 x fp16).
 CACHE_SLICE_BLOCKS = 1024
+# seeded random draws per randomized parity test (more with PKV_RANDOM_DRAWS)
+RANDOM_DRAWS = int(os.environ.get("PKV_RANDOM_DRAWS", "24"))
 
 
 def log(*a):

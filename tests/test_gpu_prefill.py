@@ -17,7 +17,7 @@ import torch
 import workloads
 from oracle import runner
 from paged_kv_cache_60_amd import harness
-from tests.gpu_util import ORACLE_THREADS, assert_caches_bit_exact, assert_close_to_oracle, log
+from tests.gpu_util import ORACLE_THREADS, RANDOM_DRAWS, assert_caches_bit_exact, assert_close_to_oracle, log
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +198,27 @@ def test_batch_of_more_than_4096_sequences(hq, hkv):
             for h in range(hq):
                 ref[r, h] = oattn.attend_one(q[r, h], K[:p + 1, h // G], V[:p + 1, h // G], 0.125)
     assert_close_to_oracle(got, ref, "f16", "prefill batch 4100")
+
+
+_RSHAPES = [(hq, hkv, d, bs, kv) for (hq, hkv) in ((4, 4), (8, 4), (16, 4), (32, 4))
+            for d in (64, 128) for bs in (16, 32, 64) for kv in ("f16", "fp8", "fp8_e5m2")]
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_DRAWS))
+def test_random_prefill_batches(seed):
+    """Seeded random shapes, context lengths (0-900) and chunk lengths (from
+    empty and one row to longer than the context), every row against the
+    oracle and both caches bit-exact."""
+    g = np.random.default_rng(3000 + seed)
+    hq, hkv, d, bs, kv = _RSHAPES[int(g.integers(0, len(_RSHAPES)))]
+    n = int(g.integers(1, 14))
+    lengths = [int(x) for x in g.integers(0, 900, size=n)]
+    chunks = []
+    for L in lengths:
+        r = g.random()
+        chunks.append(0 if r < 0.1 else 1 if r < 0.2 else L + int(g.integers(1, 40)) if r < 0.3
+                      else int(g.integers(0, L + 1)))
+    per_head = kv != "f16" and g.random() < 0.5
+    log(f"random prefill {seed}: {hq}/{hkv} d{d} bs{bs} {kv}{'+ph' if per_head else ''} "
+        f"lengths {lengths} chunks {chunks}")
+    _check(workloads.small_prefill(4000 + seed, lengths, chunks, hq, hkv, d, bs, kv, per_head=per_head))

@@ -22,7 +22,7 @@ import workloads
 from oracle import attention as oattn
 from oracle import runner
 from paged_kv_cache_60_amd import harness, ops
-from tests.gpu_util import ORACLE_THREADS, assert_caches_bit_exact, assert_close_to_oracle, log
+from tests.gpu_util import ORACLE_THREADS, RANDOM_DRAWS, assert_caches_bit_exact, assert_close_to_oracle, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -252,7 +252,7 @@ def _random_spec(g, bs):
     return spec
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(RANDOM_DRAWS))
 def test_random_batches_grouped_and_plain(seed):
     """Seeded random shapes and group layouts: the grouped call (and plain
     decode on the same caches and tables) within tolerance of the oracle at
@@ -280,3 +280,42 @@ def test_random_batches_grouped_and_plain(seed):
         assert_close_to_oracle(plain, ref, kv, f"random {seed} plain part {part}")
         c0 = dict(c, groups=np.zeros((3, 0), dtype=np.int32))
         assert np.array_equal(_run_direct(c0, hq, d, kv, part).view(np.uint16), plain.view(np.uint16))
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_DRAWS))
+def test_random_forked_scripts(seed):
+    """Seeded random forked-prompt scripts (1-4 prompts of 1-400 tokens, 1-6
+    members each with private tails of 0-40 tokens, independent sequences
+    between the groups) through the engine: two decode steps with the groups
+    the block manager finds (when it finds any) and with plain decode, every
+    output against the oracle, tables and lengths equal, caches bit-exact."""
+    g = np.random.default_rng(5000 + seed)
+    hq, hkv, d, bs, kv = _SHAPES[int(g.integers(0, len(_SHAPES)))]
+    n = int(g.integers(1, 5))
+    prompts = [int(x) for x in g.integers(1, 400, size=n)]
+    members = [int(x) for x in g.integers(1, 7, size=n)]
+    tails = [[int(x) for x in g.integers(0, 41, size=m)] for m in members]
+    singles = [int(x) for x in g.integers(0, 3, size=n)]
+    per_head = kv != "f16" and g.random() < 0.5
+    wl = workloads.small_forks(seed=6000 + seed, prompts=prompts, members=members, tails=tails,
+                               singles=singles, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                               kv_dtype=kv, max_steps=2, per_head=per_head)
+    part = int(g.choice([16, 80, 0]))
+    log(f"random forks {seed}: {hq}/{hkv} d{d} bs{bs} {kv}{'+ph' if per_head else ''} prompts {prompts} "
+        f"members {members} singles {singles} partition {part}")
+    o = runner.run(wl, steps=2, threads=ORACLE_THREADS)
+    for shared in (True, False):
+        eng = harness.make_engine(wl)
+        harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
+        outs, metas = harness.run_steps(eng, wl, 2, part, shared_prefix=shared)
+        torch.cuda.synchronize()
+        if shared:
+            log(f"random forks {seed}: {0 if eng.groups is None else eng.groups.shape[1]} groups")
+        for s in range(2):
+            tab, ctx = metas[s]
+            assert ctx.tolist() == o.ctx_lens[s]
+            for i, t in enumerate(o.tables[s]):
+                assert tab[i, :len(t)].tolist() == t
+            assert_close_to_oracle(outs[s], o.outputs[s], kv, f"random forks {seed} shared={shared} step {s}")
+        assert_caches_bit_exact(eng.k_cache, o.k_cache, f"random forks {seed} K cache")
+        assert_caches_bit_exact(eng.v_cache, o.v_cache, f"random forks {seed} V cache")
