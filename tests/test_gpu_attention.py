@@ -19,7 +19,7 @@ import workloads
 from oracle import attention as oattn
 from oracle import runner
 from paged_kv_cache_60_amd import harness, ops
-from tests.gpu_util import (ORACLE_THREADS, assert_caches_bit_exact, assert_close_to_oracle, cache_bits, log,
+from tests.gpu_util import (ORACLE_THREADS, RANDOM_DRAWS, assert_caches_bit_exact, assert_close_to_oracle, cache_bits, log,
                             oracle_bits)
 
 pytestmark = pytest.mark.gpu
@@ -268,3 +268,34 @@ def test_config3_prefix_cache_matches_scripted_sharing():
     assert_close_to_oracle(o2[0], o.outputs[0], "f16", "config 3 cached")
     assert_caches_bit_exact(eng.k_cache, o.k_cache, "config 3 cached K cache")
     assert_caches_bit_exact(eng.v_cache, o.v_cache, "config 3 cached V cache")
+
+
+_RSHAPES = [(hq, hkv, d, bs, kv) for (hq, hkv) in ((4, 4), (8, 4), (16, 4), (32, 4))
+            for d in (64, 128) for bs in (16, 32, 64) for kv in ("f16", "fp8", "fp8_e5m2")]
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_DRAWS))
+def test_random_decode_scripts(seed):
+    """Seeded random batches of independent sequences (1-24 of them; lengths
+    from 1 to 2500, a third of them next to a block or unit edge) decoded for
+    three steps through the engine (write step with its metadata, pass 1 on
+    the vector or matrix-core path, pass 2) at a random worker count: tables
+    and lengths equal the oracle's, every output within tolerance, caches
+    bit-exact."""
+    g = np.random.default_rng(7000 + seed)
+    hq, hkv, d, bs, kv = _RSHAPES[int(g.integers(0, len(_RSHAPES)))]
+    n = int(g.integers(1, 25))
+    lengths = []
+    for _ in range(n):
+        if g.random() < 0.33:
+            edge = int(g.choice([bs, 16, 32, 64])) * int(g.integers(1, 12))
+            lengths.append(max(1, edge + int(g.integers(-2, 3))))
+        else:
+            lengths.append(int(g.integers(1, 2501)))
+    per_head = kv != "f16" and g.random() < 0.5
+    part = int(g.choice([16, 80, 0]))
+    log(f"random decode {seed}: {hq}/{hkv} d{d} bs{bs} {kv}{'+ph' if per_head else ''} lengths {lengths} "
+        f"partition {part}")
+    wl = workloads.small_custom(seed=8000 + seed, lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                block_size=bs, kv_dtype=kv, max_steps=3, per_head=per_head)
+    _check(wl, steps=3, partition_tokens=part)
