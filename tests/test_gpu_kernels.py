@@ -11,7 +11,7 @@ import torch
 import workloads
 from oracle import cache_ops, fp8, runner
 from paged_kv_cache_60_amd import ops
-from tests.gpu_util import cache_bits, log, oracle_bits
+from tests.gpu_util import RANDOM_DRAWS, cache_bits, log, oracle_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -239,5 +239,59 @@ def test_debug_checks_refuse_racing_slots_and_pairs_before_queuing():
         guards.set_debug_checks(was)
     cache_ops.scatter(o_k, o_v, k_new.cpu().numpy(), v_new.cpu().numpy(), slots, bs)
     cache_ops.block_copy(o_k, o_v, ok_pairs)
+    assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
+    assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
+
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_DRAWS))
+def test_random_writes_and_copies(seed):
+    """Seeded random scatters and copies, bit-exact against the oracle: a
+    shape (1-40 KV heads, D 64/128, block size 16/32/64, fp16/e4m3/e5m2 with
+    a random multiplier per tensor or per KV head), 0-3000 tokens on distinct
+    slots of which some are -1, negative or past the pool, then disjoint copy
+    pairs of which some point outside the pool."""
+    g = np.random.default_rng(9000 + seed)
+    hkv = int(g.choice([1, 2, 8, 32, 40]))
+    d = int(g.choice([64, 128]))
+    bs = int(g.choice([16, 32, 64]))
+    kv = str(g.choice(["f16", "fp8", "fp8_e5m2"]))
+    nb = int(g.integers(2, 80))
+    T = int(g.integers(0, min(3000, nb * bs) + 1))
+    log(f"random write {seed}: hkv={hkv} d={d} bs={bs} {kv} nb={nb} T={T}")
+    slots = g.permutation(nb * bs)[:T].astype(np.int64)
+    bad = g.random(T)
+    slots[bad < 0.05] = -1
+    slots[(bad >= 0.05) & (bad < 0.08)] = -3
+    slots[(bad >= 0.08) & (bad < 0.10)] = nb * bs + 5
+    K = (g.standard_normal((T, hkv, d), dtype=np.float32) * float(g.choice([0.1, 1.0, 30.0]))).astype(np.float16)
+    V = g.standard_normal((T, hkv, d), dtype=np.float32).astype(np.float16)
+    o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, kv)
+    o_slots = np.where((slots >= 0) & (slots < nb * bs), slots, -1)
+    if kv != "f16" and g.random() < 0.5:
+        kinv = (g.random(hkv) * 200 + 0.5).astype(np.float32)
+        vinv = (g.random(hkv) * 200 + 0.5).astype(np.float32)
+        ka, va = torch.from_numpy(kinv).to(DEV), torch.from_numpy(vinv).to(DEV)
+    else:
+        kinv = vinv = 1.0 if kv == "f16" else float(np.float32(g.random() * 200 + 0.5))
+        ka = va = kinv
+    cache_ops.scatter(o_k, o_v, K, V, o_slots, bs, kv, kinv, vinv)
+    if T:
+        ops.paged_kv_write(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v,
+                           torch.from_numpy(slots).to(DEV), kv, ka, va)
+    # disjoint pairs: sources and destinations drawn without repeats
+    perm = g.permutation(nb)
+    n = int(g.integers(0, nb // 2 + 1))
+    pairs = [(int(perm[i]), int(perm[nb - 1 - i])) for i in range(n)]
+    for i in range(len(pairs)):
+        r = g.random()
+        if r < 0.1:
+            pairs[i] = (pairs[i][0], nb + 3)
+        elif r < 0.2:
+            pairs[i] = (-2, pairs[i][1])
+    cache_ops.block_copy(o_k, o_v, [p for p in pairs if 0 <= p[0] < nb and 0 <= p[1] < nb])
+    if pairs:
+        ops.paged_block_copy(g_k, g_v, torch.tensor(pairs, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
     assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
     assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
