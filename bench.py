@@ -748,6 +748,7 @@ def main():
             "partition_tokens": args.partition,
             "attention_workers": workers,
             "shared_prefix_groups": int(eng.groups.shape[1]) if shared else 0,
+            "disjoint_blocks": eng.disjoint is not None,
             "timing": "gpu events per step, L2/MALL flushed between steps" if args.flush else "wall clock",
         },
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),

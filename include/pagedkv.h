@@ -200,7 +200,9 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  *                  to fp16 exactly before the arithmetic).
  *   partition_tokens 0 = one worker per SIMD of the device (fp16 KV with one
  *                  query head per KV head) or two (other shapes), within
- *                  what the device can hold at once; else a multiple of 16:
+ *                  what the device can hold at once, rounded down to a
+ *                  multiple of num_kv_heads where that drops under 1/16 of
+ *                  them and keeps whole workgroups of 4; else a multiple of 16:
  *                  each worker takes about this many tokens of the longest
  *                  possible batch (at most 8192 workers either way).
  *   workspace      device, >= paged_attn_decode_workspace_bytes(...) bytes
@@ -312,8 +314,15 @@ int paged_attn_decode_workers(int num_seqs, int num_q_heads, int num_kv_heads, i
  *                  attends only to its own ctx_len of them. Entries that break
  *                  the precondition give wrong results but never an access
  *                  outside the buffers (members past the batch are dropped).
- *                  With num_groups = 0 the call is paged_attn_decode (the
- *                  same bits).
+ *                  With num_groups = 0 the caller declares that no block is
+ *                  held by two sequences of the batch: the call is
+ *                  paged_attn_decode (the same shares and sums, the same
+ *                  bits), with its waves ordered for disjoint blocks -- each
+ *                  XCD reads all KV heads of a range of tiles, not a few heads
+ *                  of every tile, when one XCD's heads of a block would be
+ *                  under 32 KiB (faster for disjoint blocks; slower where
+ *                  sequences do share blocks, which head-major order serves
+ *                  through one L2, so the declaration is the caller's).
  *   k_scale, v_scale, k_scales, v_scales  fp8 only: per-tensor multipliers, or
  *                  one per KV head when k_scales and v_scales (device float
  *                  [num_kv_heads]) are both non-NULL.

@@ -96,6 +96,10 @@ struct AttnArgs {
   int NG = 0;
   int g_log2 = 0;              // log2(query heads per KV head)
   int32_t* ws_part = nullptr;  // [B] each sequence's part record (grouped pass 1 -> merge)
+  int32_t* ws_seg = nullptr;   // [B][2] the unit range of each sequence's part (grouped pass 1 -> merge)
+  // W / Hkv when the waves are dealt to the shares in head groups (W a
+  // multiple of Hkv), else 0; see worker_index
+  int head_groups = 0;
 };
 
 // The logit and output scales of KV head h.
@@ -222,18 +226,29 @@ __device__ __forceinline__ Piece locate(const int* pt, int B, int P, int64_t t, 
 }
 
 // Worker index of wave `wave` of this workgroup. Workgroups are dispatched to
-// the eight XCDs round-robin (workgroup g runs on XCD g % 8), so workgroups
-// g, g + 8, g + 16, ... share one L2. They are given consecutive worker
-// indices, which puts one contiguous slice of the head-major unit space -- a
-// few KV heads of every sequence -- on each XCD: K/V blocks that several
-// sequences share (a common prefix, beams of one prompt) are then read
-// through a single L2.
-__device__ __forceinline__ int64_t worker_index(int wave, int NW) {
+// The worker index of a wave: which equal share of the head-major unit space
+// it streams. The eight XCDs take workgroups round-robin (workgroup g runs on
+// XCD g % 8); workgroups g, g + 8, g + 16, ... take consecutive positions, so
+// that each XCD, and its L2, holds one contiguous run of positions.
+// Without head groups the position is the worker index: an XCD streams one
+// contiguous slice of the unit space, a few KV heads of every sequence.
+// With head groups (hg = W / Hkv), the Hkv consecutive positions p of a group
+// take worker (p % Hkv) * hg + p / Hkv: the same share of every KV head's unit
+// space (the shares of the head-major space fall on head boundaries when W is
+// a multiple of Hkv), one head each. The waves of a group then walk the same
+// tiles of the same sequences at about the same pace, and a block's heads,
+// which lie side by side in the pool, are read together: the same bytes from
+// fewer, larger regions of memory at once, which streams a few percent faster
+// than every wave reading a region of its own.
+__device__ __forceinline__ int64_t worker_index(int wave, int NW, const AttnArgs& a) {
   const int n = gridDim.x;
   const int xcd = blockIdx.x % 8;
   const int q = n / 8, r = n % 8;
   const int wg = xcd * q + min(xcd, r) + (int)(blockIdx.x / 8);
-  return (int64_t)wg * NW + wave;
+  const int64_t p = (int64_t)wg * NW + wave;
+  const int hg = a.head_groups;
+  if (hg > 0 && hg * a.Hkv == a.workers) return (int64_t)((int)p % a.Hkv) * hg + (int)p / a.Hkv;
+  return p;
 }
 
 template <int D, int G, int FMT, int NW>
@@ -260,7 +275,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i <= a.B; i += NW * 64) a.ws_pt[i] = pt[i];
   const int P = wave_uniform(pt[a.B]);
   const int64_t total = (int64_t)a.Hkv * P;
-  const int64_t w = worker_index(wave, NW);
+  const int64_t w = worker_index(wave, NW, a);
   const int64_t start = share_start(w, total, a.workers);
   const int64_t end = share_start(w + 1, total, a.workers);
 
@@ -619,12 +634,14 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
   const int hq = wid - seq * a.Hq;
   const int kvh = hq / G;
   const int g = hq - kvh * G;
+  // the three prefix entries in one round trip
   const int p0 = a.ws_pt[seq];
-  const int n_u = a.ws_pt[seq + 1] - p0;
+  const int p1 = a.ws_pt[seq + 1];
+  const int P = a.ws_pt[a.B];
+  const int n_u = p1 - p0;
   f16* out = a.out + (size_t)wid * D + lane * DL;
   Row<DL> r;
   if (n_u > 0) {
-    const int P = a.ws_pt[a.B];
     const int64_t total = (int64_t)a.Hkv * P;
     const int64_t s0 = (int64_t)kvh * P + p0;  // the segment's units: [s0, s1)
     if (held_whole(s0, s0 + n_u, total, a.workers)) return;  // written by pass 1
@@ -780,6 +797,19 @@ int64_t unit_upper_bound(int B, int max_blocks, int block_size, int unit) {
   return (int64_t)B * ((lmax + unit - 1) / unit);
 }
 
+// Head groups for W workers over Hkv KV heads (worker_index) on a batch that
+// shares no blocks: W / Hkv, or 0 (one slice of the unit space per wave) when
+// W is not a multiple of Hkv or when the slice of a block that one XCD reads
+// in head-major order -- Hkv / 8 heads side by side, head_bytes each -- is
+// already 32 KiB or more. Measured on MI355X: Llama-2-7B layer (16 KiB per
+// XCD per block) pass 1 186 us with head groups against 189 us; OPT-13B layer
+// (40 KiB) 1156 us against 1151 us.
+int head_groups_for(int W, int Hkv, size_t head_bytes) {
+  if (Hkv <= 0 || W % Hkv != 0) return 0;
+  const size_t slice = (size_t)((Hkv + 7) / 8) * head_bytes;
+  return slice < 32768 ? W / Hkv : 0;
+}
+
 struct Plan {
   KernFn fn;
   KernFn reduce;
@@ -821,6 +851,11 @@ int plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int bloc
     W = (int64_t)wgs * kWaves;
     const int64_t by_simd = (int64_t)waves_per_simd(G, kv_dtype != PKV_KV_F16) * 4 * cus;
     if (W > by_simd) W = by_simd;
+    // a multiple of Hkv where that keeps whole workgroups and loses under 1/16
+    // of the workers: the shares then fall on KV-head boundaries, which
+    // head groups need (worker_index)
+    const int64_t Wh = W / num_kv_heads * num_kv_heads;
+    if (Wh % kWaves == 0 && Wh * 16 >= W * 15) W = Wh;
   }
   if (W > ub_all) W = ub_all;
   if (W > kMaxWorkers) W = kMaxWorkers;
@@ -864,10 +899,11 @@ namespace {
 // Workspace of paged_attn_decode_shared, byte offsets of its regions (each
 // 256-byte aligned): the grouped pass 1's slots ([kMaxGroupWorkers][2]
 // [kGroupCols] columns of D outputs, then of (max, sum)), the unit prefix
-// over the sequences and their part records. Without groups the call is
+// over the sequences, their part records and their parts' unit ranges.
+// Without groups the call is
 // paged_attn_decode's, so the total also covers that workspace.
 struct GroupLayout {
-  size_t o, ml, pt, part, total;
+  size_t o, ml, pt, part, seg, total;
 };
 
 GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
@@ -883,6 +919,7 @@ GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
   L.ml = take(cols * 2 * sizeof(float));
   L.pt = take((size_t)(B + 1) * sizeof(int32_t));
   L.part = take((size_t)B * sizeof(int32_t));
+  L.seg = take((size_t)B * 2 * sizeof(int32_t));
   const size_t plain = paged_attn_decode_workspace_bytes(B, Hq, Hkv, D, 1, 16, 0);
   L.total = off > plain ? off : plain;
   return L;
@@ -942,7 +979,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int max_blocks_per_seq, const int32_t* ctx_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int num_blocks, float sm_scale, int kv_dtype, float k_scale,
                 float v_scale, const float* k_scales, const float* v_scales, int partition_tokens,
-                void* workspace, size_t workspace_bytes, int passes, void* stream, bool compact_ws = false) {
+                void* workspace, size_t workspace_bytes, int passes, void* stream, bool compact_ws = false,
+                bool disjoint = false) {
   if (passes < 1 || passes > 3 || num_blocks <= 0) return PKV_ERR_INVALID;
   Plan pl;
   int rc = plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, kv_dtype,
@@ -1000,6 +1038,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.num_blocks = num_blocks;
     a.unit_tokens = pl.unit;
     a.workers = pl.workers;
+    a.head_groups = disjoint ? head_groups_for(pl.workers, num_kv_heads,
+                                               (size_t)block_size * head_dim * (fp8 ? 1 : 2))
+                             : 0;
     a.qk_scale = sm_scale * kLog2e * (fp8 ? k_scale : 1.0f);
     a.v_out_scale = fp8 ? v_scale : 1.0f;
     a.k_scale_h = fp8 ? k_scales : nullptr;
@@ -1155,12 +1196,17 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_INVALID;
   const bool fp8 = kv_dtype != PKV_KV_F16;
   const bool per_head = fp8 && k_scales != nullptr;
-  if (num_groups == 0) {  // nothing shared: paged_attn_decode itself, the same bits
+  // No groups: the batch is declared to share no blocks. paged_attn_decode's
+  // kernels, shares and sums (the same bits), with the waves dealt in head
+  // groups (worker_index): no block is read by two sequences, so nothing is
+  // lost by spreading a block's KV heads over one XCD instead of giving each
+  // XCD a few heads of every sequence.
+  if (num_groups == 0) {
     const int p = ((passes & 3) ? 1 : 0) | ((passes & 4) ? 2 : 0);
     return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, ctx_lens, num_seqs,
                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale, kv_dtype, k_scale,
                        v_scale, per_head ? k_scales : nullptr, per_head ? v_scales : nullptr, partition_tokens,
-                       workspace, workspace_bytes, p, stream);
+                       workspace, workspace_bytes, p, stream, false, true);
   }
   // every unit of the batch (tail, shared units and setup charge of one part
   // per sequence at most) must fit the int32 prefix
@@ -1183,6 +1229,7 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a.ws_pt = reinterpret_cast<int32_t*>(ws + lay.pt);
   a.ws_part = reinterpret_cast<int32_t*>(ws + lay.part);
+  a.ws_seg = reinterpret_cast<int32_t*>(ws + lay.seg);
   a.out = static_cast<f16*>(out);
   a.max_blocks = max_blocks_per_seq;
   a.B = num_seqs;

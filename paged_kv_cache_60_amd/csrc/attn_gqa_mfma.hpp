@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
     for (int i = threadIdx.x; i <= a.B; i += NW * 64) a.ws_pt[i] = pt[i];
   const int P = wave_uniform(pt[a.B]);
   const int64_t total = (int64_t)a.Hkv * P;
-  const int64_t w = worker_index(wave, NW);
+  const int64_t w = worker_index(wave, NW, a);
   const int64_t start = share_start(w, total, a.workers);
   const int64_t end = share_start(w + 1, total, a.workers);
 

@@ -137,11 +137,19 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
   const int gl = a.g_log2;
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= a.B; i += NW * 64) a.ws_pt[i] = pt[i];
-    for (int i = threadIdx.x; i < a.B; i += NW * 64) a.ws_part[i] = info[i];
+    for (int i = threadIdx.x; i < a.B; i += NW * 64) {
+      const int v = info[i];
+      a.ws_part[i] = v;
+      // the part's units in the unit prefix ((0, 0), no units, for a part
+      // that would reach past the batch: only inconsistent group entries)
+      const int pf = i - part_mi(v), pe = pf + part_nm(v);
+      const bool ok = pf >= 0 && pe <= a.B;
+      *reinterpret_cast<int2*>(a.ws_seg + 2 * i) = ok ? make_int2(pt[pf], pt[pe]) : make_int2(0, 0);
+    }
   }
   const int P = wave_uniform(pt[a.B]);
   const int64_t total = (int64_t)a.Hkv * P;
-  const int64_t w = worker_index(wave, NW);
+  const int64_t w = worker_index(wave, NW, a);
   const int64_t start = share_start(w, total, a.workers);
   const int64_t end = share_start(w + 1, total, a.workers);
 
@@ -502,21 +510,19 @@ __global__ void __launch_bounds__(256) attn_reduce_group_kernel(AttnArgs a) {
   const int hq = wid - seq * a.Hq;
   const int kvh = hq / G;
   const int g = hq - kvh * G;
+  // the part record, the part's unit range and the unit total in one round trip
   const int v = a.ws_part[seq];
+  const int2 sg = *reinterpret_cast<const int2*>(a.ws_seg + 2 * seq);
+  const int P = a.ws_pt[a.B];
   const int mi = part_mi(v);
-  const int nm = part_nm(v);
-  const int pf = seq - mi;
   f16* out = a.out + (size_t)wid * D + lane * DL;
   Row<DL> r;
-  if (pf >= 0 && pf + nm <= a.B) {
-    const int P = a.ws_pt[a.B];
-    const int64_t total = (int64_t)a.Hkv * P;
-    const int64_t s0 = (int64_t)kvh * P + a.ws_pt[pf];
-    const int64_t s1 = (int64_t)kvh * P + a.ws_pt[pf + nm];
-    if (s1 > s0) {
-      if (held_whole(s0, s1, total, a.workers)) return;  // written by pass 1
-      fold_pieces<D>(r, a.ws_o, a.ws_ml, kGroupCols, mi * G + g, s0, s1, total, a.workers);
-    }
+  const int64_t total = (int64_t)a.Hkv * P;
+  const int64_t s0 = (int64_t)kvh * P + sg.x;
+  const int64_t s1 = (int64_t)kvh * P + sg.y;
+  if (s1 > s0) {
+    if (held_whole(s0, s1, total, a.workers)) return;  // written by pass 1
+    fold_pieces<D>(r, a.ws_o, a.ws_ml, kGroupCols, mi * G + g, s0, s1, total, a.workers);
   }
   write_row(r, out);
 }

@@ -155,7 +155,10 @@ class PagedKVEngine:
         which reads those blocks once per run; decode steps only append, so
         the runs stay valid until the batch is set up again. None (default):
         do so when the block manager finds a run of two or more sequences
-        sharing at least one 32-token unit; True / False force either call."""
+        sharing at least one 32-token unit; True / False force either call.
+        Without runs, a batch whose sequences hold no block in common attends
+        through paged_attn_decode_shared with no groups, which declares that
+        (paged_attn_decode's bits, its waves ordered for disjoint blocks)."""
         torch.cuda.synchronize(self.device)  # queued kernels may still read the previous buffers
         B = len(batch_seqs)
         self.batch = np.ascontiguousarray(np.asarray(batch_seqs, dtype=np.int64))
@@ -183,6 +186,7 @@ class PagedKVEngine:
         self.tables_dev = torch.from_numpy(tab).to(self.device)
         self.ctx_dev.copy_(torch.from_numpy(ctx))
         self.groups = None
+        self.disjoint = None
         if shared_prefix is None:
             shared_prefix = B <= ops.SHARED_MAX_SEQS and self._sharing_found()
         if shared_prefix:
@@ -191,8 +195,22 @@ class PagedKVEngine:
             wsb = ops.shared_workspace_bytes(B, self.hq, self.hkv, self.d)
         else:
             wsb = ops.workspace_bytes(B, self.hq, self.hkv, self.d, self.max_blocks, self.bs, self.partition_tokens)
+            if 0 < B <= ops.SHARED_MAX_SEQS and self._blocks_disjoint(tab, ctx):
+                # no block is read by two sequences: paged_attn_decode_shared
+                # with no groups declares that, and orders the waves for it;
+                # steps keep it true (appends take fresh blocks, and a
+                # copy-on-write gives the writer a fresh one)
+                self.disjoint = torch.empty((3, 0), dtype=torch.int32, device=self.device)
+                wsb = max(wsb, ops.shared_workspace_bytes(B, self.hq, self.hkv, self.d))
         self.workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=self.device)
         torch.cuda.synchronize(self.device)
+
+    def _blocks_disjoint(self, tab, ctx) -> bool:
+        """Whether no block of the batch's tables (the entries its context
+        lengths reach) is held by two of its sequences."""
+        n = (ctx.astype(np.int64) + self.bs - 1) // self.bs
+        used = tab[np.arange(tab.shape[1])[None, :] < n[:, None]]
+        return np.unique(used).size == used.size
 
     def _sharing_found(self) -> bool:
         """Whether the batch holds a run of sequences sharing leading blocks
@@ -266,10 +284,11 @@ class PagedKVEngine:
         """Attention of the step; passes: 1 = pass 1 (with the shared-prefix
         pass when groups are set), 2 = pass 2 (the merge), 3 = both."""
         sm_scale = 1.0 / float(self.d) ** 0.5
-        if self.groups is not None:
+        groups = self.groups if self.groups is not None else self.disjoint
+        if groups is not None:
             bits = (3 if passes & 1 else 0) | (4 if passes & 2 else 0)
             ops.paged_attn_decode_shared(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev,
-                                         self.groups, sm_scale, self.kv_dtype, self.k_scale, self.v_scale,
+                                         groups, sm_scale, self.kv_dtype, self.k_scale, self.v_scale,
                                          self.partition_tokens, self.workspace, bits)
             return
         ops.paged_attn_decode(out, q, self.k_cache, self.v_cache, self.tables_dev, self.ctx_dev, sm_scale,

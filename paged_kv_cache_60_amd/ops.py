@@ -286,8 +286,11 @@ def paged_attn_decode_shared(out, q, k_cache, v_cache, block_tables, ctx_lens, g
     """paged_attn_decode for a batch whose runs of sequences share leading
     blocks: groups is a device int32 tensor [3, num_groups] holding, per
     group, its first batch index, its member count and its shared tokens (as
-    BlockManager.prefix_groups returns them). passes: bit 0 or 1 the grouped
-    pass 1, bit 2 the merge of parts split between workers."""
+    BlockManager.prefix_groups returns them); with no groups ([3, 0]) the
+    caller declares that no block is held by two sequences, and the call is
+    paged_attn_decode with its waves ordered for disjoint blocks (the same
+    bits). passes: bit 0 or 1 the grouped pass 1, bit 2 the merge of parts
+    split between workers."""
     w = "paged_attn_decode_shared"
     _require(q.is_cuda and q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 3, w, "q")
     _require(out.is_cuda and out.dtype == torch.float16 and out.is_contiguous() and out.shape == q.shape, w, "out")

@@ -208,18 +208,32 @@ def test_direct_per_head_scales():
     assert_close_to_oracle(_run_direct(c, 64, 128, "fp8_e5m2", 0), ref, "fp8_e5m2", "per-head")
 
 
-def test_direct_no_groups_matches_plain_decode_bits():
-    """With no groups the call is pass 1 and the merge of paged_attn_decode:
-    the same bits."""
-    spec = [("single", L) for L in (1, 17, 300, 1000, 64, 5)]
-    c = _direct_case(21, 32, 8, 128, 16, "f16", spec)
-    got = _run_direct(c, 32, 128, "f16", 0)
-    out = torch.empty((c["B"], 32, 128), dtype=torch.float16, device=DEV)
+@pytest.mark.parametrize("hq,hkv,d,bs,kv", [(32, 8, 128, 16, "f16"), (8, 8, 128, 16, "f16"), (16, 8, 64, 32, "f16"),
+                                             (40, 40, 128, 16, "f16"), (64, 8, 128, 64, "fp8"),
+                                             (32, 32, 128, 32, "fp8_e5m2")])
+def test_direct_no_groups_matches_plain_decode_bits(hq, hkv, d, bs, kv):
+    """With no groups (blocks declared disjoint) the call is pass 1 and the
+    merge of paged_attn_decode, its waves dealt in head groups where the
+    shape allows: the same shares and sums, so the same bits, on the vector
+    path (1 and 2 query heads per KV head), the matrix-core path and a KV head
+    count that does not divide 1024 (the worker count is rounded to it). The
+    output starts as 5.0, so a share that no wave took would show."""
+    spec = [("single", L) for L in (1, 17, 300, 1000, 64, 5, 2000, 0, 129)]
+    c = _direct_case(21 + hq + bs, hq, hkv, d, bs, kv, spec)
+    W = ops.decode_workers(c["B"], hq, hkv, d, bs, c["tab"].shape[1], kv, 0)
+    log(f"no groups {hq}/{hkv} d{d} bs{bs} {kv}: {W} workers")
+    assert W % hkv == 0
+    got = _run_direct(c, hq, d, kv, 0)
+    out = torch.full((c["B"], hq, d), 7.0, dtype=torch.float16, device=DEV)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
     ops.paged_attn_decode(out, dev(c["q"]), dev(c["kc"]), dev(c["vc"]), dev(c["tab"]),
-                          dev(np.asarray(c["ctx"], dtype=np.int32)), 128 ** -0.5)
+                          dev(np.asarray(c["ctx"], dtype=np.int32)), d ** -0.5, kv, float(c["ks"]), float(c["vs"]))
     torch.cuda.synchronize()
-    assert np.array_equal(got.view(np.uint16), out.cpu().numpy().view(np.uint16))
+    plain = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), plain.view(np.uint16))
+    ref = oattn.decode_attention(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], bs, d ** -0.5, kv,
+                                 c["ks"], c["vs"])
+    assert_close_to_oracle(got, ref, kv, "no groups")
 
 
 def test_direct_repeat_calls_bit_identical():
