@@ -645,8 +645,8 @@ def main():
     kernel = "attn_partition_mfma_kernel" if group >= 4 else "attn_partition_kernel"
     shared = eng.groups is not None
     if shared:
-        # the grouped pass 1 runs one worker (wave) per SIMD
-        workers = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        # the grouped pass 1 runs one worker (wave) per SIMD for an fp16 cache, two for fp8
+        workers = (1 if wl.kv_dtype == "f16" else 2) * 4 * torch.cuda.get_device_properties(0).multi_processor_count
         # one grouped pass 1 over every sequence: each group's shared blocks once, then the members' tails
         kernel = "attn_group_mfma_kernel"
         log(f"bench: {eng.groups.shape[1]} shared-prefix groups")

@@ -925,10 +925,10 @@ GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
   return L;
 }
 
-// Workers of the grouped pass 1: one per SIMD (its 32-column tiles and
-// several units of loads in flight keep about 300 registers per lane; two
-// per SIMD measured slower for fp8 as well), within what the device holds at
-// once; with partition_tokens, about that
+// Workers of the grouped pass 1: group_waves_per_simd per SIMD (one for fp16,
+// whose 32-column tiles and two units of loads in flight keep about 320
+// registers per lane; two for fp8, with one unit in flight each), within
+// what the device holds at once; with partition_tokens, about that
 // many tokens each of the largest unit space the batch can describe (every
 // sequence's tail plus a part's shared units, each at most the table width,
 // and a part's setup charge).
@@ -944,7 +944,8 @@ int group_workers(KernFn fn, int B, int Hkv, int max_blocks, int block_size, int
     int wgs = 0, cus = 0;
     if (!device_capacity(fn, dyn_lds_bytes(B, true), &wgs, &cus)) return PKV_ERR_HIP;
     W = (int64_t)wgs * kWaves;
-    const int64_t by_simd = (int64_t)4 * cus;
+    const int per_simd = kv_dtype == PKV_KV_F16 ? group_waves_per_simd<kF16>() : group_waves_per_simd<kE4M3>();
+    const int64_t by_simd = (int64_t)per_simd * 4 * cus;
     if (W > by_simd) W = by_simd;
   }
   if (W > ub) W = ub;

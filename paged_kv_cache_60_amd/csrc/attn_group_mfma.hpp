@@ -102,8 +102,18 @@ __device__ void build_group_parts(const AttnArgs& a, int* pt, int* scan, int* in
   build_scan(a.B, pt, scan, [&](int i) { return group_seq_units(info[i], pt[i + 1]); });
 }
 
+// Waves per SIMD of the grouped pass 1: fp8 units hold half the bytes of
+// fp16 ones, so with one wave per SIMD an fp8 unit's arithmetic (widening,
+// the matrix products, the softmax, V through LDS) outlasts its loads; two
+// waves per SIMD, each with one unit of loads in flight (221 registers, no
+// spill), overlap one wave's arithmetic with the other's loads. fp16 keeps one
+// wave per SIMD with two units in flight (at two waves per SIMD its ring
+// spills, and one unit in flight each measured slower).
+template <int FMT>
+constexpr int group_waves_per_simd() { return FMT != kF16 ? 2 : 1; }
+
 template <int D, int FMT, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(NW * 64, group_waves_per_simd<FMT>()) attn_group_mfma_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr bool FP8 = FMT != kF16;
   constexpr int ELEM = FP8 ? 1 : 2;
@@ -117,9 +127,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_group_mfma_kernel(AttnArgs a)
   constexpr int VLD = 32 / RPL;         // V loads per lane per 32-token unit
   constexpr int VS = D + 16;            // LDS row stride of V, halves
   constexpr int CB = kGroupCols / 16;   // 16-column blocks
-  // units whose loads are in flight at once: 8 KiB fp8 units need more of
-  // them to cover the memory latency with one wave per SIMD
-  constexpr int DEPTH = FP8 ? 4 : 2;
+  // units whose loads are in flight at once, per wave (group_waves_per_simd)
+  constexpr int DEPTH = FP8 ? 1 : 2;
   static_assert(CB == 2, "two column blocks");
   static_assert(RPL <= 16 && 16 % RPL == 0, "a V load stays inside one tile");
 
