@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/pagedkv.h"
 #include "device_common.hpp"
@@ -516,36 +517,38 @@ __device__ __forceinline__ void fold(Row<DL>& r, float m, float l, const float* 
   r.M = Mn;
 }
 
-// The lane's DL elements of the output rows of pieces j0 .. j0+7 of a batch
-// of nk <= 64 pieces, lane j holding the start of piece j's row (any readable
-// address for a piece that adds nothing); past nk, the last piece again.
-template <int DL>
+// The lane's DL elements of the output rows of pieces j0 .. j0+NB-1 of a
+// batch of nk <= 64 pieces, lane j holding the start of piece j's row (any
+// readable address for a piece that adds nothing); past nk, the last piece
+// again. Rows are fp32 (unnormalised partials) or fp16 (partials divided by
+// their own sum), widened to fp32 here.
+template <int DL, int NB>
 struct RowBatch {
-  float v[8][DL];
+  float v[NB][DL];
 };
-template <int DL>
-__device__ __forceinline__ RowBatch<DL> load_rows(const float* row, int j0, int nk) {
+template <int DL, int NB, typename T>
+__device__ __forceinline__ RowBatch<DL, NB> load_rows(const T* row, int j0, int nk) {
   const int lane = threadIdx.x & 63;
   const uint64_t rp = reinterpret_cast<uint64_t>(row);
-  RowBatch<DL> b;
+  RowBatch<DL, NB> b;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < NB; ++u) {
     const int j = min(j0 + u, nk - 1);
     const uint64_t pj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rp >> 32), j) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp, j);
-    const float* oj = reinterpret_cast<const float*>(pj) + lane * DL;
+    const T* oj = reinterpret_cast<const T*>(pj) + lane * DL;
 #pragma unroll
-    for (int e = 0; e < DL; ++e) b.v[u][e] = oj[e];
+    for (int e = 0; e < DL; ++e) b.v[u][e] = (float)oj[e];
   }
   return b;
 }
 
 // acc += the rows of b weighted by lane j's wgt for piece j0 + u, in piece
 // order (a weight of 0: no piece, or one that underflowed, adds nothing)
-template <int DL>
-__device__ __forceinline__ void add_rows(float* acc, float wgt, const RowBatch<DL>& b, int j0, int nk) {
+template <int DL, int NB>
+__device__ __forceinline__ void add_rows(float* acc, float wgt, const RowBatch<DL, NB>& b, int j0, int nk) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < NB; ++u) {
     const float w = j0 + u < nk ? readlane_f32(wgt, min(j0 + u, nk - 1)) : 0.0f;
     if (w == 0.0f) continue;
 #pragma unroll
@@ -556,25 +559,29 @@ __device__ __forceinline__ void add_rows(float* acc, float wgt, const RowBatch<D
 // Adds to acc (the lane's DL elements) the weighted output rows of nk <= 64
 // pieces: lane j holds piece j's weight (0: no piece, nothing is added) and
 // the start of its row (any readable address when the weight is 0). The rows
-// of the first eight pieces come in `first`, loaded by the caller before it
-// had the weights; the rest are loaded eight pieces at a time, so that their
+// of the first NB pieces come in `first`, loaded by the caller before it had
+// the weights; the rest are loaded NB pieces at a time, so that their
 // latencies overlap. The sum runs in piece order.
-template <int DL>
-__device__ __forceinline__ void sum_rows(float* acc, float wgt, const float* row, int nk, const RowBatch<DL>& first) {
-  add_rows<DL>(acc, wgt, first, 0, nk);
-  for (int j0 = 8; j0 < nk; j0 += 8) add_rows<DL>(acc, wgt, load_rows<DL>(row, j0, nk), j0, nk);
+template <int DL, int NB, typename T>
+__device__ __forceinline__ void sum_rows(float* acc, float wgt, const T* row, int nk,
+                                         const RowBatch<DL, NB>& first) {
+  add_rows<DL, NB>(acc, wgt, first, 0, nk);
+  for (int j0 = NB; j0 < nk; j0 += NB) add_rows<DL, NB>(acc, wgt, load_rows<DL, NB>(row, j0, nk), j0, nk);
 }
 
 // Folds into r the pieces of the segment holding units [s0, s1) of a unit
 // space of `total` units cut into W shares. The piece of worker w sits in
 // slot 0 if it starts the worker's share, else in slot 1; a slot holds `cols`
-// columns of D + 2 floats (o in ws_o, (max, sum) in ws_ml) and the row is
-// column `col`. Pieces are taken 64 at a time (lane k: piece k of the batch),
-// each batch folded into r; each lane owns D/64 output elements.
-template <int D>
-__device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_ml, int cols, int col,
+// columns of D outputs in ws_o and (max, sum) in ws_ml, and the row is column
+// `col`. Outputs of type float are unnormalised (relative to the max); of type
+// f16 they are divided by the piece's sum, so a row then weighs sum times the
+// max's factor. Pieces are taken 64 at a time (lane k: piece k of the batch),
+// NB rows at a time, each batch folded into r; each lane owns D/64 outputs.
+template <int D, typename T = float, int NB = 8>
+__device__ void fold_pieces(Row<D / 64>& r, const T* ws_o, const float* ws_ml, int cols, int col,
                             int64_t s0, int64_t s1, int64_t total, int64_t W) {
   constexpr int DL = D / 64;
+  constexpr bool kNormalised = !std::is_same<T, float>::value;
   const int lane = threadIdx.x & 63;
   if (s0 < 0 || s0 >= s1 || s1 > total) return;  // only inconsistent group entries get here
   // worker holding unit u: the largest w with share_start(w) <= u
@@ -592,9 +599,9 @@ __device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_m
     const int64_t pi = (wk * 2 + (st >= s0 ? 0 : 1)) * cols + col;
     const float m_ld = ws_ml[2 * pi];
     const float l_ld = ws_ml[2 * pi + 1];
-    const float* row = ws_o + pi * D;
+    const T* row = ws_o + pi * D;
     const int nk = min(64, np - k0);
-    const RowBatch<DL> first = load_rows<DL>(row, 0, nk);  // in flight while the weights are made
+    const RowBatch<DL, NB> first = load_rows<DL, NB>(row, 0, nk);  // in flight while the weights are made
     __builtin_amdgcn_sched_barrier(0);  // keep the uses of m_ld and l_ld below the row loads
     const float m = live ? m_ld : -INFINITY;
     const float l = live ? l_ld : 0.0f;
@@ -603,7 +610,7 @@ __device__ void fold_pieces(Row<D / 64>& r, const float* ws_o, const float* ws_m
     float acc[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) acc[e] = 0.0f;
-    sum_rows<DL>(acc, wgt, row, nk, first);
+    sum_rows<DL, NB>(acc, kNormalised ? wgt * l : wgt, row, nk, first);
     fold(r, M, wave_sum(l * wgt), acc);
   }
 }
@@ -898,7 +905,7 @@ namespace {
 
 // Workspace of paged_attn_decode_shared, byte offsets of its regions (each
 // 256-byte aligned): the grouped pass 1's slots ([kMaxGroupWorkers][2]
-// [kGroupCols] columns of D outputs, then of (max, sum)), the unit prefix
+// [kGroupCols] columns of D fp16 outputs, then of fp32 (max, sum)), the unit prefix
 // over the sequences, their part records and their parts' unit ranges.
 // Without groups the call is
 // paged_attn_decode's, so the total also covers that workspace.
@@ -915,7 +922,7 @@ GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
     return at;
   };
   const size_t cols = (size_t)kMaxGroupWorkers * 2 * kGroupCols;
-  L.o = take(cols * D * sizeof(float));
+  L.o = take(cols * D * sizeof(f16));  // fp16, each divided by its piece's sum
   L.ml = take(cols * 2 * sizeof(float));
   L.pt = take((size_t)(B + 1) * sizeof(int32_t));
   L.part = take((size_t)B * sizeof(int32_t));

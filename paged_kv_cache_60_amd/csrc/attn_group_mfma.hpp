@@ -28,7 +28,7 @@
 // to end, KV head major, and cut into equal shares, one per worker (a wave),
 // as in pass 1 of paged_attn_decode. A worker walks its share piece by piece;
 // a piece that is a whole segment writes its columns' outputs directly, any
-// other piece leaves (max, sum, unnormalised output) per column in the
+// other piece leaves (max, sum, output / sum in fp16) per column in the
 // worker's slot 0 (first piece of the share) or 1 (last), which
 // attn_reduce_group_kernel combines.
 //
@@ -490,10 +490,20 @@ __global__ void __launch_bounds__(NW * 64, group_waves_per_simd<FMT>()) attn_gro
           *reinterpret_cast<f16x4*>(orow + 16 * d) = h;
         }
       } else {
+        // the piece's output divided by its own sum, as fp16: a weighted mean
+        // of V rows, so within V's range, at half the bytes of fp32 partials
+        // (every share of a grouped launch is usually a piece of a segment,
+        // so these bytes are written and read again on every step)
         const size_t pi = ((size_t)w * 2 + slot) * kGroupCols + c;
-        float* orow = a.ws_o + pi * D + 4 * grp;
+        const float sc = l_part[cb] > 0.0f ? v_scale / l_part[cb] : 0.0f;
+        f16* orow = reinterpret_cast<f16*>(a.ws_o) + pi * D + 4 * grp;
 #pragma unroll
-        for (int d = 0; d < NT; ++d) *reinterpret_cast<f32x4*>(orow + 16 * d) = o[cb][d] * v_scale;
+        for (int d = 0; d < NT; ++d) {
+          f16x4 h;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = (f16)(o[cb][d][v] * sc);
+          *reinterpret_cast<f16x4*>(orow + 16 * d) = h;
+        }
         if (grp == 0) {
           a.ws_ml[2 * pi] = m_run[cb];
           a.ws_ml[2 * pi + 1] = l_part[cb];
@@ -531,7 +541,8 @@ __global__ void __launch_bounds__(256) attn_reduce_group_kernel(AttnArgs a) {
   const int64_t s1 = (int64_t)kvh * P + sg.y;
   if (s1 > s0) {
     if (held_whole(s0, s1, total, a.workers)) return;  // written by pass 1
-    fold_pieces<D>(r, a.ws_o, a.ws_ml, kGroupCols, mi * G + g, s0, s1, total, a.workers);
+    fold_pieces<D, f16, 16>(r, reinterpret_cast<const f16*>(a.ws_o), a.ws_ml, kGroupCols, mi * G + g, s0, s1,
+                            total, a.workers);
   }
   write_row(r, out);
 }

@@ -135,10 +135,10 @@ def test_shared_workspace_bytes():
     lib = _lib.load()
 
     def expect(b, hq, hkv, d):
-        # grouped pass-1 slots for 2048 workers x 2 x 32 columns, the unit prefix, the
-        # part records and the parts' unit ranges (256-aligned each), and at least
-        # paged_attn_decode's workspace
-        regions = [2048 * 2 * 32 * d * 4, 2048 * 2 * 32 * 2 * 4, (b + 1) * 4, b * 4, b * 8]
+        # grouped pass-1 slots for 2048 workers x 2 x 32 columns (fp16 outputs, fp32 max
+        # and sum), the unit prefix, the part records and the parts' unit ranges
+        # (256-aligned each), and at least paged_attn_decode's workspace
+        regions = [2048 * 2 * 32 * d * 2, 2048 * 2 * 32 * 2 * 4, (b + 1) * 4, b * 4, b * 8]
         grouped = sum(-(-n // 256) * 256 for n in regions)
         return max(grouped, lib.paged_attn_decode_workspace_bytes(b, hq, hkv, d, 1, 16, 0))
     f = lib.paged_attn_decode_shared_workspace_bytes
