@@ -178,7 +178,8 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  * and cut into equal contiguous shares, one per worker (a wave). Pass 1: each
  * worker runs an online softmax over its share; a segment it holds whole is
  * written to `out`, a segment split between workers leaves (max, sum,
- * unnormalised output) partials. Pass 2 combines the partials of split
+ * output) partials (the output fp32 and unnormalised for 1 or 2 query heads
+ * per KV head, fp16 and divided by the sum for 4 or 8). Pass 2 combines the partials of split
  * segments and writes zeros for sequences with ctx_len 0.
  *
  *   out            device, fp16 [num_seqs][num_q_heads][head_dim]

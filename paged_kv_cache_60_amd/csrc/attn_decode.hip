@@ -17,13 +17,15 @@
 // segment inside the share):
 //   - a piece that is its whole segment is normalised and written to the
 //     output directly;
-//   - otherwise the piece's online-softmax state (max m, sum l, unnormalised
-//     output o) goes to one of the worker's two partial slots: slot 0 for the
-//     first piece of the share, slot 1 for the last (any piece between them
-//     is a whole segment).
+//   - otherwise the piece's online-softmax state (max m, sum l, and its
+//     output: unnormalised fp32 on the vector path, divided by l as fp16 on
+//     the matrix-core path) goes to one of the worker's two partial slots:
+//     slot 0 for the first piece of the share, slot 1 for the last (any piece
+//     between them is a whole segment).
 // Pass 2 combines, for every (sequence, query head) whose segment was split,
 // the pieces of the consecutive workers that hold it, with weights
-// exp(m_p - max m), and writes zeros for empty sequences. The split depends
+// exp(m_p - max m) (times l_p for the normalised ones), and writes zeros for
+// empty sequences. The split depends
 // only on the context lengths and the worker count, so results are
 // deterministic and independent of block placement. Every worker streams the
 // same number of tokens, no workgroup is idle and none waits on another.
@@ -67,7 +69,7 @@ struct AttnArgs {
   const uint8_t* vc;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  float* ws_o;     // [kMaxWorkers][2][G][D]  unnormalised outputs of partial pieces
+  float* ws_o;     // [kMaxWorkers][2][G][D]  outputs of partial pieces (fp32, or fp16 for G >= 4)
   float* ws_ml;    // [kMaxWorkers][2][G][2]  (max, sum) of partial pieces
   int32_t* ws_pt;  // [B + 1]                 unit prefix over sequences (pass 1 -> pass 2)
   f16* out;
@@ -652,7 +654,13 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(AttnArgs a) {
     const int64_t total = (int64_t)a.Hkv * P;
     const int64_t s0 = (int64_t)kvh * P + p0;  // the segment's units: [s0, s1)
     if (held_whole(s0, s0 + n_u, total, a.workers)) return;  // written by pass 1
-    fold_pieces<D>(r, a.ws_o, a.ws_ml, G, g, s0, s0 + n_u, total, a.workers);
+    // the matrix-core pass (G >= 4) leaves its pieces as fp16 divided by their
+    // sums; the vector pass as fp32 relative to their maxima
+    if constexpr (G >= 4)
+      fold_pieces<D, f16, 8>(r, reinterpret_cast<const f16*>(a.ws_o), a.ws_ml, G, g, s0, s0 + n_u, total,
+                              a.workers);
+    else
+      fold_pieces<D>(r, a.ws_o, a.ws_ml, G, g, s0, s0 + n_u, total, a.workers);
   }
   write_row(r, out);
 }

@@ -301,10 +301,18 @@ __global__ void __launch_bounds__(NW * 64) attn_partition_mfma_kernel(AttnArgs a
           *reinterpret_cast<f16x4*>(orow + 16 * c) = h;
         }
       } else {
+        // the piece's output divided by its own sum, as fp16 (a weighted mean
+        // of V rows, so within V's range), at half the bytes of fp32
         const size_t pi = ((size_t)w * 2 + slot) * G + col;
-        float* orow = a.ws_o + pi * D + 4 * grp;
+        const float sc = l_part > 0.0f ? v_scale / l_part : 0.0f;
+        f16* orow = reinterpret_cast<f16*>(a.ws_o) + pi * D + 4 * grp;
 #pragma unroll
-        for (int c = 0; c < NT; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = o[c] * v_scale;
+        for (int c = 0; c < NT; ++c) {
+          f16x4 h;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = (f16)(o[c][v] * sc);
+          *reinterpret_cast<f16x4*>(orow + 16 * c) = h;
+        }
         if (grp == 0) {
           a.ws_ml[2 * pi] = m_run;
           a.ws_ml[2 * pi + 1] = l_part;
