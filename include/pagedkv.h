@@ -207,7 +207,7 @@ int paged_block_swap(void* k_cache, void* v_cache, void* k_host, void* v_host, c
  *                  each worker takes about this many tokens of the longest
  *                  possible batch (at most 8192 workers either way).
  *   workspace      device, >= paged_attn_decode_workspace_bytes(...) bytes
- *                  (fp32 partials and the unit prefix; contents on entry are
+ *                  (partials and the unit prefix; contents on entry are
  *                  ignored). Calls that share a workspace must not overlap.
  * Shapes: head_dim 64 or 128; block_size 16, 32 or 64; num_q_heads a multiple
  * of num_kv_heads with 1, 2, 4 or 8 query heads per KV head. Batches of more
