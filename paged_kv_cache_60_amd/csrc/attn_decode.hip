@@ -105,14 +105,6 @@ struct AttnArgs {
   int head_groups = 0;
 };
 
-// The logit and output scales of KV head h.
-__device__ __forceinline__ float head_qk_scale(const AttnArgs& a, int h) {
-  return a.k_scale_h ? a.qk_base * a.k_scale_h[h] : a.qk_scale;
-}
-__device__ __forceinline__ float head_v_scale(const AttnArgs& a, int h) {
-  return a.v_scale_h ? a.v_scale_h[h] : a.v_out_scale;
-}
-
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
 
 __device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
@@ -941,8 +933,7 @@ GroupLayout group_layout(int B, int Hq, int Hkv, int D) {
 }
 
 // Workers of the grouped pass 1: group_waves_per_simd per SIMD (one for fp16,
-// whose 32-column tiles and two units of loads in flight keep about 320
-// registers per lane; two for fp8, with one unit in flight each), within
+// two for fp8), within
 // what the device holds at once; with partition_tokens, about that
 // many tokens each of the largest unit space the batch can describe (every
 // sequence's tail plus a part's shared units, each at most the table width,
