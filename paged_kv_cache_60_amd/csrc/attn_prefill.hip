@@ -89,6 +89,15 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 
 __device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
 
+// max of three floats in one v_max3_f32. fmaxf on matrix-core results costs
+// two extra instructions per call: the compiler first quiets possible
+// signalling NaNs, which these logits never are.
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // A float the caller knows is equal on all lanes, moved to a scalar register.
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
@@ -408,13 +417,20 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
   }
   const bool all_live = nt == QT;
 
+  // Softmax state per column, in the lanes of its column: the running max
+  // m (log2 units) is kept as two derived values that the token loop uses
+  // directly, so that a step without a move of the max spends no vector
+  // instructions on it: thr = (m + kLazy) / qk_scale, the raw logit above
+  // which the max must move (-inf while m is -inf), and neg_m = -m (0 while
+  // m is -inf). l_part is the lane's share of the column's sum.
   f32x4 o[kNcg][NT];
-  float m_run[kNcg], l_part[kNcg];
+  float thr[kNcg], neg_m[kNcg], l_part[kNcg];
 #pragma unroll
   for (int cg = 0; cg < kNcg; ++cg) {
 #pragma unroll
     for (int c = 0; c < NT; ++c) o[cg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[cg] = -INFINITY;
+    thr[cg] = -INFINITY;
+    neg_m[cg] = 0.0f;
     l_part[cg] = 0.0f;
   }
 
@@ -474,9 +490,10 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
 
     // online softmax per column; lane (col, grp) sees tokens t0 + 4grp + v and
     // t0 + 16 + 4grp + v. Raw logits are masked to -inf where needed; the
-    // running max m_run (log2 units) is moved only when some lane's logits
-    // exceed it by more than kLazy, so between moves no lane shuffles and the
-    // accumulators are not rescaled (p <= 2^kLazy then, well inside fp16).
+    // running max m (log2 units) is moved only when some lane's logit exceeds
+    // it by more than kLazy (a raw logit above thr), so between moves no lane
+    // shuffles and the accumulators are not rescaled (p <= 2^kLazy then, well
+    // inside fp16).
     const bool plain = all_live && ok_a && ok_b && t0 + kChunk - 1 <= pos0;
     float z[kNcg][8];
     float mt[kNcg];
@@ -496,40 +513,42 @@ __global__ void __launch_bounds__(kWaves * 64, kMinBlocks) attn_prefill_kernel(P
           z[cg][4 + v] = (ok_b && tb <= qpos[cg]) ? z[cg][4 + v] : -INFINITY;
         }
       }
-      float m = z[cg][0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, z[cg][i]);
-      mt[cg] = m * qk_scale;
+      // the lane's largest raw logit
+      const float ma = max3_f32(z[cg][0], z[cg][1], z[cg][2]);
+      const float mb = max3_f32(z[cg][3], z[cg][4], z[cg][5]);
+      const float mc = max3_f32(z[cg][6], z[cg][7], ma);
+      mt[cg] = max3_f32(mb, mc, mc);
     }
     bool need = false;
 #pragma unroll
-    for (int cg = 0; cg < kNcg; ++cg) need = need || mt[cg] > m_run[cg] + kLazy;
+    for (int cg = 0; cg < kNcg; ++cg) need = need || mt[cg] > thr[cg];
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int cg = 0; cg < kNcg; ++cg) {
         float m = mt[cg];
         m = fmaxf(m, shfl_xor_f32(m, 16));
         m = fmaxf(m, shfl_xor_f32(m, 32));
-        const float mn = fmaxf(m_run[cg], m);
-        const float alpha = fast_exp2(m_run[cg] - safe_max(mn));
+        m *= qk_scale;
+        const float m_old = thr[cg] == -INFINITY ? -INFINITY : -neg_m[cg];
+        const float mn = fmaxf(m_old, m);
+        const float alpha = fast_exp2(m_old - safe_max(mn));
         l_part[cg] *= alpha;
 #pragma unroll
         for (int c = 0; c < NT; ++c) o[cg][c] *= alpha;
-        m_run[cg] = mn;
+        neg_m[cg] = -safe_max(mn);
+        thr[cg] = (mn + kLazy) / qk_scale;
       }
     }
     f16x8 pb[kNcg];
 #pragma unroll
     for (int cg = 0; cg < kNcg; ++cg) {
-      const float neg_m = -safe_max(m_run[cg]);
-      float ps = 0.0f;
+      float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(z[cg][i], qk_scale, neg_m));
-        ps += p;
-        pb[cg][i] = (_Float16)p;
+        p[i] = fast_exp2(__builtin_fmaf(z[cg][i], qk_scale, neg_m[cg]));
+        pb[cg][i] = (_Float16)p[i];
       }
-      l_part[cg] += ps;
+      l_part[cg] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
 
     // O^T += V^T . P^T, one 16-row head-dim tile at a time
