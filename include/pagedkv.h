@@ -284,6 +284,21 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, con
                               float sm_scale, int kv_dtype, float k_scale, float v_scale,
                               int partition_tokens, void* stream);
 
+/*
+ * pkv_time_next_pass1 -- measurement hook, for benchmarks and profilers. The
+ * next pass-1 launch that the calling thread makes (through
+ * paged_attn_decode, _passes, _scaled, _noalloc or paged_attn_decode_shared)
+ * is launched with hipExtLaunchKernel and records start_event and stop_event
+ * (hipEvent_t, created by the caller with timing enabled) as the start and
+ * the stop of that kernel's own execution, so that
+ * hipEventElapsedTime(start_event, stop_event) is the kernel's duration
+ * alone, without the idle time that separate event records add to the
+ * stream. The hook then disarms; both null disarms it as well. Exactly one
+ * null: PKV_ERR_INVALID. It changes no result. A call that fails before its
+ * pass-1 launch leaves the hook armed.
+ */
+int pkv_time_next_pass1(void* start_event, void* stop_event);
+
 /* The number of workers (waves) pass 1 uses for this shape on the current
  * device (for one launch of up to 4096 sequences), or a negative status for an
  * invalid shape or a failed device query. */

@@ -90,6 +90,7 @@ SIGNATURES = {
     "paged_attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int,
                                            _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _c_int, _vp]),
     "paged_attn_decode_workers": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_time_next_pass1": (_c_int, [_vp, _vp]),
     "paged_attn_decode_shared_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int]),
     "paged_attn_decode_shared": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
                                           _c_int, _c_int, _c_int, _c_f, _c_int, _c_f, _c_f, _vp,

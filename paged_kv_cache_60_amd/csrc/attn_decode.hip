@@ -45,6 +45,7 @@
 //
 // Exponentials are taken base 2 with log2(e) folded into the logit scale.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -668,6 +669,24 @@ namespace {
 
 typedef void (*KernFn)(AttnArgs);
 
+// Events that the next pass-1 launch of this thread records as its own start
+// and stop (pkv_time_next_pass1); null when not armed.
+thread_local hipEvent_t g_pass1_start = nullptr;
+thread_local hipEvent_t g_pass1_stop = nullptr;
+
+// A pass-1 launch: through hipExtLaunchKernel with the armed events (which
+// it consumes), else an ordinary launch. Returns the launch's status.
+hipError_t launch_pass1(KernFn fn, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, const AttnArgs& a) {
+  if (g_pass1_start) {
+    hipEvent_t e0 = g_pass1_start, e1 = g_pass1_stop;
+    g_pass1_start = g_pass1_stop = nullptr;
+    hipExtLaunchKernelGGL(fn, grid, block, lds, s, e0, e1, 0u, a);
+  } else {
+    hipLaunchKernelGGL(fn, grid, block, lds, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int FMT>
 KernFn pick_partition_kernel(int G) {
   switch (G) {
@@ -1054,8 +1073,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.v_scale_h = fp8 ? v_scales : nullptr;
     a.qk_base = sm_scale * kLog2e;
     if (passes & 1) {
-      hipLaunchKernelGGL(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64), dyn_lds_bytes(B), s, a);
-      if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+      if (launch_pass1(pl.fn, dim3((unsigned)(pl.workers / kWaves)), dim3(kWaves * 64),
+                       (uint32_t)dyn_lds_bytes(B), s, a) != hipSuccess)
+        return PKV_ERR_HIP;
     }
     if (passes & 2) {
       const int waves = B * num_q_heads;
@@ -1258,14 +1278,21 @@ extern "C" int paged_attn_decode_shared(void* out, const void* q, const void* k_
   a.g_log2 = log2_exact(G);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (passes & 3) {
-    hipLaunchKernelGGL(group_fn, dim3((unsigned)(W / kWaves)), dim3(kWaves * 64), dyn_lds_bytes(num_seqs, true), s,
-                       a);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    if (launch_pass1(group_fn, dim3((unsigned)(W / kWaves)), dim3(kWaves * 64),
+                     (uint32_t)dyn_lds_bytes(num_seqs, true), s, a) != hipSuccess)
+      return PKV_ERR_HIP;
   }
   if (passes & 4) {
     const int waves = num_seqs * num_q_heads;
     hipLaunchKernelGGL(reduce_fn, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
+  return PKV_OK;
+}
+
+extern "C" int pkv_time_next_pass1(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return PKV_ERR_INVALID;
+  pkv::g_pass1_start = static_cast<hipEvent_t>(start_event);
+  pkv::g_pass1_stop = static_cast<hipEvent_t>(stop_event);
   return PKV_OK;
 }

@@ -201,6 +201,22 @@ def decode_workers(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, ma
     return n
 
 
+def time_next_pass1(start=None, stop=None) -> None:
+    """Arm the library's measurement hook: the next pass-1 launch of this
+    thread records `start` and `stop` (torch.cuda.Event with timing enabled,
+    each already recorded once so that its handle exists) as its own start and
+    stop; `start.elapsed_time(stop)` after a synchronize is then that kernel's
+    duration alone. No arguments: disarm."""
+    if (start is None) != (stop is None):
+        raise ValueError("time_next_pass1 takes both events or neither")
+    h0 = h1 = None
+    if start is not None:
+        h0, h1 = int(start.cuda_event), int(stop.cuda_event)
+        if not h0 or not h1:
+            raise ValueError("record each event once before arming the hook (its handle is created then)")
+    check(_lib.load().pkv_time_next_pass1(h0, h1), "pkv_time_next_pass1")
+
+
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, sm_scale, kv_dtype=F16,
                       k_scale=1.0, v_scale=1.0, partition_tokens=0, workspace=None, passes=3,
                       stream=None):

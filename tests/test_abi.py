@@ -254,3 +254,12 @@ def test_step_metadata_rejects_misaligned_pointers(pos, ptr):
     p[pos] = ptr
     assert lib.paged_step_metadata(p[0], p[1], p[2], p[3], 3, p[4], p[5], 1, p[6], 1, p[7], 3, 4,
                                    N) == _lib.PKV_ERR_INVALID
+
+
+def test_timing_hook_takes_both_events_or_neither():
+    """pkv_time_next_pass1 only stores its events (no GPU call); one null is
+    rejected and both null disarms. No test arms it with fake handles."""
+    lib = _lib.load()
+    assert lib.pkv_time_next_pass1(FAKE, N) == -1
+    assert lib.pkv_time_next_pass1(N, FAKE) == -1
+    assert lib.pkv_time_next_pass1(N, N) == 0

@@ -235,6 +235,44 @@ def test_repeat_calls_bit_identical():
     assert np.array_equal(o1[0].view(np.uint16), o2[0].view(np.uint16))
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_pass1_timing_hook(shared):
+    """The measurement hook (pkv_time_next_pass1): the armed pass-1 launch
+    records both events, so they give a positive duration; the hook is used
+    once and disarms; the output is bit-identical to an unarmed call on the
+    same state. shared=True runs the grouped pass (a forked batch)."""
+    if shared:
+        wl = workloads.small_forks(seed=23, prompts=[200, 90], members=[4, 3], tails=[[1, 2, 3, 4], [0, 9, 30]],
+                                   singles=[70, 5], num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=16)
+    else:
+        wl = workloads.small_custom(seed=22, lengths=[5, 300, 1000, 17, 2049], num_q_heads=32, num_kv_heads=8,
+                                    head_dim=128, block_size=32)
+    eng = harness.make_engine(wl)
+    harness.replay_setup(eng, wl, chunk_tokens=1 << 16)
+    harness.run_steps(eng, wl, 1, shared_prefix=shared)
+    _, _, q = harness.step_inputs(wl, 0, DEV)
+    B = len(wl.batch)
+    plain = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float16, device=DEV)
+    timed = torch.empty_like(plain)
+    again = torch.empty_like(plain)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    eng.attend(q, plain)
+    ops.time_next_pass1(*ev)
+    eng.attend(q, timed)
+    eng.attend(q, again)  # disarmed again: must not touch the events
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    log(f"timing hook ({'grouped' if shared else 'plain'} pass 1): {ms * 1e3:.1f} us")
+    assert 0.0 < ms < 1000.0
+    assert np.array_equal(plain.cpu().numpy().view(np.uint16), timed.cpu().numpy().view(np.uint16))
+    assert np.array_equal(plain.cpu().numpy().view(np.uint16), again.cpu().numpy().view(np.uint16))
+    with pytest.raises(ValueError):
+        ops.time_next_pass1(ev[0], None)
+
+
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (8, 2)])
 def test_batch_of_more_than_4096_sequences(hq, hkv):
     """4100 short sequences run as two launches (4096 + 4); every output is checked."""
