@@ -157,7 +157,8 @@ def load_block_manager() -> ctypes.CDLL:
     """The library whose pkv_bm_* functions BlockManager calls: libpagedkv.so,
     unless $PKV_BM_LIB names a host-only build of the block manager (the tests
     build one with the address and undefined-behaviour sanitizers and run the
-    block-manager suite against it). Only the pkv_* symbols are bound then."""
+    block-manager suite against it). Only the block manager's symbols (pkv_bm_*
+    and pkv_status_str) are bound then."""
     global _bm_lib
     path = os.environ.get("PKV_BM_LIB")
     if not path:
@@ -165,7 +166,7 @@ def load_block_manager() -> ctypes.CDLL:
     if _bm_lib is None:
         lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
-            if name.startswith("pkv_"):
+            if name.startswith("pkv_bm_") or name == "pkv_status_str":
                 fn = getattr(lib, name)
                 fn.restype = res
                 fn.argtypes = args
