@@ -11,7 +11,7 @@ import torch
 TOL = {"f16": (2e-3, 1e-2), "fp8": (3e-2, 1e-2), "fp8_e5m2": (3e-2, 1e-2)}  # (atol, rtol) per KV dtype
 
 # Threads for the oracle's per-sequence attention at full size (the host share
-# of a one-GPU machine is 16 cores); PKV_ORACLE_THREADS overrides.
+# of a one-GPU MI355X node is 16 cores); PKV_ORACLE_THREADS overrides.
 ORACLE_THREADS = int(os.environ.get("PKV_ORACLE_THREADS", "16"))
 
 # Block slice for bit-exact cache comparisons (bounded host memory: a slice of
