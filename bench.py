@@ -23,8 +23,9 @@ attention pass 1: its algorithmic bytes per launch over its average launch
 duration, measured with HIP events on every EVENT_EVERY-th timed launch. The
 events are attached to the pass-1 launch itself (the library's
 pkv_time_next_pass1 hook launches it with hipExtLaunchKernel), so they time
-the kernel's execution, on the stream it runs on, without the idle time that
-separate event records put into the stream.
+the kernel's execution alone, on the stream it runs on. Under the profiler
+the launch that carries them starts and ends a few microseconds apart from
+its neighbours in the stream; hence only every EVENT_EVERY-th launch.
 `cpu_baseline` is the CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations

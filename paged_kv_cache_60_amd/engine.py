@@ -21,8 +21,9 @@ Pinned metadata buffers form a ring of RING slots, so the host can prepare
 the next steps while earlier steps' kernels are still queued. Before the host
 overwrites a slot it waits for an event recorded after the step that last
 read it. An event in the stream idles the GPU for a few microseconds (about
-5 us per event measured on MI355X), so one event covers EVENT_EVERY steps and
-is recorded after the step's last kernel, never between its kernels.
+5.7 us between the step's last kernel and the next step's first, measured on
+MI355X), so one event covers EVENT_EVERY steps and is recorded after the
+step's last kernel, never between its kernels.
 """
 from __future__ import annotations
 
@@ -34,8 +35,8 @@ from .block_manager import BlockManager
 
 F16_NAN_BITS = 0x7E00
 FP8_NAN_BITS = 0x7F
-RING = 8          # pinned metadata slots
-EVENT_EVERY = 4   # steps covered by one completion event; RING is a multiple of it
+RING = 32         # pinned metadata slots
+EVENT_EVERY = 16  # steps covered by one completion event; RING is a multiple of it
 
 
 class PagedKVEngine:
