@@ -109,7 +109,13 @@ int paged_kv_write_scaled(const void* k_new, const void* v_new, void* k_cache, v
  * block-table update (row, logical index, block) into
  * block_tables[row * max_blocks + index] (updates outside [0, num_rows) x
  * [0, max_blocks) are skipped). slot_mapping, ctx_src and updates may be
- * pinned host memory read directly by the kernel. Work that reads ctx_dst or
+ * pinned host memory read directly by the kernel. When all three are pinned
+ * host memory (or empty), num_tokens, n_ctx and n_updates are each at most
+ * 128, num_blocks * block_size fits in 31 bits and the stream is not being
+ * captured, the call reads them itself and passes their values in the
+ * launch's arguments, which saves the kernel a round trip over the bus; they
+ * must then hold the step's values when the call is made. In every case they
+ * must not change until the kernel has run. Work that reads ctx_dst or
  * block_tables must be queued after this call.
  */
 int paged_kv_write_step(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/pagedkv.h"
 #include "device_common.hpp"
 
@@ -60,6 +62,18 @@ struct StepMeta {
   int max_blocks;
 };
 
+// A small decode step's slots, context lengths and table updates, copied
+// from pinned host memory into the launch's own arguments: the kernel then
+// reads them from the argument segment instead of across the bus. Slots
+// outside [0, num_slots) are stored as -1 (skipped either way).
+constexpr int kInlineRows = 128;
+struct StepInline {
+  int32_t slots[kInlineRows];
+  int32_t ctx[kInlineRows];
+  int32_t upd[3 * kInlineRows];
+};
+struct NoInline {};
+
 // k_inv_h / v_inv_h: one multiplier per KV head (device memory), or null to
 // use k_inv / v_inv for every head.
 // One grid row (blockIdx.y) per KV head; along x, the threads take the
@@ -70,14 +84,17 @@ struct StepMeta {
 // updates. With META every load of an iteration (the slot, the K and V
 // chunks, the metadata items; the slots and metadata may sit in host memory)
 // is issued before the first store, so an iteration costs one round trip, not
-// a chain of them.
-template <int FMT, bool META>
+// a chain of them. With INL = StepInline the slots and metadata come from
+// `inl` (at most kInlineRows of each) and the pointers to them are unused.
+template <int FMT, bool META, class INL = NoInline>
 __global__ void __launch_bounds__(256)
 kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
                 uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                 const int64_t* __restrict__ slots, int64_t num_tokens, int cpr_log2, int num_kv_heads,
                 int64_t num_slots, int bs_log2, float k_inv, float v_inv,
-                const float* __restrict__ k_inv_h, const float* __restrict__ v_inv_h, StepMeta meta) {
+                const float* __restrict__ k_inv_h, const float* __restrict__ v_inv_h, StepMeta meta,
+                INL inl) {
+  constexpr bool kInline = std::is_same<INL, StepInline>::value;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
@@ -96,11 +113,20 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
     const bool do_ctx = meta_row && i < meta.n_ctx;
     const bool do_upd = meta_row && i < meta.n_updates;
     int ctx = 0, row = -1, idx = -1, blk = 0;
-    if (do_ctx) ctx = meta.ctx_src[i];
-    if (do_upd) {
-      row = meta.updates[3 * i];
-      idx = meta.updates[3 * i + 1];
-      blk = meta.updates[3 * i + 2];
+    if constexpr (kInline) {
+      if (do_ctx) ctx = inl.ctx[i];
+      if (do_upd) {
+        row = inl.upd[3 * i];
+        idx = inl.upd[3 * i + 1];
+        blk = inl.upd[3 * i + 2];
+      }
+    } else {
+      if (do_ctx) ctx = meta.ctx_src[i];
+      if (do_upd) {
+        row = meta.updates[3 * i];
+        idx = meta.updates[3 * i + 1];
+        blk = meta.updates[3 * i + 2];
+      }
     }
     const bool chunk = i < n;
     const int64_t t = i >> cpr_log2;
@@ -109,7 +135,10 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
     int64_t slot = -1;
     u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
     if (chunk) {
-      slot = slots[t];
+      if constexpr (kInline)
+        slot = inl.slots[t];
+      else
+        slot = slots[t];
       kv = k_new[src];
       vv = v_new[src];
       // In a decode step (META: a few tokens, one round trip decides the
@@ -157,6 +186,28 @@ kv_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new
 namespace pkv {
 namespace {
 
+// Whether p is pinned host memory, so that the host can read it here. A
+// pointer the runtime does not know leaves an error, which is cleared.
+bool pinned_host(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return at.type == hipMemoryTypeHost;
+}
+
+// Whether work queued on s is being captured into a graph (or the query
+// fails, which is taken as yes).
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int64_t* slot_mapping, int num_tokens, int num_blocks, int num_kv_heads,
                     int head_dim, int block_size, int kv_dtype, float k_inv_scale, float v_inv_scale,
@@ -194,6 +245,33 @@ int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v
   const bool fp8 = kv_dtype != PKV_KV_F16;
   const float ki = fp8 ? k_inv_scale : 1.0f;
   const float vi = fp8 ? v_inv_scale : 1.0f;
+  const dim3 grid((unsigned)blocks, (unsigned)num_kv_heads);
+  // a decode step small enough to travel in the launch's arguments, with
+  // its slots and metadata in pinned host memory, on a stream that is not
+  // being captured (a captured launch keeps reading the host memory at each
+  // replay)
+  if (meta && num_tokens <= kInlineRows && m.n_ctx <= kInlineRows && m.n_updates <= kInlineRows &&
+      num_slots <= 0x7FFFFFFF && !capturing(s) && (num_tokens == 0 || pinned_host(slot_mapping)) &&
+      (m.n_ctx == 0 || pinned_host(m.ctx_src)) && (m.n_updates == 0 || pinned_host(m.updates))) {
+    StepInline in;
+    for (int t = 0; t < num_tokens; ++t) {
+      const int64_t sl = slot_mapping[t];
+      in.slots[t] = sl >= 0 && sl < num_slots ? (int32_t)sl : -1;
+    }
+    for (int i = 0; i < m.n_ctx; ++i) in.ctx[i] = m.ctx_src[i];
+    for (int i = 0; i < 3 * m.n_updates; ++i) in.upd[i] = m.updates[i];
+    decltype(&kv_write_kernel<kF16, true, StepInline>) ik;
+    if (kv_dtype == PKV_KV_F16)
+      ik = kv_write_kernel<kF16, true, StepInline>;
+    else if (kv_dtype == PKV_KV_FP8_E4M3)
+      ik = kv_write_kernel<kE4M3, true, StepInline>;
+    else
+      ik = kv_write_kernel<kE5M2, true, StepInline>;
+    hipLaunchKernelGGL(ik, grid, dim3(threads), 0, s, kn, vn, kc, vc, slot_mapping, (int64_t)num_tokens,
+                       cpr_log2, num_kv_heads, num_slots, bs_log2, ki, vi, fp8 ? k_inv_h : nullptr,
+                       fp8 ? v_inv_h : nullptr, m, in);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
   decltype(&kv_write_kernel<kF16, false>) kern;
   if (kv_dtype == PKV_KV_F16)
     kern = meta ? kv_write_kernel<kF16, true> : kv_write_kernel<kF16, false>;
@@ -201,9 +279,9 @@ int launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v
     kern = meta ? kv_write_kernel<kE4M3, true> : kv_write_kernel<kE4M3, false>;
   else
     kern = meta ? kv_write_kernel<kE5M2, true> : kv_write_kernel<kE5M2, false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)num_kv_heads), dim3(threads), 0, s, kn, vn, kc, vc,
-                     slot_mapping, (int64_t)num_tokens, cpr_log2, num_kv_heads, num_slots, bs_log2, ki, vi,
-                     fp8 ? k_inv_h : nullptr, fp8 ? v_inv_h : nullptr, m);
+  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, kn, vn, kc, vc, slot_mapping, (int64_t)num_tokens,
+                     cpr_log2, num_kv_heads, num_slots, bs_log2, ki, vi, fp8 ? k_inv_h : nullptr,
+                     fp8 ? v_inv_h : nullptr, m, NoInline{});
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -182,21 +182,28 @@ def test_step_metadata_bit_exact():
 
 
 @pytest.mark.parametrize("kv_dtype", ["f16", "fp8"])
-def test_kv_write_step_bit_exact(kv_dtype):
-    tables, upd, ctx, expect = _meta_case(4)
-    B = len(ctx)
+@pytest.mark.parametrize("where,B,n_upd", [("pinned", 37, 20), ("pinned", 128, 128), ("pinned", 200, 150),
+                                           ("device", 37, 20)])
+def test_kv_write_step_bit_exact(kv_dtype, where, B, n_upd):
+    """The write kernel of a decode step: small steps with pinned metadata
+    travel in the launch's arguments (up to 128 tokens, lengths and updates),
+    larger ones and device metadata are read by the kernel; same bits."""
+    tables, upd, ctx, expect = _meta_case(4, B=B, n_upd=n_upd)
     g = np.random.default_rng(5)
     nb, hkv, bs, d = 40, 8, 16, 128
     slots = g.permutation(nb * bs)[:B].astype(np.int64)
     slots[::7] = -1
+    slots[5] = nb * bs + 3   # past the pool: skipped
+    slots[12] = 1 << 40      # past 32 bits: skipped
     K = g.standard_normal((B, hkv, d), dtype=np.float32).astype(np.float16)
     V = g.standard_normal((B, hkv, d), dtype=np.float32).astype(np.float16)
     o_k, o_v, g_k, g_v = _caches(nb, hkv, bs, d, kv_dtype)
-    cache_ops.scatter(o_k, o_v, K, V, slots, bs, kv_dtype, 61.0, 61.0)
+    cache_ops.scatter(o_k, o_v, K, V, np.where(slots < nb * bs, slots, -1), bs, kv_dtype, 61.0, 61.0)
     t_dev = torch.from_numpy(tables).to(DEV)
     c_dev = torch.full((B,), -5, dtype=torch.int32, device=DEV)
-    ops.paged_kv_write_step(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v, _pinned(slots),
-                            _pinned(ctx), c_dev, _pinned(upd.reshape(-1)), len(upd), t_dev, kv_dtype, 61.0, 61.0)
+    put = _pinned if where == "pinned" else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV))
+    ops.paged_kv_write_step(torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), g_k, g_v, put(slots),
+                            put(ctx), c_dev, put(upd.reshape(-1)), len(upd), t_dev, kv_dtype, 61.0, 61.0)
     torch.cuda.synchronize()
     assert np.array_equal(cache_bits(g_k), oracle_bits(o_k))
     assert np.array_equal(cache_bits(g_v), oracle_bits(o_v))
